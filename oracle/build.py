@@ -1,0 +1,28 @@
+"""Build the CPU oracle's shared library (oracle/liboracle.so) with gcc.
+
+Test infrastructure only: see oracle/__init__.py.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    # -ffp-contract=off: every product and sum is rounded as written (no FMA
+    # contraction), so results do not depend on the host CPU's instruction set.
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-std=c11", "-Wall", "-Wextra", SRC, "-o", LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

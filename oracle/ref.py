@@ -1,0 +1,157 @@
+"""ctypes front end of the C oracle (oracle.c).  Test infrastructure only.
+
+Every function takes and returns NumPy arrays.  Failing argument checks raise
+ValueError (the C side returns -2 for bad sizes, -3 for an expert id outside
+[0, E)).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            from . import build as _b
+            _b.build()
+        L = C.CDLL(lib_path)
+        P = C.c_void_p
+        i = C.c_int
+        L.oracle_e4m3_value.restype = C.c_double
+        L.oracle_e4m3_value.argtypes = [C.c_uint8]
+        L.oracle_e8m0_value.restype = C.c_double
+        L.oracle_e8m0_value.argtypes = [C.c_uint8]
+        L.oracle_dequant.restype = C.c_double
+        L.oracle_dequant.argtypes = [C.c_uint8, C.c_uint8]
+        L.oracle_e4m3_table.argtypes = [P]
+        L.oracle_e8m0_table.argtypes = [P]
+        L.oracle_bf16_value.restype = C.c_double
+        L.oracle_bf16_value.argtypes = [C.c_uint16]
+        L.oracle_round_f32.restype = C.c_float
+        L.oracle_round_f32.argtypes = [C.c_double]
+        L.oracle_bf16_rne.restype = C.c_uint16
+        L.oracle_bf16_rne.argtypes = [C.c_float]
+        L.oracle_silu.restype = C.c_double
+        L.oracle_silu.argtypes = [C.c_double]
+        L.oracle_gate_up.restype = i
+        L.oracle_gate_up.argtypes = [P, P, P, P, i, i, i, i, i, P, P, P, i]
+        L.oracle_down.restype = i
+        L.oracle_down.argtypes = [P, P, P, P, P, i, i, i, i, i, P, i]
+        L.oracle_moe_decode.restype = i
+        L.oracle_moe_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, P, i]
+        L.oracle_max_threads.restype = i
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _rc(rc):
+    if rc == -2:
+        raise ValueError("oracle: bad sizes (need K>=1, E>=1, H and I multiples of 32)")
+    if rc == -3:
+        raise ValueError("oracle: expert id outside [0, E)")
+    if rc:
+        raise ValueError(f"oracle: error {rc}")
+
+
+def e4m3_table() -> np.ndarray:
+    out = np.empty(256, np.float64)
+    _load().oracle_e4m3_table(_p(out))
+    return out
+
+
+def e8m0_table() -> np.ndarray:
+    out = np.empty(256, np.float64)
+    _load().oracle_e8m0_table(_p(out))
+    return out
+
+
+def dequant(code: int, scale: int) -> float:
+    return _load().oracle_dequant(code, scale)
+
+
+def bf16_value(bits: int) -> float:
+    return _load().oracle_bf16_value(bits)
+
+
+def round_f32(v: float) -> float:
+    return _load().oracle_round_f32(v)
+
+
+def bf16_rne(f: float) -> int:
+    return _load().oracle_bf16_rne(f)
+
+
+def silu(g: float) -> float:
+    return _load().oracle_silu(g)
+
+
+def _dims(layer_arrays, x_or_act_shape=None):
+    wgu, sgu, wd, sd = layer_arrays
+    E, I2, H = wgu.shape
+    return E, H, I2 // 2
+
+
+def gate_up(x, ids, wgu, sgu, nthreads: int = 0, return_gu: bool = False):
+    """act[B,K,I] BF16 bits (and optionally FP64 g, u) from x[B,H] bits."""
+    x = _c(x, np.uint16); ids = _c(ids, np.int32)
+    wgu = _c(wgu, np.uint8); sgu = _c(sgu, np.uint8)
+    E, I2, H = wgu.shape
+    I = I2 // 2
+    B, K = ids.shape
+    assert x.shape == (B, H) and sgu.shape == (E, I2, H // 32)
+    act = np.empty((B, K, I), np.uint16)
+    g = np.empty((B, K, I), np.float64) if return_gu else None
+    u = np.empty((B, K, I), np.float64) if return_gu else None
+    _rc(_load().oracle_gate_up(_p(x), _p(ids), _p(wgu), _p(sgu), B, K, E, H, I, _p(act),
+                               _p(g) if return_gu else None, _p(u) if return_gu else None, nthreads))
+    return (act, g, u) if return_gu else act
+
+
+def down(act, ids, w, wd, sd, nthreads: int = 0):
+    """y[B,H] FP64 from a given intermediate act[B,K,I] (BF16 bits)."""
+    act = _c(act, np.uint16); ids = _c(ids, np.int32); w = _c(w, np.float32)
+    wd = _c(wd, np.uint8); sd = _c(sd, np.uint8)
+    E, H, I = wd.shape
+    B, K = ids.shape
+    assert act.shape == (B, K, I) and w.shape == (B, K) and sd.shape == (E, H, I // 32)
+    y = np.empty((B, H), np.float64)
+    _rc(_load().oracle_down(_p(act), _p(ids), _p(w), _p(wd), _p(sd), B, K, E, H, I, _p(y), nthreads))
+    return y
+
+
+def moe_decode(x, ids, w, wgu, sgu, wd, sd, nthreads: int = 0):
+    """(y[B,H] FP64, act[B,K,I] BF16 bits) for the whole layer."""
+    x = _c(x, np.uint16); ids = _c(ids, np.int32); w = _c(w, np.float32)
+    wgu = _c(wgu, np.uint8); sgu = _c(sgu, np.uint8); wd = _c(wd, np.uint8); sd = _c(sd, np.uint8)
+    E, I2, H = wgu.shape
+    I = I2 // 2
+    B, K = ids.shape
+    assert wd.shape == (E, H, I)
+    act = np.empty((B, K, I), np.uint16)
+    y = np.empty((B, H), np.float64)
+    _rc(_load().oracle_moe_decode(_p(x), _p(ids), _p(w), _p(wgu), _p(sgu), _p(wd), _p(sd),
+                                  B, K, E, H, I, _p(act), _p(y), nthreads))
+    return y, act
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()

@@ -1,0 +1,308 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself (a library routine, the OCP format definitions, exact arithmetic, a
+closed form, an invariant of the layer's mathematics, or an expert-centric
+brute force).  CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+from moe_decode_gate_amd import inputs as gen
+
+
+# ---------------------------------------------------------------- formats --
+
+def test_e4m3_table_matches_torch_all_codes():
+    ours = oracle.e4m3_table()
+    lib = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert sorted(np.flatnonzero(nan)) == [0x7F, 0xFF]          # S.1111.111 only: the FN variant
+    assert np.array_equal(ours[~nan], lib[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(lib[~nan]))
+
+
+@pytest.mark.parametrize("code,value", [
+    (0x38, 1.0), (0x7E, 448.0), (0xFE, -448.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9),
+    (0x08, 2.0 ** -6), (0x40, 2.0), (0x3C, 1.5), (0x00, 0.0), (0x78, 256.0),
+])
+def test_e4m3_format_definition_values(code, value):
+    # OCP 8-bit FP E4M3: bias 7, subnormal step 2^-9, largest finite 1.75 * 2^8.
+    assert oracle.e4m3_table()[code] == value
+
+
+def test_e4m3_negative_zero_and_nan():
+    t = oracle.e4m3_table()
+    assert t[0x80] == 0.0 and math.copysign(1.0, t[0x80]) < 0
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
+
+
+def test_e8m0_table_matches_torch_all_scales():
+    ours = oracle.e8m0_table()
+    lib = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert math.isnan(ours[255]) and math.isnan(lib[255])
+    assert np.array_equal(ours[:255], lib[:255])
+    assert ours[127] == 1.0 and ours[0] == 2.0 ** -127 and ours[254] == 2.0 ** 127
+
+
+def test_dequant_is_exact_product_all_65536():
+    t = oracle.e4m3_table()
+    for s in range(256):
+        for c in range(0, 256, 17 if s % 3 else 1):
+            v = oracle.dequant(c, s)
+            if c in (0x7F, 0xFF) or s == 255:
+                assert math.isnan(v)
+            else:
+                assert v == math.ldexp(t[c], s - 127)
+
+
+def test_bf16_rne_matches_torch(rng):
+    f = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(2000) * 1e-38).astype(np.float32),          # subnormal range
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, -3.3895314e38, 1e-45], np.float32),
+    ])
+    # exact ties: low 16 bits == 0x8000, both parities of the kept LSB
+    ties = (rng.integers(0x3F000000, 0x40800000, 4000, dtype=np.uint32) & 0xFFFF0000) | 0x8000
+    f = np.concatenate([f, ties.view(np.float32)])
+    lib = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = np.array([oracle.bf16_rne(float(v)) for v in f], np.uint16)
+    assert np.array_equal(ours, lib)
+
+
+def test_bf16_rne_nan_stays_nan():
+    b = oracle.bf16_rne(float("nan"))
+    assert (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
+
+
+def test_bf16_value_roundtrip(rng):
+    bits = rng.integers(0, 65536, 5000, dtype=np.uint16)
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = np.array([oracle.bf16_value(int(b)) for b in bits])
+    fin = ~np.isnan(lib)
+    assert np.array_equal(ours[fin], lib[fin]) and np.all(np.isnan(ours[~fin]))
+
+
+def test_round_f32_matches_numpy(rng):
+    v = rng.standard_normal(5000) * 10.0 ** rng.integers(-30, 30, 5000)
+    ours = np.array([oracle.round_f32(float(a)) for a in v], np.float32)
+    assert np.array_equal(ours, v.astype(np.float32))
+
+
+def test_silu_matches_torch_and_is_stable():
+    g = np.concatenate([np.linspace(-40, 40, 2001), [-750.0, -1e6, 750.0, 1e6, 0.0]])
+    lib = torch.nn.functional.silu(torch.from_numpy(g)).numpy()
+    ours = np.array([oracle.silu(float(a)) for a in g])
+    assert np.all(np.isfinite(ours))
+    np.testing.assert_allclose(ours, lib, rtol=1e-15, atol=1e-300)
+    assert oracle.silu(64.0) == 64.0 * (1.0 / (1.0 + math.exp(-64.0)))
+
+
+# ----------------------------------------------------------- the layer --
+
+def _tiny_layer(E, K, H, I, seed, std=0.02):
+    spec = gen.LayerSpec(E=E, K=K, H=H, I=I, seed=seed)
+    return spec, gen.make_layer(spec, std=std)
+
+
+def _dense_reference(x, ids, w, L):
+    """sum_k w_k * MLP_{e_k}(x) with torch float64 matmuls on torch-decoded
+    weights; the intermediate is rounded FP64 -> FP32 -> BF16 by torch."""
+    def deq(codes, scales):
+        v = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+        s = torch.from_numpy(scales).view(torch.float8_e8m0fnu).to(torch.float64)
+        return v * s.repeat_interleave(32, dim=-1)
+    E, I2, H = L.wgu.shape
+    I = I2 // 2
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    B, K = ids.shape
+    y = torch.zeros(B, H, dtype=torch.float64)
+    act = np.zeros((B, K, I), np.uint16)
+    for b in range(B):
+        for k in range(K):
+            e = int(ids[b, k])
+            gu = deq(L.wgu[e], L.sgu[e])
+            dn = deq(L.wd[e], L.sd[e])
+            g = gu[:I] @ xf[b]
+            u = gu[I:] @ xf[b]
+            a = (torch.nn.functional.silu(g) * u).to(torch.float32).to(torch.bfloat16)
+            act[b, k] = a.view(torch.int16).numpy().view(np.uint16)
+            y[b] += float(w[b, k]) * (dn @ a.to(torch.float64))
+    return y.numpy(), act
+
+
+@pytest.mark.parametrize("E,K,H,I,B", [(4, 1, 64, 32, 2), (4, 2, 64, 32, 3), (8, 2, 128, 64, 1)])
+def test_oracle_matches_expert_centric_brute_force(E, K, H, I, B):
+    spec, L = _tiny_layer(E, K, H, I, seed=77 + E + K + B, std=0.3)
+    t = gen.make_tokens(spec, B)
+    y, act = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    yb, actb, _ = brute.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    assert np.array_equal(act, actb)
+    np.testing.assert_allclose(y, np.array(yb), rtol=1e-13, atol=1e-300)
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_oracle_matches_dense_swiglu_reference(K):
+    spec, L = _tiny_layer(16, K, 256, 96, seed=300 + K, std=0.1)
+    t = gen.make_tokens(spec, 4)
+    y, act = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    yr, actr = _dense_reference(t.x, t.ids, t.w, L)
+    assert np.array_equal(act, actr)
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-15)
+
+
+def test_k1_unit_weight_is_one_dense_mlp():
+    spec, L = _tiny_layer(3, 1, 64, 64, seed=9, std=0.2)
+    t = gen.make_tokens(spec, 2)
+    t.w[:] = 1.0
+    y, _ = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    yr, _ = _dense_reference(t.x, t.ids, t.w, L)
+    np.testing.assert_allclose(y, yr, rtol=1e-12, atol=1e-15)
+
+
+@pytest.fixture(scope="module")
+def small():
+    spec, L = _tiny_layer(8, 3, 128, 64, seed=4242, std=0.1)
+    t = gen.make_tokens(spec, 5)
+    return spec, L, t
+
+
+def _y(t, L, ids=None, w=None, x=None, sd=None):
+    y, _ = oracle.moe_decode(t.x if x is None else x, t.ids if ids is None else ids,
+                             t.w if w is None else w, L.wgu, L.sgu, L.wd, L.sd if sd is None else sd)
+    return y
+
+
+def test_invariant_linear_in_router_weights(small):
+    spec, L, t = small
+    # weights with few significant bits, so that w1 + w2 is exact in FP32
+    w1 = (np.round(t.w * 256) / 256).astype(np.float32)
+    w2 = (np.random.default_rng(5).integers(-64, 64, t.w.shape) / 32.0).astype(np.float32)
+    # y(w1 + w2) = y(w1) + y(w2) and y(2 w) = 2 y(w): the combine is linear in w
+    y12 = _y(t, L, w=(w1 + w2).astype(np.float32))
+    ysum = _y(t, L, w=w1) + _y(t, L, w=w2)
+    np.testing.assert_allclose(y12, ysum, rtol=0, atol=1e-13 * np.abs(ysum).max())
+    np.testing.assert_array_equal(_y(t, L, w=(2 * w1).astype(np.float32)), 2 * _y(t, L, w=w1))
+
+
+def test_invariant_zero_weight_slot_contributes_nothing(small):
+    spec, L, t = small
+    w = t.w.copy(); w[:, 1] = 0.0
+    ids2 = t.ids.copy(); ids2[:, 1] = (ids2[:, 1] + 3) % spec.E
+    np.testing.assert_array_equal(_y(t, L, w=w), _y(t, L, w=w, ids=ids2))
+    # and equals the layer with that slot removed
+    keep = [0, 2]
+    y_removed, _ = oracle.moe_decode(t.x, t.ids[:, keep].copy(), t.w[:, keep].copy(), L.wgu, L.sgu, L.wd, L.sd)
+    np.testing.assert_allclose(_y(t, L, w=w), y_removed, rtol=1e-14, atol=1e-300)
+
+
+def test_invariant_slot_permutation(small):
+    spec, L, t = small
+    p = [2, 0, 1]
+    np.testing.assert_allclose(_y(t, L, ids=t.ids[:, p].copy(), w=t.w[:, p].copy()), _y(t, L),
+                               rtol=1e-14, atol=1e-300)
+
+
+def test_invariant_duplicate_expert_equals_summed_weight(small):
+    spec, L, t = small
+    ids = t.ids.copy(); ids[:, 1] = ids[:, 0]
+    w = (np.round(t.w * 1024) / 1024).astype(np.float32)       # so that w0 + w1 is exact
+    wsum = w.copy(); wsum[:, 0] = w[:, 0] + w[:, 1]; wsum[:, 1] = 0.0
+    y_dup, y_sum = _y(t, L, ids=ids, w=w), _y(t, L, ids=ids, w=wsum)
+    np.testing.assert_allclose(y_dup, y_sum, rtol=0, atol=1e-13 * np.abs(y_sum).max())
+
+
+def test_invariant_token_permutation(small):
+    spec, L, t = small
+    p = np.array([3, 1, 4, 0, 2])
+    yp = _y(t, L, ids=t.ids[p].copy(), w=t.w[p].copy(), x=t.x[p].copy())
+    np.testing.assert_array_equal(yp, _y(t, L)[p])
+
+
+@pytest.mark.parametrize("shift", [1, -3, 5])
+def test_invariant_down_scale_shift_scales_output_exactly(small, shift):
+    spec, L, t = small
+    sd = (L.sd.astype(np.int32) + shift).astype(np.uint8)
+    np.testing.assert_array_equal(_y(t, L, sd=sd), _y(t, L) * 2.0 ** shift)
+
+
+def test_fingerprint_closed_form():
+    """Exact closed form.  Gate rows all 2.0 and x all 1.0 give g = 2H = 64,
+    and SiLU(64) rounds to exactly 64.  Up rows of expert e hold the single
+    code (e+1) at h = 0, so u = e+1 and act = 64 (e+1), exact in BF16.  Down
+    row h holds 1.0 at column h (H = I), scale 2^0.  Hence
+        y[b,h] = sum_k w[b,k] * 64 * (ids[b,k] + 1)
+    for every h: a wrong expert, slot, weight or row index changes the value.
+    """
+    E, K, H, I = 6, 3, 32, 32
+    wgu = np.zeros((E, 2 * I, H), np.uint8)
+    sgu = np.full((E, 2 * I, H // 32), 127, np.uint8)
+    wgu[:, :I, :] = 0x40                                       # 2.0
+    code_of = {1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4A, 6: 0x4C}   # 1,2,3,4,5,6 in E4M3
+    for e in range(E):
+        wgu[e, I:, 0] = code_of[e + 1]
+    wd = np.zeros((E, H, I), np.uint8)
+    sd = np.full((E, H, I // 32), 127, np.uint8)
+    for h in range(H):
+        wd[:, h, h % I] = 0x38
+    x = np.full((2, H), 0x3F80, np.uint16)                     # bf16 1.0
+    ids = np.array([[0, 3, 5], [2, 2, 4]], np.int32)
+    w = np.array([[0.5, 0.25, 0.125], [0.5, 0.5, 2.0 ** -6]], np.float32)
+    y, act = oracle.moe_decode(x, ids, w, wgu, sgu, wd, sd)
+    expect = np.array([sum(float(w[b, k]) * 64 * (ids[b, k] + 1) for k in range(K)) for b in range(2)])
+    np.testing.assert_array_equal(y, np.repeat(expect[:, None], H, axis=1))
+    for b in range(2):
+        for k in range(K):
+            assert oracle.bf16_value(int(act[b, k, 0])) == 64.0 * (ids[b, k] + 1)
+
+
+def test_oracle_rejects_out_of_range_ids():
+    spec, L = _tiny_layer(4, 2, 64, 32, seed=1)
+    t = gen.make_tokens(spec, 2)
+    ids = t.ids.copy(); ids[1, 1] = 4
+    with pytest.raises(ValueError):
+        oracle.moe_decode(t.x, ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    ids[1, 1] = -1
+    with pytest.raises(ValueError):
+        oracle.moe_decode(t.x, ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+
+
+def test_oracle_thread_count_does_not_change_result(small):
+    spec, L, t = small
+    y1, a1 = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd, nthreads=1)
+    y4, a4 = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd, nthreads=4)
+    assert np.array_equal(a1, a4) and np.array_equal(y1, y4)
+
+
+def test_nan_code_propagates(small):
+    spec, L, t = small
+    wd = L.wd.copy()
+    e = int(t.ids[0, 0])
+    wd[e, 7, 3] = 0x7F
+    y, _ = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, wd, L.sd)
+    assert math.isnan(y[0, 7])
+    assert np.isfinite(np.delete(y[0], 7)).all()
+
+
+def test_golden_tiny_layer_regression():
+    """The tiny layer's generator bits and oracle output are those stored by
+    tests/golden/make_golden.py (oracle + generator only)."""
+    import hashlib
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_layer.json")
+    ref = json.load(open(path))
+    spec = gen.CONFIGS["tiny"]["spec"]
+    L = gen.make_layer(spec)
+    t = gen.make_tokens(spec, 1)
+    h = hashlib.sha256()
+    for a in (L.wgu, L.sgu, L.wd, L.sd):
+        h.update(a.tobytes())
+    assert h.hexdigest() == ref["weights_sha256"]
+    y, act = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    assert act.ravel().tolist() == ref["act_bits"]
+    assert [float(v).hex() for v in y.ravel()] == ref["y"]
