@@ -1,0 +1,160 @@
+/*
+ * wd.h — C ABI of the MI355X (gfx950) small-batch MoE decode layer in its
+ * output-neuron-centric ("warp decode") form.
+ *
+ * The layer (warp-decode write-ups: "Better MoE model inference with warp
+ * decode", TL;DR and Key claims, section "How the two kernels work"; the
+ * Chinese summary "Cursor推出MoE推理加速方法Warp Decode", section 技术原理):
+ *
+ *     y[b] = sum_k topk_w[b,k] * Down_e( SiLU(Gate_e x[b]) (.) Up_e x[b] ),
+ *            e = topk_ids[b,k],
+ *
+ * computed by two kernels: a gate/up kernel that writes the SiLU-gated
+ * intermediate once as BF16, and a down kernel that folds the router weight
+ * into its FP32 accumulator, so no per-expert output, padding, gather,
+ * scatter or combine buffer exists.
+ *
+ * Data formats and layouts (all tensors dense, row-major, reduction axis
+ * innermost):
+ *   x        [B, H]        BF16 bit patterns (uint16)
+ *   topk_ids [B, K]        int32 expert ids, each in [0, E); duplicates allowed
+ *   topk_w   [B, K]        fp32 router weights, used as given (not renormalised)
+ *   w_gu     [E, 2I, H]    MXFP8 element codes, OCP E4M3 "FN" (uint8);
+ *                          rows [0, I) are the gate projection, rows [I, 2I)
+ *                          the up projection
+ *   s_gu     [E, 2I, H/32] OCP E8M0 block exponents (uint8), value 2^(s-127),
+ *                          one per 32 consecutive elements of a row
+ *   w_d      [E, H, I]     MXFP8 codes of the down projection
+ *   s_d      [E, H, I/32]  E8M0 exponents of the down projection
+ *   act      [B, K, I]     BF16 intermediate SiLU(g) * u, rounded to nearest even
+ *   out      [B, H]        BF16 output, rounded to nearest even from FP32
+ *
+ * Arithmetic: MXFP8 weights are converted to FP32 as they are read (the
+ * conversion is exact), activations stay BF16 in memory, all products and sums
+ * are FP32.  Summation order is fixed by the kernel's lane layout, so repeated
+ * calls with the same inputs give bit-identical results.
+ *
+ * Ownership: the caller owns every buffer (device memory) and the stream; the
+ * compute entry points allocate, free and synchronise nothing, so they may be
+ * recorded into a HIP graph.  Work is enqueued on `stream` (a hipStream_t;
+ * NULL is the default stream) and the call returns without waiting.
+ *
+ * Errors: every entry point returns WD_OK (0) or a negative status.  Argument
+ * checks run on the host before any HIP call; nothing is launched when a check
+ * fails.  A fault inside a kernel surfaces at the caller's next synchronising
+ * HIP call.  An expert id outside [0, E) is not a host-checked precondition
+ * (ids live in device memory); the kernels never read out of bounds for it:
+ * its slot's intermediate row is written as NaN and every output of its token
+ * becomes NaN.
+ *
+ * Size limits of this build: H and I multiples of 32, H <= 8192,
+ * K * I <= 16384, B * K * I < 2^31.  B = 0 is accepted and launches nothing
+ * (activation/output/routing pointers may then be NULL).
+ */
+#ifndef WD_H
+#define WD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum wd_status {
+    WD_OK = 0,
+    WD_ERR_NULL = -1,        /* a required pointer is NULL */
+    WD_ERR_DIMS = -2,        /* B < 0, K < 1, E < 1, H or I not a positive multiple of 32 */
+    WD_ERR_ALIGN = -3,       /* x, w_gu, w_d, act, workspace not 16-byte aligned; ids, w not 4-byte; out not 2-byte */
+    WD_ERR_WORKSPACE = -4,   /* workspace smaller than wd_workspace_bytes() */
+    WD_ERR_DEVICE = -5,      /* no HIP device, or the current device is not gfx950 */
+    WD_ERR_LAUNCH = -6,      /* the kernel launch was rejected by the HIP runtime */
+    WD_ERR_UNSUPPORTED = -7  /* sizes beyond this build's limits, or a bad launch configuration */
+};
+
+/* Launch configuration (tuning).  Any field left 0 takes the library default
+ * for the call's sizes.
+ *   rows_per_wave    1, 2 or 4: output rows one 64-lane wave computes (each
+ *                    row is still one wave-wide reduction)
+ *   waves_per_block  1..4: waves per workgroup
+ *   order            1 = row-block major (the waves of all tokens and slots
+ *                    for one block of rows are adjacent, so tokens that share
+ *                    an expert re-read its rows while they are in cache);
+ *                    2 = token/slot major (one slot's rows are adjacent)
+ *   xcd_remap        1 = renumber workgroups so that each of the 8 XCDs gets
+ *                    one contiguous range of the work order; 2 = keep the
+ *                    hardware's round-robin numbering
+ */
+typedef struct wd_launch {
+    int rows_per_wave;
+    int waves_per_block;
+    int order;
+    int xcd_remap;
+} wd_launch;
+
+/* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section
+ * "How the two kernels work"; the Chinese summary's "Gate/Up Kernel"): one
+ * 64-lane wave per (token b, slot k, intermediate row j).  The wave streams
+ * gate row j and up row I+j of expert e = topk_ids[b,k], converting MXFP8 to
+ * FP32 in registers, reads x[b] once for both dot products, reduces across its
+ * lanes and writes act[b,k,j] = BF16(SiLU(g) * u). */
+int wd_gate_up(const uint16_t *x, const int32_t *topk_ids,
+               const uint8_t *w_gu, const uint8_t *s_gu, uint16_t *act,
+               int B, int K, int E, int H, int I, void *stream);
+int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
+                  const uint8_t *w_gu, const uint8_t *s_gu, uint16_t *act,
+                  int B, int K, int E, int H, int I, const wd_launch *cfg, void *stream);
+
+/* Down kernel (moe_down_3d_batched; same sections; the Chinese summary's
+ * "Down Kernel"): one wave per (token b, output dim h).  The wave walks the K
+ * routed experts' rows Wd[e_k, h, :], folds topk_w[b,k] into one FP32
+ * accumulator, reduces across its 64 lanes with DPP and lane-swap operations
+ * (no LDS) and writes out[b,h] = BF16(acc). */
+int wd_down(const uint16_t *act, const int32_t *topk_ids, const float *topk_w,
+            const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
+            int B, int K, int E, int H, int I, void *stream);
+int wd_down_ex(const uint16_t *act, const int32_t *topk_ids, const float *topk_w,
+               const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
+               int B, int K, int E, int H, int I, const wd_launch *cfg, void *stream);
+
+/* Whole layer: wd_gate_up into `workspace` (used as act[B,K,I]), then wd_down,
+ * both on `stream`.  workspace_bytes must be >= wd_workspace_bytes(B, K, I). */
+int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                  const uint8_t *w_gu, const uint8_t *s_gu,
+                  const uint8_t *w_d, const uint8_t *s_d,
+                  void *workspace, size_t workspace_bytes, uint16_t *out,
+                  int B, int K, int E, int H, int I, void *stream);
+
+/* Bytes of the intermediate act[B,K,I] (BF16); 0 for invalid sizes. */
+size_t wd_workspace_bytes(int B, int K, int I);
+
+/* Static string naming a status code (never NULL). */
+const char *wd_status_string(int status);
+
+/* ---- measurement helpers (not on the layer's path) --------------------- */
+
+/* Exhaustive MXFP8 conversion probe: out[s * 256 + c] = the FP32 value the
+ * layer kernels compute for element code c under block exponent byte s, for
+ * all 256 x 256 pairs (65,536 floats, device memory, 16-byte aligned). */
+int wd_dequant_probe(float *out, void *stream);
+
+/* Contiguous-read bandwidth kernel: reads `bytes` (a multiple of 16) from
+ * `buf` with 16-byte loads in a grid-stride loop and writes one word per
+ * workgroup to sink[0 .. blocks) so the reads cannot be elided.  blocks <= 0
+ * picks a default; sink must hold that many uint32 (wd_stream_blocks()). */
+int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, void *stream);
+int wd_stream_blocks(void);
+
+/* Contiguous copy with 16-byte loads and stores (bytes a multiple of 16). */
+int wd_stream_copy(void *dst, const void *src, size_t bytes, int blocks, void *stream);
+
+/* Enqueue one wave that sleeps for about `sleep_units` * 8192 shader clocks
+ * (bounded to 2^20 units).  Used to let the host queue work ahead of the GPU
+ * before event-timed regions. */
+int wd_gpu_sleep(int sleep_units, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WD_H */

@@ -1,0 +1,210 @@
+"""Python binding of libwd.so (the C ABI in include/wd.h).
+
+Argument marshalling only: the functions check dtypes, devices, contiguity
+and shapes of torch tensors, then pass raw device pointers, sizes and the
+current HIP stream to the library.  All computation happens in the library's
+HIP kernels.  Importing this module fails loudly when the library has not
+been built (python -m moe_decode_gate_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libwd.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "wd.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                      "(python -m moe_decode_gate_amd.build)")
+_lib = C.CDLL(LIB_PATH)
+
+WD_OK = 0
+STATUS = {0: "WD_OK", -1: "WD_ERR_NULL", -2: "WD_ERR_DIMS", -3: "WD_ERR_ALIGN", -4: "WD_ERR_WORKSPACE",
+          -5: "WD_ERR_DEVICE", -6: "WD_ERR_LAUNCH", -7: "WD_ERR_UNSUPPORTED"}
+
+
+class WDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.wd_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+
+
+class Launch(C.Structure):
+    """Launch configuration (wd_launch); 0 fields take the library default."""
+    _fields_ = [("rows_per_wave", C.c_int), ("waves_per_block", C.c_int),
+                ("order", C.c_int), ("xcd_remap", C.c_int)]
+
+
+_P, _I, _S = C.c_void_p, C.c_int, C.c_size_t
+_sig = {
+    "wd_gate_up": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "wd_gate_up_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, C.POINTER(Launch), _P]),
+    "wd_down": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "wd_down_ex": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, C.POINTER(Launch), _P]),
+    "wd_moe_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _I, _I, _I, _I, _I, _P]),
+    "wd_workspace_bytes": (_S, [_I, _I, _I]),
+    "wd_status_string": (C.c_char_p, [_I]),
+    "wd_dequant_probe": (_I, [_P, _P]),
+    "wd_stream_read": (_I, [_P, _S, _P, _I, _P]),
+    "wd_stream_blocks": (_I, []),
+    "wd_stream_copy": (_I, [_P, _P, _S, _I, _P]),
+    "wd_gpu_sleep": (_I, [_I, _P]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions include/wd.h declares."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(wd_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def _check(rc: int, where: str):
+    if rc != WD_OK:
+        raise WDError(rc, where)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t
+
+
+_U8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu)
+_BF16 = (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def _dims(w_gu: torch.Tensor):
+    E, I2, H = w_gu.shape
+    return E, H, I2 // 2
+
+
+def _cfg(cfg):
+    if cfg is None:
+        return None
+    if isinstance(cfg, Launch):
+        return C.byref(cfg)
+    return C.byref(Launch(**cfg))
+
+
+def gate_up(x, topk_ids, w_gu, s_gu, act=None, cfg=None, stream=None):
+    """act[B,K,I] (bf16) = BF16(SiLU(Gate x) * Up x) per (token, slot)."""
+    E, H, I = _dims(w_gu)
+    B, K = topk_ids.shape
+    _dev(x, "x", _BF16, (B, H)); _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(w_gu, "w_gu", _U8, (E, 2 * I, H)); _dev(s_gu, "s_gu", _U8, (E, 2 * I, H // 32))
+    if act is None:
+        act = torch.empty((B, K, I), dtype=torch.bfloat16, device=x.device)
+    _dev(act, "act", _BF16, (B, K, I))
+    if cfg is None:
+        rc = _lib.wd_gate_up(_ptr(x), _ptr(topk_ids), _ptr(w_gu), _ptr(s_gu), _ptr(act), B, K, E, H, I,
+                             _stream(stream))
+    else:
+        rc = _lib.wd_gate_up_ex(_ptr(x), _ptr(topk_ids), _ptr(w_gu), _ptr(s_gu), _ptr(act), B, K, E, H, I,
+                                _cfg(cfg), _stream(stream))
+    _check(rc, "wd_gate_up")
+    return act
+
+
+def down(act, topk_ids, topk_w, w_d, s_d, out=None, cfg=None, stream=None):
+    """out[B,H] (bf16) = sum_k topk_w[b,k] * Down_e act[b,k]."""
+    E, H, I = w_d.shape
+    B, K = topk_ids.shape
+    _dev(act, "act", _BF16, (B, K, I)); _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,), (B, K))
+    _dev(w_d, "w_d", _U8); _dev(s_d, "s_d", _U8, (E, H, I // 32))
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.bfloat16, device=act.device)
+    _dev(out, "out", _BF16, (B, H))
+    if cfg is None:
+        rc = _lib.wd_down(_ptr(act), _ptr(topk_ids), _ptr(topk_w), _ptr(w_d), _ptr(s_d), _ptr(out),
+                          B, K, E, H, I, _stream(stream))
+    else:
+        rc = _lib.wd_down_ex(_ptr(act), _ptr(topk_ids), _ptr(topk_w), _ptr(w_d), _ptr(s_d), _ptr(out),
+                             B, K, E, H, I, _cfg(cfg), _stream(stream))
+    _check(rc, "wd_down")
+    return out
+
+
+def workspace_bytes(B: int, K: int, I: int) -> int:
+    return _lib.wd_workspace_bytes(B, K, I)
+
+
+def moe_decode(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, out=None, workspace=None, stream=None):
+    """The whole layer (gate/up then down) on one stream; returns out[B,H] bf16."""
+    E, H, I = _dims(w_gu)
+    B, K = topk_ids.shape
+    _dev(x, "x", _BF16, (B, H)); _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,), (B, K))
+    _dev(w_gu, "w_gu", _U8, (E, 2 * I, H)); _dev(s_gu, "s_gu", _U8, (E, 2 * I, H // 32))
+    _dev(w_d, "w_d", _U8, (E, H, I)); _dev(s_d, "s_d", _U8, (E, H, I // 32))
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", _BF16, (B, H))
+    need = workspace_bytes(B, K, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", (torch.uint8, torch.bfloat16))
+    rc = _lib.wd_moe_decode(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gu), _ptr(s_gu), _ptr(w_d), _ptr(s_d),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                            B, K, E, H, I, _stream(stream))
+    _check(rc, "wd_moe_decode")
+    return out
+
+
+def dequant_probe(device="cuda", stream=None) -> torch.Tensor:
+    """[256 scales, 256 codes, 4 byte lanes] FP32 conversions (see wd.h)."""
+    out = torch.empty((256, 256, 4), dtype=torch.float32, device=device)
+    _check(_lib.wd_dequant_probe(_ptr(out), _stream(stream)), "wd_dequant_probe")
+    return out
+
+
+def stream_blocks() -> int:
+    return _lib.wd_stream_blocks()
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0, stream=None):
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.wd_stream_read(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)), "wd_stream_read")
+
+
+def stream_copy(dst: torch.Tensor, src: torch.Tensor, blocks: int = 0, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _check(_lib.wd_stream_copy(_ptr(dst), _ptr(src), nbytes, blocks, _stream(stream)), "wd_stream_copy")
+
+
+def gpu_sleep(units: int, stream=None):
+    _check(_lib.wd_gpu_sleep(units, _stream(stream)), "wd_gpu_sleep")
+
+
+# Raw entry points for callers that manage pointers themselves (tests, bench).
+raw = _lib

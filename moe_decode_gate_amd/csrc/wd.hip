@@ -1,0 +1,300 @@
+// Host side of the MoE decode library: argument checks, launch configuration
+// and the C entry points declared in include/wd.h.
+//
+// Every check runs before the first HIP call, so a rejected call touches no
+// device.  Compute entry points enqueue on the caller's stream and return
+// without synchronising, allocating or freeing.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+#include <cstring>
+
+#include "wd.h"
+#include "wd_kernels.h"
+
+namespace {
+
+using wd::LayerArgs;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+// The current device must be a gfx950 GPU.  Queried once per device.
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) { (void)hipGetLastError(); return WD_ERR_DEVICE; }
+    if (dev >= kMaxDevices) return WD_ERR_DEVICE;
+    int st = g_arch[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) { (void)hipGetLastError(); return WD_ERR_DEVICE; }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_arch[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? WD_OK : WD_ERR_DEVICE;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+int check_dims(int B, int K, int E, int H, int I) {
+    if (B < 0 || K < 1 || E < 1 || H < 32 || I < 32 || H % 32 || I % 32) return WD_ERR_DIMS;
+    if (H > 8192 || (long long)K * I > 16384) return WD_ERR_UNSUPPORTED;
+    if ((long long)B * K * I >= INT_MAX || (long long)B * H >= INT_MAX) return WD_ERR_UNSUPPORTED;
+    return WD_OK;
+}
+
+// Resolve a launch configuration: fill unset fields with the defaults for
+// this batch size, then validate.
+int resolve(const wd_launch *in, int B, bool down, wd_launch *out) {
+    wd_launch c = in ? *in : wd_launch{0, 0, 0, 0};
+    if (c.rows_per_wave == 0) c.rows_per_wave = down ? (B >= 8 ? 2 : 1) : (B >= 8 ? 2 : 1);
+    if (c.waves_per_block == 0) c.waves_per_block = 4;
+    if (c.order == 0) c.order = 1;
+    if (c.xcd_remap == 0) c.xcd_remap = 1;
+    if (c.rows_per_wave != 1 && c.rows_per_wave != 2 && c.rows_per_wave != 4) return WD_ERR_UNSUPPORTED;
+    if (c.waves_per_block < 1 || c.waves_per_block > 4) return WD_ERR_UNSUPPORTED;
+    if (c.order != 1 && c.order != 2) return WD_ERR_UNSUPPORTED;
+    if (c.xcd_remap != 1 && c.xcd_remap != 2) return WD_ERR_UNSUPPORTED;
+    *out = c;
+    return WD_OK;
+}
+
+int launched() {
+    return hipGetLastError() == hipSuccess ? WD_OK : WD_ERR_LAUNCH;
+}
+
+// ---- dispatch on compile-time chunk count and rows per wave -------------
+
+typedef void (*KernelFn)(LayerArgs);
+
+template <template <int, int, bool> class Sel, int CPL>
+KernelFn pick_r(int R, bool tail) {
+    switch (R) {
+        case 1: return tail ? Sel<CPL, 1, true>::fn() : Sel<CPL, 1, false>::fn();
+        case 2: return tail ? Sel<CPL, 2, true>::fn() : Sel<CPL, 2, false>::fn();
+        case 4: return tail ? Sel<CPL, 4, true>::fn() : Sel<CPL, 4, false>::fn();
+    }
+    return nullptr;
+}
+
+template <int CPL, int R, bool TAIL>
+struct GateUpSel { static KernelFn fn() { return wd::gate_up_kernel<CPL, R, TAIL>; } };
+template <int CPL, int R, bool TAIL>
+struct DownSel { static KernelFn fn() { return wd::down_kernel<CPL, R, TAIL>; } };
+
+// Smallest compiled chunks-per-lane >= need.
+int round_cpl_gate_up(int need) {
+    for (int c : {1, 2, 4, 8}) if (c >= need) return c;
+    return -1;
+}
+int round_cpl_down(int need) {
+    for (int c : {1, 2, 3, 4, 6, 8, 12, 16}) if (c >= need) return c;
+    return -1;
+}
+
+KernelFn gate_up_fn(int cpl, int R, bool tail) {
+    switch (cpl) {
+        case 1: return pick_r<GateUpSel, 1>(R, tail);
+        case 2: return pick_r<GateUpSel, 2>(R, tail);
+        case 4: return pick_r<GateUpSel, 4>(R, tail);
+        case 8: return pick_r<GateUpSel, 8>(R, tail);
+    }
+    return nullptr;
+}
+KernelFn down_fn(int cpl, int R, bool tail) {
+    switch (cpl) {
+        case 1: return pick_r<DownSel, 1>(R, tail);
+        case 2: return pick_r<DownSel, 2>(R, tail);
+        case 3: return pick_r<DownSel, 3>(R, tail);
+        case 4: return pick_r<DownSel, 4>(R, tail);
+        case 6: return pick_r<DownSel, 6>(R, tail);
+        case 8: return pick_r<DownSel, 8>(R, tail);
+        case 12: return pick_r<DownSel, 12>(R, tail);
+        case 16: return pick_r<DownSel, 16>(R, tail);
+    }
+    return nullptr;
+}
+
+int launch(KernelFn fn, LayerArgs a, int waves_per_block, hipStream_t s) {
+    const int blocks = (a.nwaves + waves_per_block - 1) / waves_per_block;
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+    return launched();
+}
+
+int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, const uint8_t *s_gu,
+                 uint16_t *act, int B, int K, int E, int H, int I, const wd_launch *cfg,
+                 void *stream, bool checked_device) {
+    int rc = check_dims(B, K, E, H, I);
+    if (rc) return rc;
+    if (!w_gu || !s_gu) return WD_ERR_NULL;
+    if (B > 0 && (!x || !ids || !act)) return WD_ERR_NULL;
+    if (!aligned(w_gu, 16) || (B > 0 && (!aligned(x, 16) || !aligned(act, 16) || !aligned(ids, 4))))
+        return WD_ERR_ALIGN;
+    wd_launch c;
+    if ((rc = resolve(cfg, B, false, &c))) return rc;
+    const int cpl = round_cpl_gate_up((H / 16 + 63) / 64);
+    if (cpl < 0) return WD_ERR_UNSUPPORTED;
+    if (B == 0) return WD_OK;
+    if (!checked_device && (rc = check_device())) return rc;
+    LayerArgs a{};
+    a.x = x; a.ids = ids; a.w = w_gu; a.s = s_gu; a.out = act;
+    a.B = B; a.K = K; a.E = E; a.H = H; a.I = I;
+    a.nrowblk = I / c.rows_per_wave;
+    a.nwaves = B * K * a.nrowblk;
+    a.order = c.order; a.remap = c.xcd_remap;
+    const bool tail = (H / 16) % (64 * cpl) != 0;
+    KernelFn fn = gate_up_fn(cpl, c.rows_per_wave, tail);
+    if (!fn) return WD_ERR_UNSUPPORTED;
+    return launch(fn, a, c.waves_per_block, (hipStream_t)stream);
+}
+
+int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const uint8_t *w_d,
+              const uint8_t *s_d, uint16_t *out, int B, int K, int E, int H, int I,
+              const wd_launch *cfg, void *stream, bool checked_device) {
+    int rc = check_dims(B, K, E, H, I);
+    if (rc) return rc;
+    if (!w_d || !s_d) return WD_ERR_NULL;
+    if (B > 0 && (!act || !ids || !tw || !out)) return WD_ERR_NULL;
+    if (!aligned(w_d, 16) ||
+        (B > 0 && (!aligned(act, 16) || !aligned(ids, 4) || !aligned(tw, 4) || !aligned(out, 2))))
+        return WD_ERR_ALIGN;
+    wd_launch c;
+    if ((rc = resolve(cfg, B, true, &c))) return rc;
+    const int nc = K * (I / 16);
+    const int cpl = round_cpl_down((nc + 63) / 64);
+    if (cpl < 0) return WD_ERR_UNSUPPORTED;
+    // Chunk -> slot division by multiply and shift: with magic = floor(2^22 / nci) + 1,
+    // (cc * magic) >> 22 == cc / nci for every cc < 1024 whenever nci <= 1024 (the
+    // rounding excess cc * (magic - 2^22 / nci) / 2^22 < 2^-12 cannot reach the next
+    // integer, whose distance is at least 1 / nci >= 2^-10).  check_dims bounds
+    // K * I <= 16384, so nc = K * I / 16 <= 1024 and nci <= 1024.
+    const uint32_t nci = (uint32_t)(I / 16);
+    const uint32_t magic = (uint32_t)((1u << 22) / nci + 1);
+    if (B == 0) return WD_OK;
+    if (!checked_device && (rc = check_device())) return rc;
+    LayerArgs a{};
+    a.act_in = act; a.ids = ids; a.tw = tw; a.w = w_d; a.s = s_d; a.out = out;
+    a.B = B; a.K = K; a.E = E; a.H = H; a.I = I;
+    a.nrowblk = H / c.rows_per_wave;
+    a.nwaves = B * a.nrowblk;
+    a.order = c.order; a.remap = c.xcd_remap;
+    a.nci_magic = magic;
+    const bool tail = nc % (64 * cpl) != 0;
+    KernelFn fn = down_fn(cpl, c.rows_per_wave, tail);
+    if (!fn) return WD_ERR_UNSUPPORTED;
+    return launch(fn, a, c.waves_per_block, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int wd_gate_up(const uint16_t *x, const int32_t *topk_ids, const uint8_t *w_gu, const uint8_t *s_gu,
+               uint16_t *act, int B, int K, int E, int H, int I, void *stream) {
+    return gate_up_impl(x, topk_ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, false);
+}
+
+int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids, const uint8_t *w_gu, const uint8_t *s_gu,
+                  uint16_t *act, int B, int K, int E, int H, int I, const wd_launch *cfg, void *stream) {
+    return gate_up_impl(x, topk_ids, w_gu, s_gu, act, B, K, E, H, I, cfg, stream, false);
+}
+
+int wd_down(const uint16_t *act, const int32_t *topk_ids, const float *topk_w, const uint8_t *w_d,
+            const uint8_t *s_d, uint16_t *out, int B, int K, int E, int H, int I, void *stream) {
+    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, false);
+}
+
+int wd_down_ex(const uint16_t *act, const int32_t *topk_ids, const float *topk_w, const uint8_t *w_d,
+               const uint8_t *s_d, uint16_t *out, int B, int K, int E, int H, int I,
+               const wd_launch *cfg, void *stream) {
+    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, cfg, stream, false);
+}
+
+size_t wd_workspace_bytes(int B, int K, int I) {
+    if (B < 0 || K < 1 || I < 32 || I % 32) return 0;
+    return (size_t)B * (size_t)K * (size_t)I * 2u;
+}
+
+int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                  const uint8_t *w_gu, const uint8_t *s_gu, const uint8_t *w_d, const uint8_t *s_d,
+                  void *workspace, size_t workspace_bytes, uint16_t *out,
+                  int B, int K, int E, int H, int I, void *stream) {
+    int rc = check_dims(B, K, E, H, I);
+    if (rc) return rc;
+    if (!w_gu || !s_gu || !w_d || !s_d) return WD_ERR_NULL;
+    if (B > 0 && (!x || !topk_ids || !topk_w || !out || !workspace)) return WD_ERR_NULL;
+    if (B > 0 && !aligned(workspace, 16)) return WD_ERR_ALIGN;
+    if (workspace_bytes < wd_workspace_bytes(B, K, I)) return WD_ERR_WORKSPACE;
+    uint16_t *act = static_cast<uint16_t *>(workspace);
+    // Check both halves' arguments before launching either.
+    if (!aligned(w_gu, 16) || !aligned(w_d, 16) ||
+        (B > 0 && (!aligned(x, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(out, 2))))
+        return WD_ERR_ALIGN;
+    if (B == 0) return WD_OK;
+    if ((rc = check_device())) return rc;
+    rc = gate_up_impl(x, topk_ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, true);
+    if (rc) return rc;
+    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, true);
+}
+
+const char *wd_status_string(int status) {
+    switch (status) {
+        case WD_OK: return "ok";
+        case WD_ERR_NULL: return "null pointer argument";
+        case WD_ERR_DIMS: return "bad dimensions (need B >= 0, K >= 1, E >= 1, H and I positive multiples of 32)";
+        case WD_ERR_ALIGN: return "misaligned pointer (16 bytes for x, weights, act, workspace; 4 for ids and weights; 2 for out)";
+        case WD_ERR_WORKSPACE: return "workspace smaller than wd_workspace_bytes(B, K, I)";
+        case WD_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+        case WD_ERR_LAUNCH: return "kernel launch failed";
+        case WD_ERR_UNSUPPORTED: return "unsupported sizes or launch configuration (H <= 8192, K*I <= 16384)";
+    }
+    return "unknown status";
+}
+
+int wd_dequant_probe(float *out, void *stream) {
+    if (!out) return WD_ERR_NULL;
+    if (!aligned(out, 16)) return WD_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    hipLaunchKernelGGL(wd::dequant_probe_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, out);
+    return launched();
+}
+
+int wd_stream_blocks(void) { return 256 * 32; }
+
+int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, void *stream) {
+    if (!buf || !sink) return WD_ERR_NULL;
+    if (bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return WD_ERR_ALIGN;
+    if (blocks <= 0) blocks = wd_stream_blocks();
+    if (blocks > wd_stream_blocks()) return WD_ERR_UNSUPPORTED;
+    int rc = check_device();
+    if (rc) return rc;
+    hipLaunchKernelGGL(wd::stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const wd::u32x4 *>(buf), bytes / 16, sink, 0x9E3779B9u);
+    return launched();
+}
+
+int wd_stream_copy(void *dst, const void *src, size_t bytes, int blocks, void *stream) {
+    if (!dst || !src) return WD_ERR_NULL;
+    if (bytes % 16 || !aligned(dst, 16) || !aligned(src, 16)) return WD_ERR_ALIGN;
+    if (blocks <= 0) blocks = wd_stream_blocks();
+    if (blocks > wd_stream_blocks()) return WD_ERR_UNSUPPORTED;
+    int rc = check_device();
+    if (rc) return rc;
+    hipLaunchKernelGGL(wd::stream_copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<wd::u32x4 *>(dst), static_cast<const wd::u32x4 *>(src), bytes / 16);
+    return launched();
+}
+
+int wd_gpu_sleep(int sleep_units, void *stream) {
+    if (sleep_units < 0 || sleep_units > (1 << 20)) return WD_ERR_UNSUPPORTED;
+    int rc = check_device();
+    if (rc) return rc;
+    hipLaunchKernelGGL(wd::sleep_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, sleep_units);
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Device helpers for the gfx950 MoE decode kernels: MXFP8 element conversion,
+// BF16 unpack/round, 64-lane wave reduction, XCD-aware workgroup numbering.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wd {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;      // CDNA wavefront width
+constexpr int kChunk = 16;     // elements per lane per 16-byte code load
+constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, each with its own L2
+
+// ---- loads ---------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// ---- MXFP8 ----------------------------------------------------------------
+
+// E8M0 block exponent byte -> the FP32 scale operand of the scaled FP8
+// conversion: the byte is placed in the FP32 exponent field, i.e. the value
+// 2^(s-127) for s in [1, 254].  (Bytes 0 and 255 land on FP32 zero / infinity;
+// what the hardware does with them is measured by the exhaustive probe.)
+__device__ __forceinline__ float e8m0_operand(uint32_t s) {
+    return __builtin_bit_cast(float, s << 23);
+}
+
+// Two E4M3 codes (byte pair 0-1 when hi == false, 2-3 when hi == true) times
+// the block scale, to FP32, with gfx950's v_cvt_scalef32_pk_f32_fp8.
+template <bool HI>
+__device__ __forceinline__ f32x2 mx_pair(uint32_t word, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, scale, HI);
+}
+
+// ---- BF16 -----------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// FP32 -> BF16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// ---- 16-element dot products ----------------------------------------------
+
+// acc + sum_{i<16} deq(codes[i], scale) * v[i]: codes packed 4 per word (byte
+// 0 is the lowest-index element), v in FP32; one FMA per element, in index
+// order.
+__device__ __forceinline__ float dot16_f32(u32x4 q, float scale, const float *v, float acc) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        f32x2 lo = mx_pair<false>(q[d], scale);
+        f32x2 hi = mx_pair<true>(q[d], scale);
+        acc = __builtin_fmaf(lo.x, v[4 * d + 0], acc);
+        acc = __builtin_fmaf(lo.y, v[4 * d + 1], acc);
+        acc = __builtin_fmaf(hi.x, v[4 * d + 2], acc);
+        acc = __builtin_fmaf(hi.y, v[4 * d + 3], acc);
+    }
+    return acc;
+}
+
+// Same with the 16 activations given as packed BF16 pairs (a0: elements 0-7,
+// a1: elements 8-15; the low half of each word is the lower index).
+__device__ __forceinline__ float dot16_bf16(u32x4 q, float scale, u32x4 a0, u32x4 a1, float acc) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        f32x2 lo = mx_pair<false>(q[d], scale);
+        f32x2 hi = mx_pair<true>(q[d], scale);
+        const uint32_t p0 = d < 2 ? a0[2 * d] : a1[2 * d - 4];
+        const uint32_t p1 = d < 2 ? a0[2 * d + 1] : a1[2 * d - 3];
+        acc = __builtin_fmaf(lo.x, bf16_lo(p0), acc);
+        acc = __builtin_fmaf(lo.y, bf16_hi(p0), acc);
+        acc = __builtin_fmaf(hi.x, bf16_lo(p1), acc);
+        acc = __builtin_fmaf(hi.y, bf16_hi(p1), acc);
+    }
+    return acc;
+}
+
+// ---- 64-lane reduction ----------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Butterfly sum over the 64 lanes of a wave; every lane returns the same,
+// bit-identical total.  Within each row of 16 lanes: DPP quad_perm xor-1 and
+// xor-2, then half-row mirror and row mirror (each lane adds the partner that
+// holds the other half's partial).  Across rows: v_permlane16_swap pairs rows
+// (0,1) and (2,3), v_permlane32_swap pairs the two halves.  No LDS, no barrier.
+// Must run with all 64 lanes active.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror
+    v += dpp_mov<0x140>(v);   // row_mirror
+    {
+        uint32_t u = __builtin_bit_cast(uint32_t, v);
+        auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+    }
+    {
+        uint32_t u = __builtin_bit_cast(uint32_t, v);
+        auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+    }
+    return v;
+}
+
+// ---- workgroup numbering ----------------------------------------------------
+
+// Workgroups are handed to the XCDs round-robin (workgroup g runs on XCD
+// g % 8).  Renumber so XCD x processes one contiguous range of logical
+// workgroups, in order: work adjacent in the logical order then shares an L2.
+// A bijection on [0, n) for any n.
+__device__ __forceinline__ int xcd_logical(int g, int n) {
+    const int x = g % kXcds, q = g / kXcds;
+    const int base = n / kXcds, rem = n % kXcds;
+    return x * base + (x < rem ? x : rem) + q;
+}
+
+}  // namespace wd

@@ -1,0 +1,234 @@
+// The two gfx950 kernels of the output-neuron-centric MoE decode layer.
+//
+// Gate/up (the write-ups' moe_gate_up_3d_batched) and down
+// (moe_down_3d_batched): "Better MoE model inference with warp decode", Key
+// claims, section "How the two kernels work", and the Chinese summary's
+// 技术原理 section with its Gate/Up and Down kernel subsections.  Each 64-lane
+// wave owns output values for its whole life, streams the MXFP8 weight rows
+// it needs straight from HBM into registers, converts them to FP32 as it
+// reads them, keeps a private FP32 accumulator and finishes with a cross-lane
+// butterfly; waves never exchange data, so there is no LDS traffic, no
+// barrier and no atomic.
+#pragma once
+
+#include "wd_device.h"
+
+namespace wd {
+
+// Kernel arguments shared by both kernels.
+struct LayerArgs {
+    const uint16_t *x;       // [B,H] bf16
+    const int32_t *ids;      // [B,K]
+    const float *tw;         // [B,K]
+    const uint8_t *w;        // gate/up: [E,2I,H] codes; down: [E,H,I] codes
+    const uint8_t *s;        // matching E8M0 bytes
+    const uint16_t *act_in;  // down: [B,K,I] bf16
+    uint16_t *out;           // gate/up: act [B,K,I]; down: out [B,H]
+    int B, K, E, H, I;
+    int nwaves;              // logical waves in the grid
+    int nrowblk;             // row blocks (I / R for gate/up, H / R for down)
+    int order;               // 1: row-block major, 2: token/slot major
+    int remap;               // 1: XCD-contiguous workgroup numbering
+    uint32_t nci_magic;      // down: floor(2^22 / (I/16)) + 1; (c * magic) >> 22 == c / (I/16) for all chunks c
+};
+
+// Logical wave index of the calling wave (wave-uniform, kept in an SGPR).
+__device__ __forceinline__ int logical_wave(const LayerArgs &a) {
+    const int g = a.remap == 1 ? xcd_logical((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+    return __builtin_amdgcn_readfirstlane(g * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6));
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up: one wave per (token b, slot k, block of R intermediate rows).
+//
+// Lane l owns 16-element chunks c = l + 64 i (i < CPL) of the H axis: each
+// 16-byte code load of a row is then one fully coalesced 1 KiB wave access.
+// x[b] is loaded once per wave, converted to FP32 once, and reused by the
+// gate and the up row of all R rows.  TAIL handles H/16 not a multiple of
+// 64 * CPL (lanes past the row end contribute exact zeros).
+// ---------------------------------------------------------------------------
+template <int CPL, int R, bool TAIL>
+__global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = logical_wave(a);
+    if (t >= a.nwaves) return;                       // wave-uniform exit
+
+    int b, k, jb;
+    if (a.order == 1) {                              // t = (jb * B + b) * K + k
+        k = t % a.K; const int r = t / a.K; b = r % a.B; jb = r / a.B;
+    } else {                                         // t = (b * K + k) * nrowblk + jb
+        jb = t % a.nrowblk; const int r = t / a.nrowblk; k = r % a.K; b = r / a.K;
+    }
+    const int H = a.H, I = a.I;
+    const int NC = H >> 4;                           // chunks per row
+    int e = a.ids[b * a.K + k];
+    const bool bad = (unsigned)e >= (unsigned)a.E;   // never read out of bounds for a bad id
+    if (bad) e = 0;
+
+    // x[b] -> FP32 registers, chunk by chunk.
+    float xv[CPL][16];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        const int cc = (!TAIL || c < NC) ? c : 0;
+        const uint16_t *xp = a.x + (size_t)b * H + cc * 16;
+        const u32x4 p0 = ld16(xp), p1 = ld16(xp + 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xv[i][2 * q] = bf16_lo(p0[q]);
+            xv[i][2 * q + 1] = bf16_hi(p0[q]);
+            xv[i][8 + 2 * q] = bf16_lo(p1[q]);
+            xv[i][8 + 2 * q + 1] = bf16_hi(p1[q]);
+        }
+    }
+
+    const size_t nbr = (size_t)(H >> 5);             // scale bytes per row
+    const size_t erow = (size_t)e * 2 * I;           // first row of expert e
+    float res[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int j = jb * R + r;
+        const uint8_t *wg = a.w + (erow + j) * (size_t)H;
+        const uint8_t *wu = wg + (size_t)I * H;
+        const uint8_t *sg = a.s + (erow + j) * nbr;
+        const uint8_t *su = sg + (size_t)I * nbr;
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const bool ok = !TAIL || c < NC;
+            const int cc = ok ? c : 0;
+            const u32x4 qg = ld16(wg + cc * 16);
+            const u32x4 qu = ld16(wu + cc * 16);
+            const float fg = e8m0_operand(sg[cc >> 1]);
+            const float fu = e8m0_operand(su[cc >> 1]);
+            const float g2 = dot16_f32(qg, fg, xv[i], g);
+            const float u2 = dot16_f32(qu, fu, xv[i], u);
+            g = ok ? g2 : g;                         // lanes past the row end add nothing
+            u = ok ? u2 : u;
+        }
+        g = wave_sum(g);
+        u = wave_sum(u);
+        // SiLU(g) * u in FP32; sigmoid written so that exp never overflows.
+        const float en = expf(-__builtin_fabsf(g));
+        const float sig = g >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
+        res[r] = bad ? __builtin_nanf("") : g * sig * u;
+    }
+    float mine = res[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) mine = lane == r ? res[r] : mine;
+    if (lane < R)
+        a.out[((size_t)b * a.K + k) * I + (size_t)jb * R + lane] = to_bf16(mine);
+}
+
+// ---------------------------------------------------------------------------
+// Down: one wave per (token b, block of R output dims).
+//
+// The K routed rows Wd[e_k, h, 0:I] of one output dim are cut into 16-element
+// chunks and the K * I / 16 chunks are dealt to the lanes (chunk c = l + 64 i),
+// so each lane streams from one or more experts and every lane is busy for
+// any I that is a multiple of 32.  Lane-held act chunks (packed BF16) and the
+// chunk's router weight are loaded once per wave and reused for all R dims.
+// Per chunk the lane forms p = sum deq * act in FP32 and folds the router
+// weight in with one FMA, acc += w_k * p.
+// ---------------------------------------------------------------------------
+template <int CPL, int R, bool TAIL>
+__global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = logical_wave(a);
+    if (t >= a.nwaves) return;
+
+    int b, hb;
+    if (a.order == 1) { b = t % a.B; hb = t / a.B; }        // t = hb * B + b
+    else { hb = t % a.nrowblk; b = t / a.nrowblk; }         // t = b * nrowblk + hb
+    const int H = a.H, I = a.I, K = a.K;
+    const int NCI = I >> 4;                                  // chunks per expert row
+    const int NC = K * NCI;
+    const size_t nbr = (size_t)(I >> 5);
+
+    size_t wbase[CPL];      // byte offset of (e_k, h = 0, chunk) in Wd
+    size_t sbase[CPL];      // byte offset of its E8M0 byte in Sd
+    float wk[CPL];
+    u32x4 av0[CPL], av1[CPL];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        const bool ok = !TAIL || c < NC;
+        const int cc = ok ? c : 0;
+        const int kk = (int)(((uint64_t)cc * a.nci_magic) >> 22);   // cc / NCI (checked on the host)
+        const int ci = cc - kk * NCI;
+        int e = a.ids[b * K + kk];
+        bad |= ok && (unsigned)e >= (unsigned)a.E;
+        if ((unsigned)e >= (unsigned)a.E) e = 0;
+        wbase[i] = (size_t)e * H * I + (size_t)ci * 16;
+        sbase[i] = (size_t)e * H * nbr + (size_t)(ci >> 1);
+        wk[i] = a.tw[b * K + kk];
+        const uint16_t *ap = a.act_in + ((size_t)b * K + kk) * I + (size_t)ci * 16;
+        av0[i] = ld16(ap);
+        av1[i] = ld16(ap + 8);
+    }
+
+    float res[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const size_t h = (size_t)hb * R + r;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const u32x4 q = ld16(a.w + wbase[i] + h * I);
+            const float f = e8m0_operand(a.s[sbase[i] + h * nbr]);
+            const float p = dot16_bf16(q, f, av0[i], av1[i], 0.f);
+            const float acc2 = __builtin_fmaf(wk[i], p, acc);
+            acc = (!TAIL || (lane + 64 * i) < NC) ? acc2 : acc;
+        }
+        if (bad) acc = __builtin_nanf("");
+        res[r] = wave_sum(acc);
+    }
+    float mine = res[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) mine = lane == r ? res[r] : mine;
+    if (lane < R) a.out[(size_t)b * H + (size_t)hb * R + lane] = to_bf16(mine);
+}
+
+// ---------------------------------------------------------------------------
+// Measurement helpers.
+// ---------------------------------------------------------------------------
+
+// For E8M0 byte s = blockIdx.x and code c = threadIdx.x: the conversion of
+// the four codes c, c+1, c+2, c+3 (mod 256) packed in one word, bytes 0..3,
+// exactly as the layer kernels perform it (same operand construction, same
+// instruction).  out[((s * 256) + c) * 4 + j] holds the result for byte j.
+__global__ __launch_bounds__(256) void dequant_probe_kernel(float *out) {
+    const uint32_t s = blockIdx.x, c = threadIdx.x;
+    const uint32_t word = (c & 255u) | (((c + 1) & 255u) << 8) | (((c + 2) & 255u) << 16) | (((c + 3) & 255u) << 24);
+    const float f = e8m0_operand(s);
+    const f32x2 lo = mx_pair<false>(word, f);
+    const f32x2 hi = mx_pair<true>(word, f);
+    float *o = out + ((size_t)s * 256 + c) * 4;
+    o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+}
+
+// Reads n16 16-byte words.  Each lane folds its words into an XOR; the sink is
+// written only if that fold equals `never` (a value the caller chooses so it
+// does not occur), which keeps every load live without a reduction.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *buf, size_t n16, uint32_t *sink, uint32_t never) {
+    uint32_t acc = 0;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const u32x4 v = buf[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (acc == never) sink[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(u32x4 *dst, const u32x4 *src, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+__global__ void sleep_kernel(int units) {
+    for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+}  // namespace wd

@@ -17,3 +17,18 @@ def pytest_configure(config):
 def rng():
     import numpy as np
     return np.random.default_rng(1234)
+
+
+def _ensure_built():
+    """Build the oracle and the HIP library in-tree if a built copy is missing
+    (both builds are CPU-only: hipcc cross-compiles for gfx950)."""
+    lib = os.path.join(ROOT, "moe_decode_gate_amd", "lib", "libwd.so")
+    if not os.path.exists(lib):
+        from moe_decode_gate_amd import build as b
+        b.build()
+    if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
+        from oracle import build as ob
+        ob.build()
+
+
+_ensure_built()

@@ -1,0 +1,112 @@
+"""Helpers shared by the GPU parity tests: device copies of seeded layers,
+calls through the C ABI (via the binding), and the comparison metrics."""
+from __future__ import annotations
+
+import math
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+from moe_decode_gate_amd import inputs as gen
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class DevLayer:
+    """Device copies (uint8 tensors) of one layer's MXFP8 weights."""
+
+    def __init__(self, L: gen.Layer, device="cuda"):
+        self.spec = L.spec
+        self.host = L
+        self.wgu = torch.from_numpy(L.wgu).to(device)
+        self.sgu = torch.from_numpy(L.sgu).to(device)
+        self.wd = torch.from_numpy(L.wd).to(device)
+        self.sd = torch.from_numpy(L.sd).to(device)
+
+
+class DevTokens:
+    def __init__(self, t: gen.Tokens, device="cuda"):
+        self.host = t
+        self.x = torch.from_numpy(t.x.view(np.int16)).to(device).view(torch.bfloat16)
+        self.ids = torch.from_numpy(t.ids).to(device)
+        self.w = torch.from_numpy(t.w).to(device)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> host uint16 bit patterns."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of BF16 numbers at |v| (normal range)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = a.ravel().astype(np.float64); b = b.ravel().astype(np.float64)
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def act_flip_stats(gpu_bits: np.ndarray, ora_bits: np.ndarray):
+    """(fraction of differing elements, max difference in BF16 ulps of the oracle value)."""
+    diff = gpu_bits != ora_bits
+    if not diff.any():
+        return 0.0, 0.0
+    g = bf16_bits_to_f64(gpu_bits[diff]); o = bf16_bits_to_f64(ora_bits[diff])
+    ulps = np.abs(g - o) / bf16_ulp(o)
+    return float(diff.mean()), float(ulps.max())
+
+
+def unit_shift(y64: np.ndarray) -> int:
+    """Integer k with max|y| * 2^k in [0.5, 1): shifting every down-projection
+    E8M0 byte by k scales the layer's output by exactly 2^k."""
+    m = float(np.abs(y64).max())
+    return -int(math.floor(math.log2(m))) - 1
+
+
+def shifted(sd: torch.Tensor, k: int) -> torch.Tensor:
+    return (sd.to(torch.int32) + k).to(torch.uint8)
+
+
+def parity_report(out_bits: np.ndarray, y64: np.ndarray) -> dict:
+    y = bf16_bits_to_f64(out_bits)
+    err = np.abs(y - y64)
+    tol = 0.5 * bf16_ulp(y64) + 2e-5 * float(np.abs(y64).max())
+    return dict(cos=cosine(y, y64), max_err=float(err.max()), max_ref=float(np.abs(y64).max()),
+                worst_ratio=float((err / tol).max()), n=int(y.size),
+                finite=bool(np.isfinite(y).all()))
+
+
+def assert_output_parity(out_bits: np.ndarray, y64: np.ndarray, what: str, unit_scale: bool = True):
+    """Output gates: cosine >= 0.99999 and, on outputs of unit magnitude, max
+    |err| <= 4e-3; and per element, the BF16 output is within half a BF16 ulp
+    of the FP64 oracle plus 2e-5 of the output range (FP32 summation)."""
+    r = parity_report(out_bits, y64)
+    log(f"[parity] {what}: {r}")
+    assert r["finite"], what
+    assert r["cos"] >= 0.99999, (what, r)
+    if unit_scale:
+        assert 0.5 <= r["max_ref"] < 1.0 or r["max_ref"] == 0.0, (what, r)
+        assert r["max_err"] <= 4e-3, (what, r)
+    assert r["worst_ratio"] <= 1.0, (what, r)
+    return r
+
+
+def run_layer(dl: DevLayer, dt: DevTokens, sd: Optional[torch.Tensor] = None, cfg_gu=None, cfg_dn=None):
+    """gate/up then down through the two C entry points; returns (act, out) tensors."""
+    from moe_decode_gate_amd import binding as wd
+    act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu, cfg=cfg_gu)
+    out = wd.down(act, dt.ids, dt.w, dl.wd, dl.sd if sd is None else sd, cfg=cfg_dn)
+    torch.cuda.synchronize()
+    return act, out

@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/wd.h declares, and rejects bad arguments on the host before any
+device call."""
+import ctypes as C
+
+import pytest
+
+from moe_decode_gate_amd import binding as wd
+
+A = 0x10000          # a 16-byte-aligned stand-in address; never dereferenced here
+lib = wd.raw
+
+
+def test_every_declared_symbol_is_exported():
+    names = wd.header_functions()
+    assert {"wd_gate_up", "wd_down", "wd_moe_decode", "wd_workspace_bytes", "wd_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert lib.wd_status_string(s)
+    assert lib.wd_status_string(123) == b"unknown status"
+
+
+def test_workspace_bytes():
+    assert lib.wd_workspace_bytes(32, 8, 768) == 32 * 8 * 768 * 2
+    assert lib.wd_workspace_bytes(0, 8, 768) == 0
+    assert lib.wd_workspace_bytes(1, 0, 768) == 0
+    assert lib.wd_workspace_bytes(1, 8, 100) == 0
+
+
+def gu(x=A, ids=A, w=A, s=A, act=A, B=1, K=8, E=128, H=2048, I=768):
+    return lib.wd_gate_up(x, ids, w, s, act, B, K, E, H, I, None)
+
+
+def dn(act=A, ids=A, tw=A, w=A, s=A, out=A, B=1, K=8, E=128, H=2048, I=768):
+    return lib.wd_down(act, ids, tw, w, s, out, B, K, E, H, I, None)
+
+
+def md(ws_bytes=1 << 20, ws=A, **kw):
+    d = dict(x=A, ids=A, tw=A, wgu=A, sgu=A, wd=A, sd=A, out=A, B=1, K=8, E=128, H=2048, I=768)
+    d.update(kw)
+    return lib.wd_moe_decode(d["x"], d["ids"], d["tw"], d["wgu"], d["sgu"], d["wd"], d["sd"], ws, ws_bytes,
+                             d["out"], d["B"], d["K"], d["E"], d["H"], d["I"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(H=100), dict(I=48), dict(K=0), dict(E=0), dict(B=-1), dict(H=0), dict(I=16)])
+def test_bad_dims(kw):
+    assert gu(**kw) == -2
+    assert dn(**kw) == -2
+    assert md(**kw) == -2
+
+
+@pytest.mark.parametrize("kw", [dict(H=8192 + 32), dict(K=32, I=1024)])
+def test_unsupported_sizes(kw):
+    assert gu(**kw) == -7 or dn(**kw) == -7
+
+
+def test_null_pointers():
+    assert gu(x=None) == -1 and gu(w=None) == -1 and gu(act=None) == -1
+    assert dn(tw=None) == -1 and dn(out=None) == -1 and dn(s=None) == -1
+    assert md(ws=None) == -1 and md(wd=None) == -1
+
+
+def test_misaligned():
+    assert gu(x=A + 8) == -3 and gu(w=A + 4) == -3 and gu(ids=A + 2) == -3
+    assert dn(act=A + 8) == -3 and dn(out=A + 1) == -3 and dn(tw=A + 2) == -3
+    assert md(ws=A + 8) == -3
+
+
+def test_workspace_too_small():
+    assert md(ws_bytes=1 * 8 * 768 * 2 - 1) == -4
+
+
+def test_empty_batch_launches_nothing():
+    # B = 0 is valid and returns before any device query, with NULL activations
+    assert gu(x=None, ids=None, act=None, B=0) == 0
+    assert dn(act=None, ids=None, tw=None, out=None, B=0) == 0
+    assert md(ws=None, ws_bytes=0, x=None, ids=None, tw=None, out=None, B=0) == 0
+
+
+def test_bad_launch_config_rejected():
+    for cfg in (wd.Launch(3, 0, 0, 0), wd.Launch(0, 5, 0, 0), wd.Launch(0, 0, 3, 0), wd.Launch(0, 0, 0, 7)):
+        assert lib.wd_gate_up_ex(A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(cfg), None) == -7
+        assert lib.wd_down_ex(A, A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(cfg), None) == -7
+
+
+def test_helpers_reject_bad_arguments():
+    assert lib.wd_dequant_probe(None, None) == -1
+    assert lib.wd_dequant_probe(A + 4, None) == -3
+    assert lib.wd_stream_read(A, 15, A, 0, None) == -3
+    assert lib.wd_stream_read(A, 16, A, lib.wd_stream_blocks() + 1, None) == -7
+    assert lib.wd_stream_copy(None, A, 16, 0, None) == -1
+    assert lib.wd_gpu_sleep(-1, None) == -7
+
+
+def test_chunk_to_slot_division_is_exact():
+    # The down kernel maps chunk c to slot c // (I/16) by (c * magic) >> 22 with
+    # magic = 2^22 // nci + 1; exact for every chunk of every supported size.
+    for nci in range(2, 1025, 2):                  # I = 16 * nci, I a multiple of 32
+        magic = (1 << 22) // nci + 1
+        K_max = 16384 // (16 * nci)
+        for c in range(min(1024, K_max * nci)):
+            assert (c * magic) >> 22 == c // nci

@@ -1,0 +1,214 @@
+"""Bit-exact GPU checks of indexing, routing and determinism.
+
+All arithmetic in the fingerprint layer is exact in FP32, so any wrong expert,
+row, column, scale block, slot or router weight shows up as a changed integer.
+The remaining tests compare the HIP path with itself under transformations
+that must leave the bits unchanged (token permutation, launch configuration,
+zero-weight slots) or scale them exactly (down-projection E8M0 shift).
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_decode_gate_amd import inputs as gen
+from tests.gpu_common import DevLayer, DevTokens, bits_of, log, run_layer, shifted
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _e4m3_int(v: int) -> int:
+    """E4M3 code of a small positive integer 1..15 (exact)."""
+    if v == 1:
+        return 0x38
+    e = v.bit_length() - 1
+    m = (v - (1 << e)) << (3 - e) if e <= 3 else 0
+    return ((e + 7) << 3) | m
+
+
+def fingerprint_layer(E, K, H, I):
+    """x = 1; gate row = code 1.0 under scale 2^1 (value 2) so g = 2H and
+    SiLU(g) = g exactly in FP32; up row j of expert e = the single integer
+    u(e,j) = (7e + 3j) % 15 + 1 at column j % H; down row h of expert e = one
+    1.0 at column i(e,h) = (h + e) % I with block scale 2^((h + e) % 3).
+    Scale bytes of the other blocks are 2^-20 so a wrong block is visible."""
+    wgu = np.zeros((E, 2 * I, H), np.uint8)
+    sgu = np.full((E, 2 * I, H // 32), 127 - 20, np.uint8)
+    wgu[:, :I, :] = 0x38
+    sgu[:, :I, :] = 128
+    u = np.zeros((E, I), np.int64)
+    for e in range(E):
+        for j in range(I):
+            u[e, j] = (7 * e + 3 * j) % 15 + 1
+            wgu[e, I + j, j % H] = _e4m3_int(int(u[e, j]))
+            sgu[e, I + j, (j % H) // 32] = 127
+    wd = np.zeros((E, H, I), np.uint8)
+    sd = np.full((E, H, I // 32), 127 - 20, np.uint8)
+    for e in range(E):
+        for h in range(H):
+            i = (h + e) % I
+            wd[e, h, i] = 0x38
+            sd[e, h, i // 32] = 127 + (h + e) % 3
+    spec = gen.LayerSpec(E=E, K=K, H=H, I=I, seed=0)
+    return gen.Layer(spec, wgu, sgu, wd, sd, tuple(range(E))), u
+
+
+def fingerprint_expect(u, ids, w, H, I):
+    """Closed form: act[b,k,j] = 2H u(e,j); y[b,h] = sum_k w_k 2H u(e, i) 2^((h+e)%3), i = (h+e)%I."""
+    B, K = ids.shape
+    y = np.zeros((B, H), np.float64)
+    act = np.zeros((B, K, I), np.float64)
+    for b in range(B):
+        for k in range(K):
+            e = int(ids[b, k])
+            act[b, k] = 2 * H * u[e]
+            for h in range(H):
+                y[b, h] += float(w[b, k]) * 2 * H * u[e, (h + e) % I] * 2.0 ** ((h + e) % 3)
+    return act, y
+
+
+def _bf16_bits(v: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("E,K,H,I,B", [(128, 8, 2048, 768, 32), (8, 2, 128, 64, 3), (5, 3, 96, 160, 4)])
+def test_routing_fingerprint_bit_exact(E, K, H, I, B):
+    log(f"[case] fingerprint E={E} K={K} H={H} I={I} B={B}")
+    L, u = fingerprint_layer(E, K, H, I)
+    rng = np.random.default_rng(E + K + H + I + B)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(B)]).astype(np.int32)
+    w = np.array([[2.0 ** -(k + 1) for k in range(K)]] * B, np.float32)
+    x = np.full((B, H), 0x3F80, np.uint16)
+    dl, dt = DevLayer(L), DevTokens(gen.Tokens(x=x, ids=ids, w=w))
+    act, out = run_layer(dl, dt)
+    act_e, y_e = fingerprint_expect(u, ids, w, H, I)
+    assert np.array_equal(bits_of(act), _bf16_bits(act_e))       # act values are exact in BF16
+    assert np.array_equal(bits_of(out), _bf16_bits(y_e))         # y exact in FP32, then one RNE
+
+
+@pytest.fixture(scope="module")
+def mid():
+    spec = gen.LayerSpec(E=32, K=4, H=1536, I=320, seed=77)     # both kernels with a lane tail
+    L = gen.make_layer(spec, threads=16)
+    t = gen.make_tokens(spec, 9)
+    return DevLayer(L), t
+
+
+def test_token_permutation_bit_exact(mid):
+    dl, t = mid
+    _, out = run_layer(dl, DevTokens(t))
+    p = np.random.default_rng(0).permutation(t.ids.shape[0])
+    tp = gen.Tokens(x=t.x[p].copy(), ids=t.ids[p].copy(), w=t.w[p].copy())
+    _, outp = run_layer(dl, DevTokens(tp))
+    assert np.array_equal(bits_of(outp), bits_of(out)[p])
+
+
+@pytest.mark.parametrize("k", [1, 3, -2])
+def test_down_scale_shift_scales_output_exactly(mid, k):
+    dl, t = mid
+    dt = DevTokens(t)
+    _, out = run_layer(dl, dt)
+    _, outk = run_layer(dl, dt, sd=shifted(dl.sd, k))
+    want = (torch.from_numpy(bits_of(out).view(np.int16)).view(torch.bfloat16).float() * 2.0 ** k)
+    assert np.array_equal(bits_of(outk), want.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def test_zero_weight_slot_ignores_its_expert(mid):
+    dl, t = mid
+    w = t.w.copy(); w[:, 2] = 0.0
+    ids2 = t.ids.copy(); ids2[:, 2] = (ids2[:, 2] + 5) % dl.spec.E
+    _, a = run_layer(dl, DevTokens(gen.Tokens(x=t.x, ids=t.ids, w=w)))
+    _, b = run_layer(dl, DevTokens(gen.Tokens(x=t.x, ids=ids2, w=w)))
+    assert np.array_equal(bits_of(a), bits_of(b))
+
+
+def test_deterministic_and_full_coverage(mid):
+    """Outputs pre-filled with NaN are fully overwritten; reruns are bit-identical."""
+    from moe_decode_gate_amd import binding as wd
+    dl, t = mid
+    dt = DevTokens(t)
+    B, K = t.ids.shape
+    act = torch.full((B, K, dl.spec.I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((B, dl.spec.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu, act=act)
+    wd.down(act, dt.ids, dt.w, dl.wd, dl.sd, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(act.float()).all() and torch.isfinite(out.float()).all()
+    a1, o1 = bits_of(act), bits_of(out)
+    for _ in range(3):
+        a2, o2 = run_layer(dl, dt)
+        assert np.array_equal(bits_of(a2), a1) and np.array_equal(bits_of(o2), o1)
+
+
+def test_launch_configurations_agree_bitwise(mid):
+    """Rows per wave, waves per workgroup, work order and XCD numbering change
+    only which wave computes an output, never how: results are bit-identical."""
+    dl, t = mid
+    dt = DevTokens(t)
+    a0, o0 = run_layer(dl, dt)
+    a0, o0 = bits_of(a0), bits_of(o0)
+    for r in (1, 2, 4):
+        for wpb in (1, 3, 4):
+            for order in (1, 2):
+                for remap in (1, 2):
+                    cfg = dict(rows_per_wave=r, waves_per_block=wpb, order=order, xcd_remap=remap)
+                    a, o = run_layer(dl, dt, cfg_gu=cfg, cfg_dn=cfg)
+                    assert np.array_equal(bits_of(a), a0), cfg
+                    assert np.array_equal(bits_of(o), o0), cfg
+
+
+def test_fused_entry_matches_two_calls(mid):
+    from moe_decode_gate_amd import binding as wd
+    dl, t = mid
+    dt = DevTokens(t)
+    _, o = run_layer(dl, dt)
+    out = wd.moe_decode(dt.x, dt.ids, dt.w, dl.wgu, dl.sgu, dl.wd, dl.sd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), bits_of(o))
+
+
+def test_side_stream(mid):
+    from moe_decode_gate_amd import binding as wd
+    dl, t = mid
+    dt = DevTokens(t)
+    _, o = run_layer(dl, dt)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = wd.moe_decode(dt.x, dt.ids, dt.w, dl.wgu, dl.sgu, dl.wd, dl.sd)
+    s.synchronize()
+    assert np.array_equal(bits_of(out), bits_of(o))
+
+
+def test_out_of_range_id_poisons_only_its_token(mid):
+    """An expert id outside [0, E) is never dereferenced: its intermediate row
+    is NaN and its token's outputs are NaN; other tokens are unchanged."""
+    dl, t = mid
+    a0, o0 = run_layer(dl, DevTokens(t))
+    ids = t.ids.copy()
+    ids[2, 1] = dl.spec.E
+    ids[5, 3] = -1
+    a, o = run_layer(dl, DevTokens(gen.Tokens(x=t.x, ids=ids, w=t.w)))
+    af, of = a.float().cpu().numpy(), o.float().cpu().numpy()
+    assert np.isnan(af[2, 1]).all() and np.isnan(af[5, 3]).all()
+    assert np.isnan(of[2]).all() and np.isnan(of[5]).all()
+    keep = [b for b in range(ids.shape[0]) if b not in (2, 5)]
+    assert np.array_equal(bits_of(o)[keep], bits_of(o0)[keep])
+
+
+def test_empty_batch():
+    from moe_decode_gate_amd import binding as wd
+    spec = gen.LayerSpec(E=4, K=2, H=64, I=32, seed=1)
+    dl = DevLayer(gen.make_layer(spec))
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    out = wd.moe_decode(x, ids, w, dl.wgu, dl.sgu, dl.wd, dl.sd)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
