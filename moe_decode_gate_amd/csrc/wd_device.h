@@ -89,28 +89,28 @@ __device__ __forceinline__ float dpp_mov(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Butterfly sum over the 64 lanes of a wave; every lane returns the same,
-// bit-identical total.  Within each row of 16 lanes: DPP quad_perm xor-1 and
-// xor-2, then half-row mirror and row mirror (each lane adds the partner that
-// holds the other half's partial).  Across rows: v_permlane16_swap pairs rows
-// (0,1) and (2,3), v_permlane32_swap pairs the two halves.  No LDS, no barrier.
-// Must run with all 64 lanes active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_upd(float v) {
+    // lanes of rows outside ROW_MASK receive 0 (the `old` operand)
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave, returned to every lane (bit-identical).
+// Within each row of 16 lanes, a butterfly: DPP quad_perm xor-1 and xor-2,
+// then half-row mirror and row mirror, after which every lane of row r holds
+// the row sum S_r.  Across rows, the GFX9 row broadcasts: row_bcast:15 adds
+// S_0 into row 1 and S_2 into row 3, row_bcast:31 adds row 1 (S_0 + S_1) into
+// row 3, so lane 63 holds (S_2 + S_3) + (S_0 + S_1); v_readlane hands it to
+// all lanes.  No LDS, no barrier.  Must run with all 64 lanes active.
 __device__ __forceinline__ float wave_sum(float v) {
-    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp_mov<0x141>(v);   // row_half_mirror
-    v += dpp_mov<0x140>(v);   // row_mirror
-    {
-        uint32_t u = __builtin_bit_cast(uint32_t, v);
-        auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
-    }
-    {
-        uint32_t u = __builtin_bit_cast(uint32_t, v);
-        auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
-    }
-    return v;
+    v += dpp_mov<0xB1>(v);          // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);          // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);         // row_half_mirror
+    v += dpp_mov<0x140>(v);         // row_mirror
+    v += dpp_upd<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+    v += dpp_upd<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // ---- workgroup numbering ----------------------------------------------------

@@ -59,13 +59,25 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
 
 
 def act_flip_stats(gpu_bits: np.ndarray, ora_bits: np.ndarray):
-    """(fraction of differing elements, max difference in BF16 ulps of the oracle value)."""
+    """Compare the BF16 intermediate [B,K,I] with the oracle's.
+
+    Returns (fraction of differing elements, max difference in BF16 ulps of the
+    oracle value, whether every difference is within one ulp or within 2^-14
+    of the largest |act| of the same (token, slot) row).  FP32 accumulation of the 2H-term gate/up dot products
+    perturbs act by ~1e-6 of its row scale; after BF16 rounding that shows as
+    rare one-ulp flips, and as a few ulps only on values far below the row
+    scale (cancellation in g or u)."""
     diff = gpu_bits != ora_bits
     if not diff.any():
-        return 0.0, 0.0
-    g = bf16_bits_to_f64(gpu_bits[diff]); o = bf16_bits_to_f64(ora_bits[diff])
-    ulps = np.abs(g - o) / bf16_ulp(o)
-    return float(diff.mean()), float(ulps.max())
+        return 0.0, 0.0, True
+    o_all = bf16_bits_to_f64(ora_bits)
+    rowmax = np.abs(o_all).max(axis=-1, keepdims=True)
+    rowmax = np.broadcast_to(rowmax, o_all.shape)[diff]
+    g = bf16_bits_to_f64(gpu_bits[diff]); o = o_all[diff]
+    d = np.abs(g - o)
+    ulps = d / bf16_ulp(o)
+    within = (ulps <= 1.0) | (d <= 2.0 ** -14 * rowmax)
+    return float(diff.mean()), float(ulps.max()), bool(within.all())
 
 
 def unit_shift(y64: np.ndarray) -> int:
@@ -79,20 +91,24 @@ def shifted(sd: torch.Tensor, k: int) -> torch.Tensor:
     return (sd.to(torch.int32) + k).to(torch.uint8)
 
 
-def parity_report(out_bits: np.ndarray, y64: np.ndarray) -> dict:
+def parity_report(out_bits: np.ndarray, y64: np.ndarray, slack: float = 2e-5) -> dict:
     y = bf16_bits_to_f64(out_bits)
     err = np.abs(y - y64)
-    tol = 0.5 * bf16_ulp(y64) + 2e-5 * float(np.abs(y64).max())
+    tol = 0.5 * bf16_ulp(y64) + slack * float(np.abs(y64).max())
     return dict(cos=cosine(y, y64), max_err=float(err.max()), max_ref=float(np.abs(y64).max()),
                 worst_ratio=float((err / tol).max()), n=int(y.size),
                 finite=bool(np.isfinite(y).all()))
 
 
-def assert_output_parity(out_bits: np.ndarray, y64: np.ndarray, what: str, unit_scale: bool = True):
+def assert_output_parity(out_bits: np.ndarray, y64: np.ndarray, what: str, unit_scale: bool = True,
+                         slack: float = 2e-5):
     """Output gates: cosine >= 0.99999 and, on outputs of unit magnitude, max
     |err| <= 4e-3; and per element, the BF16 output is within half a BF16 ulp
-    of the FP64 oracle plus 2e-5 of the output range (FP32 summation)."""
-    r = parity_report(out_bits, y64)
+    of the FP64 reference plus `slack` of the output range.  slack = 2e-5
+    covers FP32 summation when both sides use the same intermediate; 2e-4
+    also covers the rare one-ulp intermediate flips propagated through the
+    down projection (one flip moves y by at most w * |Wd| * ulp(act))."""
+    r = parity_report(out_bits, y64, slack)
     log(f"[parity] {what}: {r}")
     assert r["finite"], what
     assert r["cos"] >= 0.99999, (what, r)
