@@ -52,16 +52,21 @@ def kernel_source_digest() -> str:
 
 
 def load_traffic(name: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_b1_b32.txt")
     try:
-        d = json.load(open(path))
-    except (OSError, ValueError):
+        lines = open(path).read().splitlines()
+    except OSError:
         return None
-    if d.get("kernel_source_digest") != kernel_source_digest():
-        return None
-    return d.get("hbm_bytes_per_launch")
+    for line in lines:
+        f = line.split()
+        if len(f) >= 2 and f[0] == "traffic" and f[1] == name:
+            kv = dict(x.split("=", 1) for x in f[2:])
+            if kv.get("kernel_source_digest") == kernel_source_digest():
+                return float(kv["hbm_bytes_per_launch"])
+    return None
 
 
 class Workload:
@@ -88,12 +93,12 @@ class Workload:
         self.unique = np.array([np.unique(self.host_ids[s]).size for s in range(steps)])
         self.wd = wd
 
-    def step(self, s, which="both"):
+    def step(self, s, which="both", cfg=None):
         wgu, sgu, wdn, sdn = self.copies[s % len(self.copies)]
         if which in ("both", "gate_up"):
-            self.wd.gate_up(self.x[s], self.ids[s], wgu, sgu, act=self.act[s])
+            self.wd.gate_up(self.x[s], self.ids[s], wgu, sgu, act=self.act[s], cfg=cfg)
         if which in ("both", "down"):
-            self.wd.down(self.act[s], self.ids[s], self.w[s], wdn, sdn, out=self.out[s])
+            self.wd.down(self.act[s], self.ids[s], self.w[s], wdn, sdn, out=self.out[s], cfg=cfg)
 
 
 def measure(torch, wd, work: Workload, steps: int, warmup: int):
@@ -120,20 +125,20 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
 
-    # --- timed region 2: per-kernel durations from HIP events around each launch,
-    # on the launch stream; a sleeping wave first lets the host queue the work ahead
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # --- timed region 2: per-kernel durations from HIP events that the kernels'
+    # own dispatches record (hipExtLaunchKernelGGL) on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record()                          # materialise the hipEvent_t
     torch.cuda.synchronize()
-    wd.gpu_sleep(20000)                         # ~70 ms at 2.4 GHz
+    wd.gpu_sleep(20000)                         # ~70 ms: lets the host queue the steps ahead
     for s in range(steps):
-        evs[s][0].record()
-        work.step(s, "gate_up")
-        evs[s][1].record()
-        work.step(s, "down")
-        evs[s][2].record()
+        work.step(s, "gate_up", wd.Launch(start_event=evs[s][0].cuda_event, stop_event=evs[s][1].cuda_event))
+        work.step(s, "down", wd.Launch(start_event=evs[s][2].cuda_event, stop_event=evs[s][3].cuda_event))
     torch.cuda.synchronize()
     gu_ms = np.array([evs[s][0].elapsed_time(evs[s][1]) for s in range(steps)])
-    dn_ms = np.array([evs[s][1].elapsed_time(evs[s][2]) for s in range(steps)])
+    dn_ms = np.array([evs[s][2].elapsed_time(evs[s][3]) for s in range(steps)])
 
     u = work.unique[:steps].astype(np.float64)
     per_expert_gu = 2 * spec.I * spec.H + 2 * spec.I * (spec.H // 32)
@@ -155,21 +160,37 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int):
     return res
 
 
-def hbm_read_peak(torch, wd, nbytes=4 << 30, reps=10):
+def hbm_read_peak(torch, wd, nbytes=4 << 30, reps=5):
+    """Best contiguous-read bandwidth over launch shapes (GB/s), and the copy
+    bandwidth of 1 GiB (read + write bytes / time)."""
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     sink = torch.zeros(wd.stream_blocks(), dtype=torch.int32, device="cuda")
-    best = 0.0
-    for blocks in (wd.stream_blocks(), 2048, 4096):
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            wd.stream_read(buf, sink, blocks=blocks)
-            e1.record()
-            torch.cuda.synchronize()
-            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del buf
-    return best
+    best, best_cfg = 0.0, None
+    for unroll in (1, 4, 8):
+        for blocks in (1024, 2048, 4096, wd.stream_blocks()):
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                wd.stream_read(buf, sink, blocks=blocks, unroll=unroll)
+                e1.record()
+                torch.cuda.synchronize()
+                bw = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                if bw > best:
+                    best, best_cfg = bw, (unroll, blocks)
+    # 1 GiB copy: a kernel of known traffic (1 GiB read + 1 GiB written)
+    half = 1 << 30
+    src, dst = buf[:half], buf[half:2 * half]
+    copy_best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        wd.stream_copy(dst, src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_best = max(copy_best, 2 * half / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf, src, dst
+    return best, best_cfg, copy_best
 
 
 def sampled_parity(oracle, L, work: Workload, steps_to_check):
@@ -228,8 +249,8 @@ def main():
     L = gen.make_layer(spec, threads=16)
     eprint(f"[bench] layer generated in {time.time() - t0:.1f} s")
 
-    peak = hbm_read_peak(torch, wd)
-    eprint(f"[bench] contiguous-read peak {peak:.0f} GB/s")
+    peak, peak_cfg, copy_bw = hbm_read_peak(torch, wd)
+    eprint(f"[bench] contiguous-read peak {peak:.0f} GB/s (unroll, blocks = {peak_cfg}); copy {copy_bw:.0f} GB/s")
 
     steps, warmup = args.steps, args.warmup
     copies1 = args.copies or 16
@@ -268,6 +289,7 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS, "kernel": "gate_up",
                      "traffic": load_traffic("gate_up_qwen3_b1")},
         "hbm_read_peak_GBps": peak,
+        "hbm_copy_GBps": copy_bw,
         "layer_GBps": r1["layer_GBps_graph"],
         "frac_of_8TBps": r1["layer_GBps_graph"] / PEAK_HBM_GBPS,
         "frac_of_measured_read_peak": r1["layer_GBps_graph"] / peak,

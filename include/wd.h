@@ -72,8 +72,8 @@ enum wd_status {
     WD_ERR_UNSUPPORTED = -7  /* sizes beyond this build's limits, or a bad launch configuration */
 };
 
-/* Launch configuration (tuning).  Any field left 0 takes the library default
- * for the call's sizes.
+/* Launch configuration (tuning and timing).  Any integer field left 0 takes
+ * the library default for the call's sizes.
  *   rows_per_wave    1, 2 or 4: output rows one 64-lane wave computes (each
  *                    row is still one wave-wide reduction)
  *   waves_per_block  1..4: waves per workgroup
@@ -84,12 +84,18 @@ enum wd_status {
  *   xcd_remap        1 = renumber workgroups so that each of the 8 XCDs gets
  *                    one contiguous range of the work order; 2 = keep the
  *                    hardware's round-robin numbering
+ *   start_event,     optional hipEvent_t handles (created by the caller); when
+ *   stop_event       set, the kernel's own dispatch records its start and end
+ *                    time into them (hipExtLaunchKernelGGL), so the elapsed
+ *                    time is the kernel's execution alone
  */
 typedef struct wd_launch {
     int rows_per_wave;
     int waves_per_block;
     int order;
     int xcd_remap;
+    void *start_event;
+    void *stop_event;
 } wd_launch;
 
 /* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section
@@ -108,8 +114,8 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
 /* Down kernel (moe_down_3d_batched; same sections; the Chinese summary's
  * "Down Kernel"): one wave per (token b, output dim h).  The wave walks the K
  * routed experts' rows Wd[e_k, h, :], folds topk_w[b,k] into one FP32
- * accumulator, reduces across its 64 lanes with DPP and lane-swap operations
- * (no LDS) and writes out[b,h] = BF16(acc). */
+ * accumulator, reduces across its 64 lanes with DPP row operations and one
+ * lane read (no LDS) and writes out[b,h] = BF16(acc). */
 int wd_down(const uint16_t *act, const int32_t *topk_ids, const float *topk_w,
             const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
             int B, int K, int E, int H, int I, void *stream);
@@ -133,16 +139,19 @@ const char *wd_status_string(int status);
 
 /* ---- measurement helpers (not on the layer's path) --------------------- */
 
-/* Exhaustive MXFP8 conversion probe: out[s * 256 + c] = the FP32 value the
- * layer kernels compute for element code c under block exponent byte s, for
- * all 256 x 256 pairs (65,536 floats, device memory, 16-byte aligned). */
+/* Exhaustive MXFP8 conversion probe: for every E8M0 byte s and code c, the
+ * codes c, c+1, c+2, c+3 (mod 256) are packed into one word (byte j holds
+ * c+j) and converted exactly as the layer kernels do;
+ * out[(s * 256 + c) * 4 + j] receives the FP32 value of byte j
+ * (262,144 floats, device memory, 16-byte aligned). */
 int wd_dequant_probe(float *out, void *stream);
 
 /* Contiguous-read bandwidth kernel: reads `bytes` (a multiple of 16) from
- * `buf` with 16-byte loads in a grid-stride loop and writes one word per
- * workgroup to sink[0 .. blocks) so the reads cannot be elided.  blocks <= 0
- * picks a default; sink must hold that many uint32 (wd_stream_blocks()). */
-int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, void *stream);
+ * `buf` with 16-byte loads in a grid-stride loop, `unroll` (1, 2, 4 or 8)
+ * independent loads in flight per lane, and keeps every load live through a
+ * conditional write to sink[0 .. blocks).  blocks <= 0 picks a default; sink
+ * must hold wd_stream_blocks() uint32. */
+int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int unroll, void *stream);
 int wd_stream_blocks(void);
 
 /* Contiguous copy with 16-byte loads and stores (bytes a multiple of 16). */

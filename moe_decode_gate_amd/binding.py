@@ -37,9 +37,12 @@ class WDError(RuntimeError):
 
 
 class Launch(C.Structure):
-    """Launch configuration (wd_launch); 0 fields take the library default."""
+    """Launch configuration (wd_launch); 0 fields take the library default.
+    start_event / stop_event: raw hipEvent_t handles (e.g. torch.cuda.Event's
+    cuda_event after one record()) that receive the kernel's own start/end."""
     _fields_ = [("rows_per_wave", C.c_int), ("waves_per_block", C.c_int),
-                ("order", C.c_int), ("xcd_remap", C.c_int)]
+                ("order", C.c_int), ("xcd_remap", C.c_int),
+                ("start_event", C.c_void_p), ("stop_event", C.c_void_p)]
 
 
 _P, _I, _S = C.c_void_p, C.c_int, C.c_size_t
@@ -52,7 +55,7 @@ _sig = {
     "wd_workspace_bytes": (_S, [_I, _I, _I]),
     "wd_status_string": (C.c_char_p, [_I]),
     "wd_dequant_probe": (_I, [_P, _P]),
-    "wd_stream_read": (_I, [_P, _S, _P, _I, _P]),
+    "wd_stream_read": (_I, [_P, _S, _P, _I, _I, _P]),
     "wd_stream_blocks": (_I, []),
     "wd_stream_copy": (_I, [_P, _P, _S, _I, _P]),
     "wd_gpu_sleep": (_I, [_I, _P]),
@@ -190,9 +193,9 @@ def stream_blocks() -> int:
     return _lib.wd_stream_blocks()
 
 
-def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0, stream=None):
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0, unroll: int = 4, stream=None):
     nbytes = buf.numel() * buf.element_size()
-    _check(_lib.wd_stream_read(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)), "wd_stream_read")
+    _check(_lib.wd_stream_read(_ptr(buf), nbytes, _ptr(sink), blocks, unroll, _stream(stream)), "wd_stream_read")
 
 
 def stream_copy(dst: torch.Tensor, src: torch.Tensor, blocks: int = 0, stream=None):

@@ -6,6 +6,7 @@
 // without synchronising, allocating or freeing.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <atomic>
 #include <climits>
@@ -49,7 +50,7 @@ int check_dims(int B, int K, int E, int H, int I) {
 // Resolve a launch configuration: fill unset fields with the defaults for
 // this batch size, then validate.
 int resolve(const wd_launch *in, int B, bool down, wd_launch *out) {
-    wd_launch c = in ? *in : wd_launch{0, 0, 0, 0};
+    wd_launch c = in ? *in : wd_launch{0, 0, 0, 0, nullptr, nullptr};
     if (c.rows_per_wave == 0) c.rows_per_wave = down ? (B >= 8 ? 2 : 1) : (B >= 8 ? 2 : 1);
     if (c.waves_per_block == 0) c.waves_per_block = 4;
     if (c.order == 0) c.order = 1;
@@ -118,9 +119,13 @@ KernelFn down_fn(int cpl, int R, bool tail) {
     return nullptr;
 }
 
-int launch(KernelFn fn, LayerArgs a, int waves_per_block, hipStream_t s) {
-    const int blocks = (a.nwaves + waves_per_block - 1) / waves_per_block;
-    hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * waves_per_block), 0, s, a);
+int launch(KernelFn fn, LayerArgs a, const wd_launch &c, hipStream_t s) {
+    const int blocks = (a.nwaves + c.waves_per_block - 1) / c.waves_per_block;
+    if (c.start_event || c.stop_event)
+        hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, s,
+                              (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a);
+    else
+        hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, s, a);
     return launched();
 }
 
@@ -148,7 +153,7 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     const bool tail = (H / 16) % (64 * cpl) != 0;
     KernelFn fn = gate_up_fn(cpl, c.rows_per_wave, tail);
     if (!fn) return WD_ERR_UNSUPPORTED;
-    return launch(fn, a, c.waves_per_block, (hipStream_t)stream);
+    return launch(fn, a, c, (hipStream_t)stream);
 }
 
 int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const uint8_t *w_d,
@@ -185,7 +190,7 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
     const bool tail = nc % (64 * cpl) != 0;
     KernelFn fn = down_fn(cpl, c.rows_per_wave, tail);
     if (!fn) return WD_ERR_UNSUPPORTED;
-    return launch(fn, a, c.waves_per_block, (hipStream_t)stream);
+    return launch(fn, a, c, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -265,14 +270,22 @@ int wd_dequant_probe(float *out, void *stream) {
 
 int wd_stream_blocks(void) { return 256 * 32; }
 
-int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, void *stream) {
+int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int unroll, void *stream) {
     if (!buf || !sink) return WD_ERR_NULL;
     if (bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return WD_ERR_ALIGN;
     if (blocks <= 0) blocks = wd_stream_blocks();
     if (blocks > wd_stream_blocks()) return WD_ERR_UNSUPPORTED;
+    void (*fn)(const wd::u32x4 *, size_t, uint32_t *, uint32_t) = nullptr;
+    switch (unroll) {
+        case 1: fn = wd::stream_read_kernel<1>; break;
+        case 2: fn = wd::stream_read_kernel<2>; break;
+        case 4: fn = wd::stream_read_kernel<4>; break;
+        case 8: fn = wd::stream_read_kernel<8>; break;
+        default: return WD_ERR_UNSUPPORTED;
+    }
     int rc = check_device();
     if (rc) return rc;
-    hipLaunchKernelGGL(wd::stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const wd::u32x4 *>(buf), bytes / 16, sink, 0x9E3779B9u);
     return launched();
 }

@@ -209,13 +209,23 @@ __global__ __launch_bounds__(256) void dequant_probe_kernel(float *out) {
     o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
 }
 
-// Reads n16 16-byte words.  Each lane folds its words into an XOR; the sink is
-// written only if that fold equals `never` (a value the caller chooses so it
-// does not occur), which keeps every load live without a reduction.
+// Reads n16 16-byte words in a grid-stride loop with U independent loads in
+// flight per lane.  Each lane folds its words into an XOR; the sink is written
+// only if that fold equals `never` (a value the caller chooses so it does not
+// occur), which keeps every load live without a reduction.
+template <int U>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *buf, size_t n16, uint32_t *sink, uint32_t never) {
     uint32_t acc = 0;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = buf[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < n16; i += stride) {
         const u32x4 v = buf[i];
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }

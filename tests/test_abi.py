@@ -82,7 +82,8 @@ def test_empty_batch_launches_nothing():
 
 
 def test_bad_launch_config_rejected():
-    for cfg in (wd.Launch(3, 0, 0, 0), wd.Launch(0, 5, 0, 0), wd.Launch(0, 0, 3, 0), wd.Launch(0, 0, 0, 7)):
+    for cfg in (wd.Launch(3, 0, 0, 0), wd.Launch(0, 5, 0, 0), wd.Launch(0, 0, 3, 0), wd.Launch(0, 0, 0, 7),
+                wd.Launch(0, 0, 0, -1)):
         assert lib.wd_gate_up_ex(A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(cfg), None) == -7
         assert lib.wd_down_ex(A, A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(cfg), None) == -7
 
@@ -90,8 +91,9 @@ def test_bad_launch_config_rejected():
 def test_helpers_reject_bad_arguments():
     assert lib.wd_dequant_probe(None, None) == -1
     assert lib.wd_dequant_probe(A + 4, None) == -3
-    assert lib.wd_stream_read(A, 15, A, 0, None) == -3
-    assert lib.wd_stream_read(A, 16, A, lib.wd_stream_blocks() + 1, None) == -7
+    assert lib.wd_stream_read(A, 15, A, 0, 4, None) == -3
+    assert lib.wd_stream_read(A, 16, A, lib.wd_stream_blocks() + 1, 4, None) == -7
+    assert lib.wd_stream_read(A, 16, A, 0, 3, None) == -7
     assert lib.wd_stream_copy(None, A, 16, 0, None) == -1
     assert lib.wd_gpu_sleep(-1, None) == -7
 
