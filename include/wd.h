@@ -74,8 +74,9 @@ enum wd_status {
 
 /* Launch configuration (tuning and timing).  Any integer field left 0 takes
  * the library default for the call's sizes.
- *   rows_per_wave    1, 2 or 4: output rows one 64-lane wave computes (each
- *                    row is still one wave-wide reduction)
+ *   rows_per_wave    1, 2, 4 (or 8 for down): rows each lane group computes in
+ *                    turn (a wave computes rows_per_wave * 64 / lanes_per_row
+ *                    rows)
  *   waves_per_block  1..4: waves per workgroup
  *   order            1 = row-block major (the waves of all tokens and slots
  *                    for one block of rows are adjacent, so tokens that share
@@ -84,6 +85,21 @@ enum wd_status {
  *   xcd_remap        1 = renumber workgroups so that each of the 8 XCDs gets
  *                    one contiguous range of the work order; 2 = keep the
  *                    hardware's round-robin numbering
+ *   math             1 = MXFP8 pairs converted to FP32, FMA accumulation;
+ *                    2 = MXFP8 pairs converted to BF16 (exact for normal
+ *                    values), two products per v_dot2_f32_bf16 into the FP32
+ *                    accumulator.  Both are FP32 accumulation of exact products.
+ *   lanes_per_row    gate/up only: 16, 32 or 64 lanes share one row's dot
+ *                    products, so a wave works on 64 / lanes_per_row rows at
+ *                    once (down: 64)
+ *   form             gate/up only: 1 = one wave per (token, slot, row block);
+ *                    2 = one wave per (expert, row block) serving every slot
+ *                    routed to that expert, each weight row read and
+ *                    converted once (requires lanes_per_row 64, math 2,
+ *                    weight_loads 1); both forms give bit-identical results
+ *                    for lanes_per_row 64 and math 2 (down: 1)
+ *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
+ *                    streamed once and not kept in the caches)
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end
  *                    time into them (hipExtLaunchKernelGGL), so the elapsed
@@ -96,6 +112,10 @@ typedef struct wd_launch {
     int xcd_remap;
     void *start_event;
     void *stop_event;
+    int math;
+    int lanes_per_row;
+    int form;
+    int weight_loads;
 } wd_launch;
 
 /* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section
@@ -141,9 +161,10 @@ const char *wd_status_string(int status);
 
 /* Exhaustive MXFP8 conversion probe: for every E8M0 byte s and code c, the
  * codes c, c+1, c+2, c+3 (mod 256) are packed into one word (byte j holds
- * c+j) and converted exactly as the layer kernels do;
- * out[(s * 256 + c) * 4 + j] receives the FP32 value of byte j
- * (262,144 floats, device memory, 16-byte aligned). */
+ * c+j) and converted exactly as the layer kernels do.
+ * out[(s * 256 + c) * 4 + j] receives the FP32 conversion (math mode 1) of
+ * byte j and out[262144 + (s * 256 + c) * 4 + j] the BF16 conversion (math
+ * mode 2) widened to FP32: 524,288 floats, device memory, 16-byte aligned. */
 int wd_dequant_probe(float *out, void *stream);
 
 /* Contiguous-read bandwidth kernel: reads `bytes` (a multiple of 16) from

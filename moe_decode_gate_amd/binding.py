@@ -42,7 +42,8 @@ class Launch(C.Structure):
     cuda_event after one record()) that receive the kernel's own start/end."""
     _fields_ = [("rows_per_wave", C.c_int), ("waves_per_block", C.c_int),
                 ("order", C.c_int), ("xcd_remap", C.c_int),
-                ("start_event", C.c_void_p), ("stop_event", C.c_void_p)]
+                ("start_event", C.c_void_p), ("stop_event", C.c_void_p), ("math", C.c_int),
+                ("lanes_per_row", C.c_int), ("form", C.c_int), ("weight_loads", C.c_int)]
 
 
 _P, _I, _S = C.c_void_p, C.c_int, C.c_size_t
@@ -183,8 +184,8 @@ def moe_decode(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, out=None, workspace=No
 
 
 def dequant_probe(device="cuda", stream=None) -> torch.Tensor:
-    """[256 scales, 256 codes, 4 byte lanes] FP32 conversions (see wd.h)."""
-    out = torch.empty((256, 256, 4), dtype=torch.float32, device=device)
+    """[2 math modes (FP32, BF16), 256 scales, 256 codes, 4 byte lanes] conversions (see wd.h)."""
+    out = torch.empty((2, 256, 256, 4), dtype=torch.float32, device=device)
     _check(_lib.wd_dequant_probe(_ptr(out), _stream(stream)), "wd_dequant_probe")
     return out
 

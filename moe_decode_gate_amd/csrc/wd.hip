@@ -9,6 +9,7 @@
 #include <hip/hip_ext.h>
 
 #include <atomic>
+#include <type_traits>
 #include <climits>
 #include <cstdint>
 #include <cstring>
@@ -48,17 +49,43 @@ int check_dims(int B, int K, int E, int H, int I) {
 }
 
 // Resolve a launch configuration: fill unset fields with the defaults for
-// this batch size, then validate.
+// this batch size, then validate.  Defaults come from sweeps of every
+// configuration on MI355X at the 128-expert / top-8 / H 2048 / I 768 layer:
+//   B < 8  (latency-bound, no row is read twice): one row per wave, 64 lanes
+//          per row, BF16-pair dot products, non-temporal weight loads;
+//   B >= 8 (tokens share experts): row-block-major order with XCD-contiguous
+//          numbering, so the tokens that share an expert row read it from the
+//          same L2 while it is resident; gate/up with 32 lanes per row and 4
+//          rows per lane group (8 rows per wave), down with 8 rows per wave.
 int resolve(const wd_launch *in, int B, bool down, wd_launch *out) {
-    wd_launch c = in ? *in : wd_launch{0, 0, 0, 0, nullptr, nullptr};
-    if (c.rows_per_wave == 0) c.rows_per_wave = down ? (B >= 8 ? 2 : 1) : (B >= 8 ? 2 : 1);
-    if (c.waves_per_block == 0) c.waves_per_block = 4;
+    wd_launch c = in ? *in : wd_launch{};
+    const bool batch = B >= 8;
+    if (c.form == 0) c.form = 1;
+    if (c.rows_per_wave == 0) c.rows_per_wave = !batch ? 1 : down ? 8 : c.form == 2 ? 2 : 4;
+    if (c.waves_per_block == 0) c.waves_per_block = down ? (batch ? 1 : 2) : (batch ? 4 : 1);
     if (c.order == 0) c.order = 1;
-    if (c.xcd_remap == 0) c.xcd_remap = 1;
-    if (c.rows_per_wave != 1 && c.rows_per_wave != 2 && c.rows_per_wave != 4) return WD_ERR_UNSUPPORTED;
+    if (c.xcd_remap == 0) c.xcd_remap = (!down && !batch) ? 2 : 1;
+    if (c.math == 0) c.math = (down && batch) ? wd::kMathF32 : wd::kMathDot2;
+    if (c.lanes_per_row == 0)
+        c.lanes_per_row = (!down && batch && c.form == 1 && c.math == wd::kMathDot2 && c.weight_loads != 2) ? 32 : 64;
+    if (c.weight_loads == 0) {
+        // non-temporal where no other wave re-reads the rows and the variant is compiled
+        const bool nt_ok = c.math == wd::kMathDot2 && c.form == 1 &&
+                           (down ? c.rows_per_wave == 1 : c.lanes_per_row == 64);
+        c.weight_loads = (!batch && nt_ok) ? 2 : 1;
+    }
+    if (c.rows_per_wave != 1 && c.rows_per_wave != 2 && c.rows_per_wave != 4 && c.rows_per_wave != 8)
+        return WD_ERR_UNSUPPORTED;
     if (c.waves_per_block < 1 || c.waves_per_block > 4) return WD_ERR_UNSUPPORTED;
     if (c.order != 1 && c.order != 2) return WD_ERR_UNSUPPORTED;
     if (c.xcd_remap != 1 && c.xcd_remap != 2) return WD_ERR_UNSUPPORTED;
+    if (c.math != wd::kMathF32 && c.math != wd::kMathDot2) return WD_ERR_UNSUPPORTED;
+    if (c.lanes_per_row != 16 && c.lanes_per_row != 32 && c.lanes_per_row != 64) return WD_ERR_UNSUPPORTED;
+    if (c.form != 1 && c.form != 2) return WD_ERR_UNSUPPORTED;
+    if (c.weight_loads != 1 && c.weight_loads != 2) return WD_ERR_UNSUPPORTED;
+    if (down && (c.lanes_per_row != 64 || c.form != 1)) return WD_ERR_UNSUPPORTED;
+    if (c.form == 2 && (c.lanes_per_row != 64 || c.math != wd::kMathDot2 || c.weight_loads != 1))
+        return WD_ERR_UNSUPPORTED;
     *out = c;
     return WD_OK;
 }
@@ -67,24 +94,85 @@ int launched() {
     return hipGetLastError() == hipSuccess ? WD_OK : WD_ERR_LAUNCH;
 }
 
-// ---- dispatch on compile-time chunk count and rows per wave -------------
+// ---- runtime -> compile-time dispatch ------------------------------------
 
 typedef void (*KernelFn)(LayerArgs);
 
-template <template <int, int, bool> class Sel, int CPL>
-KernelFn pick_r(int R, bool tail) {
-    switch (R) {
-        case 1: return tail ? Sel<CPL, 1, true>::fn() : Sel<CPL, 1, false>::fn();
-        case 2: return tail ? Sel<CPL, 2, true>::fn() : Sel<CPL, 2, false>::fn();
-        case 4: return tail ? Sel<CPL, 4, true>::fn() : Sel<CPL, 4, false>::fn();
-    }
-    return nullptr;
+template <int... V>
+struct Ints {};
+
+// Calls f(std::integral_constant<int, v>) for the v in the list equal to the
+// runtime value, or returns nullptr.
+template <int V0, int... Vs, class F>
+KernelFn dispatch(int v, Ints<V0, Vs...>, F f) {
+    if (v == V0) return f(std::integral_constant<int, V0>{});
+    if constexpr (sizeof...(Vs) > 0) return dispatch(v, Ints<Vs...>{}, f);
+    else return nullptr;
 }
 
-template <int CPL, int R, bool TAIL>
-struct GateUpSel { static KernelFn fn() { return wd::gate_up_kernel<CPL, R, TAIL>; } };
-template <int CPL, int R, bool TAIL>
-struct DownSel { static KernelFn fn() { return wd::down_kernel<CPL, R, TAIL>; } };
+// Which variants are compiled.  Token-form gate/up: every chunk count, row
+// count and tail; FP32 math only with 64 lanes per row and cached loads,
+// non-temporal loads only with 64 lanes per row.  Expert form: register use
+// limits R * CPL to 8.  Down: non-temporal loads only at one row per wave.
+template <int CPL, int R, int LPR, int M, int NT>
+constexpr bool gate_up_compiled() {
+    if (R == 8) return false;
+    if (M == wd::kMathF32) return LPR == 64 && NT == 0;
+    return NT == 0 || LPR == 64;
+}
+template <int CPL, int R>
+constexpr bool gate_up_expert_compiled() { return R <= 4 && R * CPL <= 8; }
+template <int CPL, int R, int M, int NT>
+constexpr bool down_compiled() { return NT == 0 || (R == 1 && M == wd::kMathDot2); }
+
+KernelFn gate_up_fn(int cpl, int R, int lpr, int tail, int math, int nt) {
+    return dispatch(cpl, Ints<1, 2, 4, 8>{}, [&](auto C) {
+        return dispatch(R, Ints<1, 2, 4>{}, [&](auto Rv) {
+            return dispatch(lpr, Ints<16, 32, 64>{}, [&](auto L) {
+                return dispatch(tail, Ints<0, 1>{}, [&](auto T) {
+                    return dispatch(math, Ints<wd::kMathF32, wd::kMathDot2>{}, [&](auto M) {
+                        return dispatch(nt, Ints<0, 1>{}, [&](auto N) -> KernelFn {
+                            if constexpr (gate_up_compiled<C, Rv, L, M, N>())
+                                return wd::gate_up_kernel<C, Rv, L, T != 0, M, N != 0>;
+                            else
+                                return nullptr;
+                        });
+                    });
+                });
+            });
+        });
+    });
+}
+
+KernelFn gate_up_expert_fn(int cpl, int R, int tail) {
+    return dispatch(cpl, Ints<1, 2, 4, 8>{}, [&](auto C) {
+        return dispatch(R, Ints<1, 2, 4>{}, [&](auto Rv) {
+            return dispatch(tail, Ints<0, 1>{}, [&](auto T) -> KernelFn {
+                if constexpr (gate_up_expert_compiled<C, Rv>())
+                    return wd::gate_up_expert_kernel<C, Rv, T != 0>;
+                else
+                    return nullptr;
+            });
+        });
+    });
+}
+
+KernelFn down_fn(int cpl, int R, int tail, int math, int nt) {
+    return dispatch(cpl, Ints<1, 2, 3, 4, 6, 8, 12, 16>{}, [&](auto C) {
+        return dispatch(R, Ints<1, 2, 4, 8>{}, [&](auto Rv) {
+            return dispatch(tail, Ints<0, 1>{}, [&](auto T) {
+                return dispatch(math, Ints<wd::kMathF32, wd::kMathDot2>{}, [&](auto M) {
+                    return dispatch(nt, Ints<0, 1>{}, [&](auto N) -> KernelFn {
+                        if constexpr (down_compiled<C, Rv, M, N>())
+                            return wd::down_kernel<C, Rv, T != 0, M, N != 0>;
+                        else
+                            return nullptr;
+                    });
+                });
+            });
+        });
+    });
+}
 
 // Smallest compiled chunks-per-lane >= need.
 int round_cpl_gate_up(int need) {
@@ -94,29 +182,6 @@ int round_cpl_gate_up(int need) {
 int round_cpl_down(int need) {
     for (int c : {1, 2, 3, 4, 6, 8, 12, 16}) if (c >= need) return c;
     return -1;
-}
-
-KernelFn gate_up_fn(int cpl, int R, bool tail) {
-    switch (cpl) {
-        case 1: return pick_r<GateUpSel, 1>(R, tail);
-        case 2: return pick_r<GateUpSel, 2>(R, tail);
-        case 4: return pick_r<GateUpSel, 4>(R, tail);
-        case 8: return pick_r<GateUpSel, 8>(R, tail);
-    }
-    return nullptr;
-}
-KernelFn down_fn(int cpl, int R, bool tail) {
-    switch (cpl) {
-        case 1: return pick_r<DownSel, 1>(R, tail);
-        case 2: return pick_r<DownSel, 2>(R, tail);
-        case 3: return pick_r<DownSel, 3>(R, tail);
-        case 4: return pick_r<DownSel, 4>(R, tail);
-        case 6: return pick_r<DownSel, 6>(R, tail);
-        case 8: return pick_r<DownSel, 8>(R, tail);
-        case 12: return pick_r<DownSel, 12>(R, tail);
-        case 16: return pick_r<DownSel, 16>(R, tail);
-    }
-    return nullptr;
 }
 
 int launch(KernelFn fn, LayerArgs a, const wd_launch &c, hipStream_t s) {
@@ -140,19 +205,23 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
         return WD_ERR_ALIGN;
     wd_launch c;
     if ((rc = resolve(cfg, B, false, &c))) return rc;
-    const int cpl = round_cpl_gate_up((H / 16 + 63) / 64);
+    const int lpr = c.lanes_per_row;
+    const int cpl = round_cpl_gate_up((H / 16 + lpr - 1) / lpr);
     if (cpl < 0) return WD_ERR_UNSUPPORTED;
+    const int rows_per_wave = (64 / lpr) * c.rows_per_wave;
+    if (I % rows_per_wave) return WD_ERR_UNSUPPORTED;
+    const bool tail = (H / 16) % (lpr * cpl) != 0;
+    KernelFn fn = c.form == 2 ? gate_up_expert_fn(cpl, c.rows_per_wave, tail)
+                              : gate_up_fn(cpl, c.rows_per_wave, lpr, tail, c.math, c.weight_loads == 2);
+    if (!fn) return WD_ERR_UNSUPPORTED;
     if (B == 0) return WD_OK;
     if (!checked_device && (rc = check_device())) return rc;
     LayerArgs a{};
     a.x = x; a.ids = ids; a.w = w_gu; a.s = s_gu; a.out = act;
     a.B = B; a.K = K; a.E = E; a.H = H; a.I = I;
-    a.nrowblk = I / c.rows_per_wave;
-    a.nwaves = B * K * a.nrowblk;
+    a.nrowblk = I / rows_per_wave;
+    a.nwaves = (c.form == 2 ? E : B * K) * a.nrowblk;
     a.order = c.order; a.remap = c.xcd_remap;
-    const bool tail = (H / 16) % (64 * cpl) != 0;
-    KernelFn fn = gate_up_fn(cpl, c.rows_per_wave, tail);
-    if (!fn) return WD_ERR_UNSUPPORTED;
     return launch(fn, a, c, (hipStream_t)stream);
 }
 
@@ -171,6 +240,7 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
     const int nc = K * (I / 16);
     const int cpl = round_cpl_down((nc + 63) / 64);
     if (cpl < 0) return WD_ERR_UNSUPPORTED;
+    if (H % c.rows_per_wave) return WD_ERR_UNSUPPORTED;
     // Chunk -> slot division by multiply and shift: with magic = floor(2^22 / nci) + 1,
     // (cc * magic) >> 22 == cc / nci for every cc < 1024 whenever nci <= 1024 (the
     // rounding excess cc * (magic - 2^22 / nci) / 2^22 < 2^-12 cannot reach the next
@@ -178,6 +248,9 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
     // K * I <= 16384, so nc = K * I / 16 <= 1024 and nci <= 1024.
     const uint32_t nci = (uint32_t)(I / 16);
     const uint32_t magic = (uint32_t)((1u << 22) / nci + 1);
+    const bool tail = nc % (64 * cpl) != 0;
+    KernelFn fn = down_fn(cpl, c.rows_per_wave, tail, c.math, c.weight_loads == 2);
+    if (!fn) return WD_ERR_UNSUPPORTED;
     if (B == 0) return WD_OK;
     if (!checked_device && (rc = check_device())) return rc;
     LayerArgs a{};
@@ -187,9 +260,6 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
     a.nwaves = B * a.nrowblk;
     a.order = c.order; a.remap = c.xcd_remap;
     a.nci_magic = magic;
-    const bool tail = nc % (64 * cpl) != 0;
-    KernelFn fn = down_fn(cpl, c.rows_per_wave, tail);
-    if (!fn) return WD_ERR_UNSUPPORTED;
     return launch(fn, a, c, (hipStream_t)stream);
 }
 

@@ -8,6 +8,7 @@
 namespace wd {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;      // CDNA wavefront width
@@ -18,6 +19,14 @@ constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, each with 
 
 __device__ __forceinline__ u32x4 ld16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// 16-byte weight load; NT marks it non-temporal (streamed once, not kept in
+// the caches), which pays off when no other wave re-reads the row.
+template <bool NT>
+__device__ __forceinline__ u32x4 ldw(const void *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    else return *reinterpret_cast<const u32x4 *>(p);
 }
 
 // ---- MXFP8 ----------------------------------------------------------------
@@ -35,6 +44,15 @@ __device__ __forceinline__ float e8m0_operand(uint32_t s) {
 template <bool HI>
 __device__ __forceinline__ f32x2 mx_pair(uint32_t word, float scale) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, scale, HI);
+}
+
+// Two E4M3 codes times the block scale, to a packed BF16 pair (element of the
+// lower byte in the low half) with v_cvt_scalef32_pk_bf16_fp8.  Exact whenever
+// the product is a normal BF16 number: an E4M3 value has at most 4
+// significant bits and BF16 keeps 8 and the FP32 exponent range.
+template <bool HI>
+__device__ __forceinline__ uint32_t mx_pair_bf16(uint32_t word, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, scale, HI));
 }
 
 // ---- BF16 -----------------------------------------------------------------
@@ -82,6 +100,41 @@ __device__ __forceinline__ float dot16_bf16(u32x4 q, float scale, u32x4 a0, u32x
     return acc;
 }
 
+// Same dot product with v_dot2_f32_bf16: weights converted to BF16 pairs
+// (exact, see mx_pair_bf16), activations used as stored (BF16 pairs), two
+// products (exact in FP32) added into the FP32 accumulator per instruction.
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, a), acc, false);
+}
+
+__device__ __forceinline__ float dot16_dot2(u32x4 q, float scale, u32x4 a0, u32x4 a1, float acc) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t p0 = d < 2 ? a0[2 * d] : a1[2 * d - 4];       // elements 4d, 4d+1
+        const uint32_t p1 = d < 2 ? a0[2 * d + 1] : a1[2 * d - 3];   // elements 4d+2, 4d+3
+        acc = dot2(mx_pair_bf16<false>(q[d], scale), p0, acc);
+        acc = dot2(mx_pair_bf16<true>(q[d], scale), p1, acc);
+    }
+    return acc;
+}
+
+// Four codes of one word converted to two BF16 pairs (elements 0-1, 2-3).
+__device__ __forceinline__ void mx_word_bf16(uint32_t word, float scale, uint32_t &lo, uint32_t &hi) {
+    lo = mx_pair_bf16<false>(word, scale);
+    hi = mx_pair_bf16<true>(word, scale);
+}
+
+// acc + sum of 16 products of pre-converted BF16 weight pairs w[0..7] with the
+// activation pairs (a0, a1); same pairing and order as dot16_dot2.
+__device__ __forceinline__ float dot16_pre(const uint32_t *w, u32x4 a0, u32x4 a1, float acc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = dot2(w[j], j < 4 ? a0[j] : a1[j - 4], acc);
+    return acc;
+}
+
+// Math modes of the layer kernels.
+enum Math { kMathF32 = 1, kMathDot2 = 2 };
+
 // ---- 64-lane reduction ----------------------------------------------------
 
 template <int CTRL>
@@ -111,6 +164,31 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_upd<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
     v += dpp_upd<0x143, 0xC>(v);    // row_bcast:31 into rows 2 and 3
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over each group of LPR consecutive lanes (LPR = 16, 32 or 64), returned
+// to every lane of the group (bit-identical within a group).  The in-row
+// butterfly is the one of wave_sum; for 32-lane groups row_bcast:15 adds row
+// 0 into row 1 and row 2 into row 3 and v_readlane of lanes 31 and 63 hands
+// the two totals back to their groups.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(LPR == 16 || LPR == 32 || LPR == 64, "group of 16, 32 or 64 lanes");
+    if constexpr (LPR == 64) {
+        return wave_sum(v);
+    } else {
+        v += dpp_mov<0xB1>(v);          // quad_perm [1,0,3,2]
+        v += dpp_mov<0x4E>(v);          // quad_perm [2,3,0,1]
+        v += dpp_mov<0x141>(v);         // row_half_mirror
+        v += dpp_mov<0x140>(v);         // row_mirror
+        if constexpr (LPR == 32) {
+            v += dpp_upd<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+            const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+            const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+            v = (threadIdx.x & 32) ? hi : lo;
+        }
+        return v;
+    }
 }
 
 // ---- workgroup numbering ----------------------------------------------------

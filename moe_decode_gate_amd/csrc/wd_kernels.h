@@ -39,17 +39,28 @@ __device__ __forceinline__ int logical_wave(const LayerArgs &a) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up: one wave per (token b, slot k, block of R intermediate rows).
+// Gate/up: one wave per (token b, slot k, block of G * R intermediate rows).
 //
-// Lane l owns 16-element chunks c = l + 64 i (i < CPL) of the H axis: each
-// 16-byte code load of a row is then one fully coalesced 1 KiB wave access.
-// x[b] is loaded once per wave, converted to FP32 once, and reused by the
-// gate and the up row of all R rows.  TAIL handles H/16 not a multiple of
-// 64 * CPL (lanes past the row end contribute exact zeros).
+// The wave is cut into G = 64 / LPR groups of LPR lanes; each group owns one
+// row at a time (R rows in turn), so the wave works on G rows at once and
+// their cross-lane reductions run side by side in the same instructions.
+// Lane t of a group owns the 16-element chunks c = t + LPR * i (i < CPL) of
+// the H axis: each 16-byte code load instruction covers G contiguous
+// LPR * 16-byte row segments.  x[b] is loaded once per wave and reused by the
+// gate and the up row of every row the lane touches.  MATH selects the
+// arithmetic: kMathF32 converts each MXFP8 pair to FP32 and accumulates with
+// FMAs; kMathDot2 converts it to a BF16 pair (also exact) and accumulates two
+// products per v_dot2_f32_bf16 into FP32, using x as stored.  TAIL handles
+// H / 16 not a multiple of LPR * CPL (lanes past the row end add nothing).
+// NT loads the weights non-temporally (for batches where no other wave reads
+// the same rows).  The row handled by group g at step r is
+// j = jb * G * R + r * G + g.
 // ---------------------------------------------------------------------------
-template <int CPL, int R, bool TAIL>
+template <int CPL, int R, int LPR, bool TAIL, int MATH, bool NT>
 __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
+    constexpr int G = 64 / LPR;
     const int lane = threadIdx.x & 63;
+    const int grp = lane / LPR, tl = lane % LPR;
     const int t = logical_wave(a);
     if (t >= a.nwaves) return;                       // wave-uniform exit
 
@@ -65,29 +76,35 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
     const bool bad = (unsigned)e >= (unsigned)a.E;   // never read out of bounds for a bad id
     if (bad) e = 0;
 
-    // x[b] -> FP32 registers, chunk by chunk.
-    float xv[CPL][16];
+    // x[b] in registers, chunk by chunk: FP32 (MATH == kMathF32) or the stored
+    // BF16 pairs (kMathDot2).
+    float xv[MATH == kMathF32 ? CPL : 1][16];
+    u32x4 xp0[CPL], xp1[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
+        const int c = tl + LPR * i;
         const int cc = (!TAIL || c < NC) ? c : 0;
         const uint16_t *xp = a.x + (size_t)b * H + cc * 16;
-        const u32x4 p0 = ld16(xp), p1 = ld16(xp + 8);
+        xp0[i] = ld16(xp);
+        xp1[i] = ld16(xp + 8);
+        if constexpr (MATH == kMathF32) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xv[i][2 * q] = bf16_lo(p0[q]);
-            xv[i][2 * q + 1] = bf16_hi(p0[q]);
-            xv[i][8 + 2 * q] = bf16_lo(p1[q]);
-            xv[i][8 + 2 * q + 1] = bf16_hi(p1[q]);
+            for (int q = 0; q < 4; ++q) {
+                xv[i][2 * q] = bf16_lo(xp0[i][q]);
+                xv[i][2 * q + 1] = bf16_hi(xp0[i][q]);
+                xv[i][8 + 2 * q] = bf16_lo(xp1[i][q]);
+                xv[i][8 + 2 * q + 1] = bf16_hi(xp1[i][q]);
+            }
         }
     }
 
     const size_t nbr = (size_t)(H >> 5);             // scale bytes per row
     const size_t erow = (size_t)e * 2 * I;           // first row of expert e
+    const int jbase = jb * (G * R) + grp;
     float res[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int j = jb * R + r;
+        const int j = jbase + r * G;
         const uint8_t *wg = a.w + (erow + j) * (size_t)H;
         const uint8_t *wu = wg + (size_t)I * H;
         const uint8_t *sg = a.s + (erow + j) * nbr;
@@ -95,30 +112,172 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
         float g = 0.f, u = 0.f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = lane + 64 * i;
+            const int c = tl + LPR * i;
             const bool ok = !TAIL || c < NC;
             const int cc = ok ? c : 0;
-            const u32x4 qg = ld16(wg + cc * 16);
-            const u32x4 qu = ld16(wu + cc * 16);
+            const u32x4 qg = ldw<NT>(wg + cc * 16);
+            const u32x4 qu = ldw<NT>(wu + cc * 16);
             const float fg = e8m0_operand(sg[cc >> 1]);
             const float fu = e8m0_operand(su[cc >> 1]);
-            const float g2 = dot16_f32(qg, fg, xv[i], g);
-            const float u2 = dot16_f32(qu, fu, xv[i], u);
+            float g2, u2;
+            if constexpr (MATH == kMathF32) {
+                g2 = dot16_f32(qg, fg, xv[i], g);
+                u2 = dot16_f32(qu, fu, xv[i], u);
+            } else {
+                g2 = dot16_dot2(qg, fg, xp0[i], xp1[i], g);
+                u2 = dot16_dot2(qu, fu, xp0[i], xp1[i], u);
+            }
             g = ok ? g2 : g;                         // lanes past the row end add nothing
             u = ok ? u2 : u;
         }
-        g = wave_sum(g);
-        u = wave_sum(u);
+        g = group_sum<LPR>(g);
+        u = group_sum<LPR>(u);
         // SiLU(g) * u in FP32; sigmoid written so that exp never overflows.
         const float en = expf(-__builtin_fabsf(g));
         const float sig = g >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
         res[r] = bad ? __builtin_nanf("") : g * sig * u;
     }
+    // lane t < R of group g stores the group's row of step t
     float mine = res[0];
 #pragma unroll
-    for (int r = 1; r < R; ++r) mine = lane == r ? res[r] : mine;
-    if (lane < R)
-        a.out[((size_t)b * a.K + k) * I + (size_t)jb * R + lane] = to_bf16(mine);
+    for (int r = 1; r < R; ++r) mine = tl == r ? res[r] : mine;
+    if (tl < R)
+        a.out[((size_t)b * a.K + k) * I + (size_t)(jbase + tl * G)] = to_bf16(mine);
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up, expert form: one wave per (expert e, block of R rows), serving every
+// (token, slot) routed to e.
+//
+// For batches in which tokens share experts, the token form above reads each
+// routed expert row once per (token, slot) that uses it.  Here the wave first
+// finds, with a ballot over topk_ids, the slots routed to its expert (no
+// index buffer and no extra kernel), loads and converts its R gate rows and R
+// up rows once, then walks those slots: for each it loads x[b] (the next
+// slot's x is fetched while the current one is computed), forms the R gate and
+// up dot products against the registers, reduces them across the wave and
+// writes act[b,k,rows].  Each lane keeps the chunk layout of the token form
+// with 64 lanes per row (chunk c = lane + 64 i, BF16 pairs through
+// v_dot2_f32_bf16), so every act value is bit-identical to that form's.
+// Waves whose expert no token uses exit after the ballot.  Slots with an id
+// outside [0, E) get NaN rows from the waves of expert 0.
+// Wave t handles expert t / nrowblk, row block t % nrowblk: consecutive waves
+// stream consecutive rows of one expert.
+// ---------------------------------------------------------------------------
+template <int CPL, int R, bool TAIL>
+__global__ __launch_bounds__(256) void gate_up_expert_kernel(LayerArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = logical_wave(a);
+    if (t >= a.nwaves) return;
+    const int e = t / a.nrowblk, jb = t % a.nrowblk;
+    const int BK = a.B * a.K, H = a.H, I = a.I, NC = H >> 4;
+
+    // which slots use this expert (and, for expert 0, which ids are invalid)
+    uint64_t any = 0, bad_any = 0;
+    for (int base = 0; base < BK; base += 64) {
+        const int sl = base + lane;
+        const int id = sl < BK ? a.ids[sl] : 0;
+        any |= __builtin_amdgcn_ballot_w64(sl < BK && id == e);
+        bad_any |= __builtin_amdgcn_ballot_w64(e == 0 && sl < BK && (unsigned)id >= (unsigned)a.E);
+    }
+    if (bad_any) {
+        for (int base = 0; base < BK; base += 64) {
+            const int sl = base + lane;
+            const int id = sl < BK ? a.ids[sl] : 0;
+            uint64_t m = __builtin_amdgcn_ballot_w64(sl < BK && (unsigned)id >= (unsigned)a.E);
+            while (m) {
+                const int s0 = base + (int)__builtin_ctzll(m);
+                m &= m - 1;
+                if (lane < R) a.out[(size_t)s0 * I + (size_t)jb * R + lane] = 0x7FC0;   // BF16 quiet NaN
+            }
+        }
+    }
+    if (!any) return;
+
+    // the wave's R gate rows and R up rows, converted once to BF16 pairs
+    const size_t nbr = (size_t)(H >> 5);
+    const size_t erow = (size_t)e * 2 * I + (size_t)jb * R;
+    uint32_t wg[R][CPL][8], wu[R][CPL][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint8_t *pg = a.w + (erow + r) * (size_t)H;
+        const uint8_t *pu = pg + (size_t)I * H;
+        const uint8_t *sg = a.s + (erow + r) * nbr;
+        const uint8_t *su = sg + (size_t)I * nbr;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const int cc = (!TAIL || c < NC) ? c : 0;
+            const u32x4 qg = ld16(pg + cc * 16), qu = ld16(pu + cc * 16);
+            const float fg = e8m0_operand(sg[cc >> 1]), fu = e8m0_operand(su[cc >> 1]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                mx_word_bf16(qg[d], fg, wg[r][i][2 * d], wg[r][i][2 * d + 1]);
+                mx_word_bf16(qu[d], fu, wu[r][i][2 * d], wu[r][i][2 * d + 1]);
+            }
+        }
+    }
+
+    // walk the slots routed to e, in slot order
+    int base = 0;
+    uint64_t m = 0;
+    auto next_slot = [&]() -> int {
+        while (m == 0) {
+            if (base >= BK) return -1;
+            const int sl = base + lane;
+            const int id = sl < BK ? a.ids[sl] : 0;
+            m = __builtin_amdgcn_ballot_w64(sl < BK && id == e);
+            base += 64;
+        }
+        const int s0 = base - 64 + (int)__builtin_ctzll(m);
+        m &= m - 1;
+        return s0;
+    };
+    auto load_x = [&](int sl, u32x4 *x0, u32x4 *x1) {
+        const uint16_t *xb = a.x + (size_t)(sl / a.K) * H;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            const int cc = (!TAIL || c < NC) ? c : 0;
+            x0[i] = ld16(xb + cc * 16);
+            x1[i] = ld16(xb + cc * 16 + 8);
+        }
+    };
+    int cur = next_slot();
+    u32x4 xa0[CPL], xa1[CPL];
+    load_x(cur, xa0, xa1);
+    while (cur >= 0) {
+        const int nxt = next_slot();
+        u32x4 xn0[CPL], xn1[CPL];
+        if (nxt >= 0) load_x(nxt, xn0, xn1);
+        float res[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float g = 0.f, u = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const bool ok = !TAIL || lane + 64 * i < NC;
+                const float g2 = dot16_pre(wg[r][i], xa0[i], xa1[i], g);
+                const float u2 = dot16_pre(wu[r][i], xa0[i], xa1[i], u);
+                g = ok ? g2 : g;
+                u = ok ? u2 : u;
+            }
+            g = wave_sum(g);
+            u = wave_sum(u);
+            const float en = expf(-__builtin_fabsf(g));
+            const float sig = g >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
+            res[r] = g * sig * u;
+        }
+        float mine = res[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) mine = lane == r ? res[r] : mine;
+        if (lane < R) a.out[(size_t)cur * I + (size_t)jb * R + lane] = to_bf16(mine);
+        if (nxt >= 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) { xa0[i] = xn0[i]; xa1[i] = xn1[i]; }
+        }
+        cur = nxt;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -132,7 +291,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
 // Per chunk the lane forms p = sum deq * act in FP32 and folds the router
 // weight in with one FMA, acc += w_k * p.
 // ---------------------------------------------------------------------------
-template <int CPL, int R, bool TAIL>
+template <int CPL, int R, bool TAIL, int MATH, bool NT>
 __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = logical_wave(a);
@@ -176,9 +335,10 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const u32x4 q = ld16(a.w + wbase[i] + h * I);
+            const u32x4 q = ldw<NT>(a.w + wbase[i] + h * I);
             const float f = e8m0_operand(a.s[sbase[i] + h * nbr]);
-            const float p = dot16_bf16(q, f, av0[i], av1[i], 0.f);
+            const float p = MATH == kMathF32 ? dot16_bf16(q, f, av0[i], av1[i], 0.f)
+                                             : dot16_dot2(q, f, av0[i], av1[i], 0.f);
             const float acc2 = __builtin_fmaf(wk[i], p, acc);
             acc = (!TAIL || (lane + 64 * i) < NC) ? acc2 : acc;
         }
@@ -198,7 +358,9 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // For E8M0 byte s = blockIdx.x and code c = threadIdx.x: the conversion of
 // the four codes c, c+1, c+2, c+3 (mod 256) packed in one word, bytes 0..3,
 // exactly as the layer kernels perform it (same operand construction, same
-// instruction).  out[((s * 256) + c) * 4 + j] holds the result for byte j.
+// instructions).  out[((s * 256) + c) * 4 + j] holds the FP32 conversion of
+// byte j; out[65536 * 4 + ((s * 256) + c) * 4 + j] the BF16 conversion,
+// widened to FP32.
 __global__ __launch_bounds__(256) void dequant_probe_kernel(float *out) {
     const uint32_t s = blockIdx.x, c = threadIdx.x;
     const uint32_t word = (c & 255u) | (((c + 1) & 255u) << 8) | (((c + 2) & 255u) << 16) | (((c + 3) & 255u) << 24);
@@ -207,6 +369,9 @@ __global__ __launch_bounds__(256) void dequant_probe_kernel(float *out) {
     const f32x2 hi = mx_pair<true>(word, f);
     float *o = out + ((size_t)s * 256 + c) * 4;
     o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+    const uint32_t blo = mx_pair_bf16<false>(word, f), bhi = mx_pair_bf16<true>(word, f);
+    float *p = o + 65536 * 4;
+    p[0] = bf16_lo(blo); p[1] = bf16_hi(blo); p[2] = bf16_lo(bhi); p[3] = bf16_hi(bhi);
 }
 
 // Reads n16 16-byte words in a grid-stride loop with U independent loads in

@@ -83,9 +83,15 @@ def test_empty_batch_launches_nothing():
 
 def test_bad_launch_config_rejected():
     for cfg in (wd.Launch(3, 0, 0, 0), wd.Launch(0, 5, 0, 0), wd.Launch(0, 0, 3, 0), wd.Launch(0, 0, 0, 7),
-                wd.Launch(0, 0, 0, -1)):
+                wd.Launch(0, 0, 0, -1), wd.Launch(0, 0, 0, 0, None, None, 3), wd.Launch(lanes_per_row=8)):
         assert lib.wd_gate_up_ex(A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(cfg), None) == -7
         assert lib.wd_down_ex(A, A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(cfg), None) == -7
+
+
+def test_lanes_per_row_limits():
+    # grouped rows apply to the gate/up kernel only, and need the row's chunks to fit the lanes
+    assert lib.wd_down_ex(A, A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(wd.Launch(lanes_per_row=16)), None) == -7
+    assert lib.wd_gate_up_ex(A, A, A, A, A, 1, 8, 128, 8192, 768, C.byref(wd.Launch(lanes_per_row=16)), None) == -7
 
 
 def test_helpers_reject_bad_arguments():

@@ -77,16 +77,29 @@ def _bf16_bits(v: np.ndarray) -> np.ndarray:
     return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+FINGERPRINT_CFGS = {
+    "defaults": (None, None),
+    "token-f32": (dict(form=1, math=1), dict(math=1)),
+    "token-dot2": (dict(form=1, math=2), dict(math=2)),
+    "expert": (dict(form=2), dict(math=2, rows_per_wave=8)),
+    "lanes16": (dict(form=1, lanes_per_row=16, rows_per_wave=2), dict(math=1, rows_per_wave=4)),
+}
+
+
+@pytest.mark.parametrize("cfgname", list(FINGERPRINT_CFGS))
 @pytest.mark.parametrize("E,K,H,I,B", [(128, 8, 2048, 768, 32), (8, 2, 128, 64, 3), (5, 3, 96, 160, 4)])
-def test_routing_fingerprint_bit_exact(E, K, H, I, B):
-    log(f"[case] fingerprint E={E} K={K} H={H} I={I} B={B}")
+def test_routing_fingerprint_bit_exact(E, K, H, I, B, cfgname):
+    cfg_gu, cfg_dn = FINGERPRINT_CFGS[cfgname]
+    if cfgname == "lanes16" and H > 2048:
+        pytest.skip("16 lanes per row holds at most H = 2048")
+    log(f"[case] fingerprint E={E} K={K} H={H} I={I} B={B} cfg={cfgname}")
     L, u = fingerprint_layer(E, K, H, I)
     rng = np.random.default_rng(E + K + H + I + B)
     ids = np.stack([rng.permutation(E)[:K] for _ in range(B)]).astype(np.int32)
     w = np.array([[2.0 ** -(k + 1) for k in range(K)]] * B, np.float32)
     x = np.full((B, H), 0x3F80, np.uint16)
     dl, dt = DevLayer(L), DevTokens(gen.Tokens(x=x, ids=ids, w=w))
-    act, out = run_layer(dl, dt)
+    act, out = run_layer(dl, dt, cfg_gu=cfg_gu, cfg_dn=cfg_dn)
     act_e, y_e = fingerprint_expect(u, ids, w, H, I)
     assert np.array_equal(bits_of(act), _bf16_bits(act_e))       # act values are exact in BF16
     assert np.array_equal(bits_of(out), _bf16_bits(y_e))         # y exact in FP32, then one RNE
@@ -148,19 +161,92 @@ def test_deterministic_and_full_coverage(mid):
 
 def test_launch_configurations_agree_bitwise(mid):
     """Rows per wave, waves per workgroup, work order and XCD numbering change
-    only which wave computes an output, never how: results are bit-identical."""
+    only which wave computes an output, never how: results are bit-identical.
+    (Lanes per gate/up row changes the summation order; see the next test.)"""
     dl, t = mid
     dt = DevTokens(t)
-    a0, o0 = run_layer(dl, dt)
-    a0, o0 = bits_of(a0), bits_of(o0)
+    for math in (1, 2):
+        base = dict(math=math, form=1, lanes_per_row=64, weight_loads=1)
+        a0, o0 = run_layer(dl, dt, cfg_gu=base, cfg_dn=base)
+        a0, o0 = bits_of(a0), bits_of(o0)
+        for r in (1, 2, 4, 8):
+            for wpb in (1, 3, 4):
+                for order in (1, 2):
+                    for remap in (1, 2):
+                        cfg = dict(rows_per_wave=r, waves_per_block=wpb, order=order, xcd_remap=remap, math=math,
+                                   form=1, lanes_per_row=64, weight_loads=1)
+                        cfg_gu = dict(cfg, rows_per_wave=min(r, 4))
+                        a, o = run_layer(dl, dt, cfg_gu=cfg_gu, cfg_dn=cfg)
+                        assert np.array_equal(bits_of(a), a0), cfg
+                        assert np.array_equal(bits_of(o), o0), cfg
+
+
+@pytest.mark.parametrize("lpr", [16, 32, 64])
+def test_gate_up_lane_groups(mid, lpr):
+    """Gate/up with 16, 32 or 64 lanes per row: every row/order/grouping gives
+    the same bits for a fixed lane count, and all lane counts stay within the
+    intermediate parity bounds of each other (only the FP32 summation order
+    differs)."""
+    from tests.gpu_common import act_flip_stats
+    dl, t = mid
+    dt = DevTokens(t)
+    ref, _ = run_layer(dl, dt, cfg_gu=dict(math=2, lanes_per_row=64), cfg_dn=dict(math=2))
+    a0 = None
     for r in (1, 2, 4):
-        for wpb in (1, 3, 4):
-            for order in (1, 2):
-                for remap in (1, 2):
-                    cfg = dict(rows_per_wave=r, waves_per_block=wpb, order=order, xcd_remap=remap)
-                    a, o = run_layer(dl, dt, cfg_gu=cfg, cfg_dn=cfg)
-                    assert np.array_equal(bits_of(a), a0), cfg
-                    assert np.array_equal(bits_of(o), o0), cfg
+        for order in (1, 2):
+            for remap in (1, 2):
+                cfg = dict(rows_per_wave=r, order=order, xcd_remap=remap, math=2, lanes_per_row=lpr)
+                a, _ = run_layer(dl, dt, cfg_gu=cfg, cfg_dn=dict(math=2))
+                if a0 is None:
+                    a0 = bits_of(a)
+                assert np.array_equal(bits_of(a), a0), cfg
+    frac, ulps, within = act_flip_stats(a0, bits_of(ref))
+    assert frac <= 2e-3 and within, (frac, ulps)
+
+
+@pytest.mark.parametrize("B", [1, 9, 40])
+def test_gate_up_expert_form_matches_token_form(B):
+    """The expert form (one wave per expert row block, serving every slot
+    routed to it) keeps the token form's lane layout and summation order:
+    its intermediate is bit-identical, for any routing (duplicates, unused
+    experts, many tokens per expert)."""
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=91)
+    dl = DevLayer(gen.make_layer(spec, threads=16))
+    t = gen.make_tokens(spec, B, routing="zipf")
+    t.ids[0, 1] = t.ids[0, 0]                      # a duplicated expert within a token
+    dt = DevTokens(t)
+    ref, _ = run_layer(dl, dt, cfg_gu=dict(form=1, math=2, lanes_per_row=64, weight_loads=1))
+    for r in (1, 2, 4):
+        for order in (1, 2):
+            for remap in (1, 2):
+                a, _ = run_layer(dl, dt, cfg_gu=dict(form=2, rows_per_wave=r, order=order, xcd_remap=remap))
+                assert np.array_equal(bits_of(a), bits_of(ref)), (r, order, remap)
+
+
+def test_gate_up_expert_form_bad_ids():
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=92)
+    dl = DevLayer(gen.make_layer(spec, threads=16))
+    t = gen.make_tokens(spec, 12)
+    ids = t.ids.copy(); ids[3, 2] = 16; ids[7, 0] = -5
+    dt = DevTokens(gen.Tokens(x=t.x, ids=ids, w=t.w))
+    a, o = run_layer(dl, dt, cfg_gu=dict(form=2))
+    af = a.float().cpu().numpy()
+    assert np.isnan(af[3, 2]).all() and np.isnan(af[7, 0]).all()
+    assert np.isfinite(np.delete(af.reshape(-1, spec.I), [3 * 4 + 2, 7 * 4 + 0], axis=0)).all()
+    of = o.float().cpu().numpy()
+    assert np.isnan(of[3]).all() and np.isnan(of[7]).all()
+
+
+def test_weight_load_modes_agree_bitwise(mid):
+    """Cached and non-temporal weight loads read the same bytes."""
+    dl, t = mid
+    dt = DevTokens(t)
+    runs = []
+    for wl in (1, 2):
+        runs.append(run_layer(dl, dt, cfg_gu=dict(weight_loads=wl, math=2, form=1, rows_per_wave=1),
+                              cfg_dn=dict(weight_loads=wl, math=2, rows_per_wave=1)))
+    (a1, o1), (a2, o2) = runs
+    assert np.array_equal(bits_of(a1), bits_of(a2)) and np.array_equal(bits_of(o1), bits_of(o2))
 
 
 def test_fused_entry_matches_two_calls(mid):

@@ -58,10 +58,14 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("math", [0, 1, 2])
 @pytest.mark.parametrize("name", list(CASES))
-def test_layer_parity(name):
+def test_layer_parity(name, math):
+    """math 0: the library's defaults for the batch size; 1 / 2: the FP32 /
+    BF16-pair math with the token form."""
     spec, B, routing, only_routed = CASES[name]
-    log(f"[case] {name} B={B} routing={routing}")
+    cfg = dict(math=math, form=1) if math else dict()
+    log(f"[case] {name} B={B} routing={routing} math={math}")
     t = gen.make_tokens(spec, B, routing=routing)
     dl = layer_for(spec, experts=t.ids.ravel() if only_routed else None)
     L = dl.host
@@ -70,7 +74,7 @@ def test_layer_parity(name):
     k = unit_shift(y64)
     sd_k = shifted(dl.sd, k)
 
-    act, out = run_layer(dl, dt, sd=sd_k)
+    act, out = run_layer(dl, dt, sd=sd_k, cfg_gu=cfg, cfg_dn=cfg)
     frac, ulps, within = act_flip_stats(bits_of(act), act_o)
     log(f"[act] {name}: flip fraction {frac:.2e}, max {ulps:.2f} ulp, all within bound: {within}, n={act_o.size}")
     # rare flips; each within one ulp, or (cancellation) within 2^-14 of the row's scale
@@ -79,7 +83,7 @@ def test_layer_parity(name):
     # down kernel alone, fed the oracle's intermediate: only FP32 summation and output rounding differ
     from moe_decode_gate_amd import binding as wd
     act_dev = torch.from_numpy(act_o.view(np.int16)).cuda().view(torch.bfloat16)
-    out_k2 = wd.down(act_dev, dt.ids, dt.w, dl.wd, sd_k)
+    out_k2 = wd.down(act_dev, dt.ids, dt.w, dl.wd, sd_k, cfg=cfg)
     torch.cuda.synchronize()
     assert_output_parity(bits_of(out_k2), y64 * 2.0 ** k, f"{name} down-only (Sd{k:+d})")
     # whole layer against the oracle's down projection of the GPU's own intermediate
@@ -89,15 +93,18 @@ def test_layer_parity(name):
     assert_output_parity(bits_of(out), y64 * 2.0 ** k, f"{name} layer (Sd{k:+d})", slack=2e-4)
     # the literal, unshifted data: cosine and per-element bounds still hold
     if k != 0:
-        _, out0 = run_layer(dl, dt)
+        _, out0 = run_layer(dl, dt, cfg_gu=cfg, cfg_dn=cfg)
         assert_output_parity(bits_of(out0), y64, f"{name} layer (unshifted)", unit_scale=False, slack=2e-4)
 
 
-def test_dequant_probe_matches_format_definition():
-    """The hardware conversion, exactly as the kernels use it, against the OCP
-    E4M3 x E8M0 definition for all 256 codes x 256 scale bytes x 4 byte lanes."""
+@pytest.mark.parametrize("math", [1, 2])
+def test_dequant_probe_matches_format_definition(math):
+    """The hardware conversion, exactly as the kernels use it (math mode 1:
+    to FP32; 2: to BF16), against the OCP E4M3 x E8M0 definition for all 256
+    codes x 256 scale bytes x 4 byte lanes.  Both targets hold every product
+    whose magnitude is a normal FP32 number exactly."""
     from moe_decode_gate_amd import binding as wd
-    got = wd.dequant_probe().cpu().numpy().astype(np.float64)          # [s, c, lane]
+    got = wd.dequant_probe()[math - 1].cpu().numpy().astype(np.float64)   # [s, c, lane]
     t4, t8 = oracle.e4m3_table(), oracle.e8m0_table()
     codes = (np.arange(256)[:, None] + np.arange(4)[None, :]) & 255    # [c, lane]
     exact = t8[:, None, None] * t4[codes][None, :, :]                  # FP64 exact product
