@@ -151,6 +151,15 @@ int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_
                   void *workspace, size_t workspace_bytes, uint16_t *out,
                   int B, int K, int E, int H, int I, void *stream);
 
+/* Router (top-k gating ahead of the layer; the pages name it as routing each
+ * token to 8 of 128 experts: the Chinese summary's 传统路径的困境 section, p2
+ * Method).  For each token b: topk_ids[b, 0..K) = the experts with the K
+ * largest logits[b, :] (larger first; equal logits: lower expert index
+ * first), topk_w[b, k] = softmax over the chosen logits,
+ * exp(l_k - l_0) / sum_j exp(l_j - l_0), in FP32.  logits [B, E] fp32, row
+ * major, finite; 1 <= K <= min(E, 64), E <= 1024.  One wave per token. */
+int wd_route(const float *logits, int B, int E, int K, int32_t *topk_ids, float *topk_w, void *stream);
+
 /* Bytes of the intermediate act[B,K,I] (BF16); 0 for invalid sizes. */
 size_t wd_workspace_bytes(int B, int K, int I);
 

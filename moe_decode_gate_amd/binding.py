@@ -54,6 +54,7 @@ _sig = {
     "wd_down_ex": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, C.POINTER(Launch), _P]),
     "wd_moe_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _I, _I, _I, _I, _I, _P]),
     "wd_workspace_bytes": (_S, [_I, _I, _I]),
+    "wd_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "wd_status_string": (C.c_char_p, [_I]),
     "wd_dequant_probe": (_I, [_P, _P]),
     "wd_stream_read": (_I, [_P, _S, _P, _I, _I, _P]),
@@ -155,6 +156,19 @@ def down(act, topk_ids, topk_w, w_d, s_d, out=None, cfg=None, stream=None):
                              B, K, E, H, I, _cfg(cfg), _stream(stream))
     _check(rc, "wd_down")
     return out
+
+
+def route(logits, K: int, topk_ids=None, topk_w=None, stream=None):
+    """(topk_ids [B,K] int32, topk_w [B,K] fp32) from router logits [B,E] fp32."""
+    _dev(logits, "logits", (torch.float32,))
+    B, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((B, K), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((B, K), dtype=torch.float32, device=logits.device)
+    _dev(topk_ids, "topk_ids", (torch.int32,), (B, K)); _dev(topk_w, "topk_w", (torch.float32,), (B, K))
+    _check(_lib.wd_route(_ptr(logits), B, E, K, _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "wd_route")
+    return topk_ids, topk_w
 
 
 def workspace_bytes(B: int, K: int, I: int) -> int:

@@ -329,6 +329,24 @@ const char *wd_status_string(int status) {
     return "unknown status";
 }
 
+int wd_route(const float *logits, int B, int E, int K, int32_t *topk_ids, float *topk_w, void *stream) {
+    if (B < 0 || E < 1 || K < 1 || K > E) return WD_ERR_DIMS;
+    if (E > 1024 || K > 64) return WD_ERR_UNSUPPORTED;
+    if (B > 0 && (!logits || !topk_ids || !topk_w)) return WD_ERR_NULL;
+    if (B > 0 && (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))) return WD_ERR_ALIGN;
+    if (B == 0) return WD_OK;
+    int rc = check_device();
+    if (rc) return rc;
+    const int rpl = (E + 63) / 64;
+    void (*fn)(const float *, int, int, int, int32_t *, float *) =
+        rpl <= 1 ? wd::route_kernel<1> : rpl <= 2 ? wd::route_kernel<2> : rpl <= 4 ? wd::route_kernel<4>
+        : rpl <= 8 ? wd::route_kernel<8> : wd::route_kernel<16>;
+    const int wpb = 4;
+    hipLaunchKernelGGL(fn, dim3((B + wpb - 1) / wpb), dim3(64 * wpb), 0, (hipStream_t)stream,
+                       logits, B, E, K, topk_ids, topk_w);
+    return launched();
+}
+
 int wd_dequant_probe(float *out, void *stream) {
     if (!out) return WD_ERR_NULL;
     if (!aligned(out, 16)) return WD_ERR_ALIGN;

@@ -166,6 +166,35 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Maximum / minimum over the 64 lanes of a wave, returned to every lane;
+// same exchange pattern as wave_sum.  Must run with all 64 lanes active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_upd_i(int v, int old) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ float wave_max(float v) {
+    auto step = [](float a, int b) { return __builtin_fmaxf(a, __builtin_bit_cast(float, b)); };
+    const int ninf = __builtin_bit_cast(int, -__builtin_inff());
+    v = step(v, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v = step(v, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v = step(v, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v = step(v, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    v = step(v, dpp_upd_i<0x142, 0xA>(__builtin_bit_cast(int, v), ninf));
+    v = step(v, dpp_upd_i<0x143, 0xC>(__builtin_bit_cast(int, v), ninf));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ int wave_min(int v) {
+    auto step = [](int a, int b) { return a < b ? a : b; };
+    const int big = 0x7FFFFFFF;
+    v = step(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+    v = step(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+    v = step(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));
+    v = step(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));
+    v = step(v, dpp_upd_i<0x142, 0xA>(v, big));
+    v = step(v, dpp_upd_i<0x143, 0xC>(v, big));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Sum over each group of LPR consecutive lanes (LPR = 16, 32 or 64), returned
 // to every lane of the group (bit-identical within a group).  The in-row
 // butterfly is the one of wave_sum; for 32-lane groups row_bcast:15 adds row

@@ -352,6 +352,52 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Router: top-k gating ahead of the layer.  One wave per token; lane l holds
+// logits l + 64 r (r < RPL).  K rounds: each finds the largest remaining logit
+// (wave max) and, among lanes holding that value, the lowest expert index
+// (wave min), then retires it.  Lane k keeps the k-th choice.  Weights are the
+// softmax over the chosen logits, exp(l_k - l_0) / sum_j exp(l_j - l_0), in
+// FP32.  Logits must be finite.
+// ---------------------------------------------------------------------------
+template <int RPL>
+__global__ __launch_bounds__(256) void route_kernel(const float *logits, int B, int E, int K, int32_t *ids,
+                                                    float *w) {
+    const int lane = threadIdx.x & 63;
+    const int b = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
+    if (b >= B) return;
+    float v[RPL];
+    bool live[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int e = lane + 64 * r;
+        live[r] = e < E;
+        v[r] = live[r] ? logits[(size_t)b * E + e] : 0.f;
+    }
+    int my_id = 0;
+    float my_l = 0.f;
+    for (int k = 0; k < K; ++k) {
+        float bv = -__builtin_inff();
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)       // ascending index within the lane: strict > keeps the lowest
+            if (live[r] && (bi == 0x7FFFFFFF || v[r] > bv)) { bv = v[r]; bi = lane + 64 * r; }
+        const float m = wave_max(bv);
+        const int idx = wave_min(bi != 0x7FFFFFFF && bv == m ? bi : 0x7FFFFFFF);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)
+            if (lane + 64 * r == idx) live[r] = false;
+        if (lane == k) { my_id = idx; my_l = m; }
+    }
+    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_l), 0));
+    const float ez = lane < K ? expf(my_l - l0) : 0.f;
+    const float z = wave_sum(ez);
+    if (lane < K) {
+        ids[(size_t)b * K + lane] = my_id;
+        w[(size_t)b * K + lane] = ez / z;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Measurement helpers.
 // ---------------------------------------------------------------------------
 

@@ -33,7 +33,7 @@ import torch
 __all__ = [
     "LayerSpec", "CONFIGS", "Layer", "Tokens",
     "quantize_mxfp8", "bf16_bits", "make_layer", "make_tokens",
-    "layer_unique_bytes", "expert_bytes",
+    "layer_unique_bytes", "expert_bytes", "make_logits",
 ]
 
 BLOCK = 32          # MX block: elements sharing one E8M0 scale
@@ -196,6 +196,13 @@ def make_tokens(spec: LayerSpec, B: int, routing: str = "softmax", step: int = 0
     z = np.exp(chosen - chosen.max(axis=1, keepdims=True))
     w = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
     return Tokens(x=x, ids=np.ascontiguousarray(ids, dtype=np.int32), w=np.ascontiguousarray(w))
+
+
+def make_logits(spec: LayerSpec, B: int, step: int = 0) -> np.ndarray:
+    """Router logits [B, E] as float32: the same N(0,1) draws that make_tokens'
+    softmax routing ranks, rounded to FP32 (the router's input precision)."""
+    rr = np.random.default_rng(np.random.SeedSequence(spec.seed, spawn_key=(_KIND_ROUTE, step, B)))
+    return np.ascontiguousarray(rr.standard_normal((B, spec.E)).astype(np.float32))
 
 
 def expert_bytes(spec: LayerSpec) -> int:

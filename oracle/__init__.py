@@ -15,5 +15,5 @@ Contents
 """
 from .ref import (  # noqa: F401
     e4m3_table, e8m0_table, dequant, bf16_value, bf16_rne, round_f32, silu,
-    gate_up, down, moe_decode, max_threads, lib_path,
+    gate_up, down, moe_decode, route, max_threads, lib_path,
 )

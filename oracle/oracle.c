@@ -26,6 +26,9 @@
  *   act[b,k,j]    = BF16_RNE( FP32_RNE( g * sigmoid(g) * u ) )
  *   y[b,h]        = sum_k w[b,k] * sum_i deq(Wd[e,h,i], Sd[e,h,i/32]) * act[b,k,i]
  *
+ * The router that produces topk_ids / topk_w from logits is oracle_route
+ * (end of file).
+ *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - gate rows are 0..I-1 and up rows I..2I-1 of the [E,2I,H] tensor;
  *   - MXFP8 is OCP MX: E4M3 "FN" elements (no infinities, S.1111.111 = NaN,
@@ -192,6 +195,37 @@ int oracle_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
     int rc = oracle_gate_up(x, ids, wgu, sgu, B, K, E, H, I, act, 0, 0, nthreads);
     if (rc) return rc;
     return oracle_down(act, ids, w, wd, sd, B, K, E, H, I, y, nthreads);
+}
+
+/* ---- router ------------------------------------------------------------
+
+ * Top-k gating ahead of the layer (the pages name it only as routing each
+ * token to a few of many experts, "128 选 8": the Chinese summary, section
+ * 传统路径的困境; p2 Method).  Plain definition: the K largest logits of a
+ * token (larger first; equal logits: the lower expert index first), and
+ * weights = softmax over the full row renormalised to the chosen K, which is
+ * the softmax of the chosen logits: w_k = exp(l_k - l_max) / sum_j exp(l_j - l_max).
+ * FP64 throughout.  Logits must be finite. */
+int oracle_route(const float *logits, int B, int E, int K, int32_t *ids, double *w) {
+    if (B < 0 || E < 1 || K < 1 || K > E) return -2;
+    for (long b = 0; b < B; ++b) {
+        const float *l = logits + b * (long)E;
+        for (int k = 0; k < K; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int j = 0; j < k; ++j) taken |= ids[b * K + j] == e;
+                if (taken) continue;
+                if (best < 0 || l[e] > l[best]) best = e;     /* strict: ties keep the lower index */
+            }
+            ids[b * K + k] = best;
+        }
+        const double lmax = (double)l[ids[b * K]];
+        double z = 0.0;
+        for (int k = 0; k < K; ++k) z += exp((double)l[ids[b * K + k]] - lmax);
+        for (int k = 0; k < K; ++k) w[b * K + k] = exp((double)l[ids[b * K + k]] - lmax) / z;
+    }
+    return 0;
 }
 
 int oracle_max_threads(void) {

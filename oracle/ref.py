@@ -48,6 +48,8 @@ def _load():
         L.oracle_moe_decode.restype = i
         L.oracle_moe_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, P, i]
         L.oracle_max_threads.restype = i
+        L.oracle_route.restype = i
+        L.oracle_route.argtypes = [P, i, i, i, P, P]
         _lib = L
     return _lib
 
@@ -151,6 +153,17 @@ def moe_decode(x, ids, w, wgu, sgu, wd, sd, nthreads: int = 0):
     _rc(_load().oracle_moe_decode(_p(x), _p(ids), _p(w), _p(wgu), _p(sgu), _p(wd), _p(sd),
                                   B, K, E, H, I, _p(act), _p(y), nthreads))
     return y, act
+
+
+def route(logits, K: int):
+    """(ids [B,K] int32, w [B,K] FP64): top-K of each row of logits [B,E]
+    (larger first, ties to the lower index) and the softmax over the chosen K."""
+    logits = _c(logits, np.float32)
+    B, E = logits.shape
+    ids = np.empty((B, K), np.int32)
+    w = np.empty((B, K), np.float64)
+    _rc(_load().oracle_route(_p(logits), B, E, K, _p(ids), _p(w)))
+    return ids, w
 
 
 def max_threads() -> int:

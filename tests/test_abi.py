@@ -104,6 +104,17 @@ def test_helpers_reject_bad_arguments():
     assert lib.wd_gpu_sleep(-1, None) == -7
 
 
+def test_route_rejects_bad_arguments():
+    assert lib.wd_route(A, 1, 128, 0, A, A, None) == -2
+    assert lib.wd_route(A, 1, 8, 9, A, A, None) == -2
+    assert lib.wd_route(A, -1, 8, 2, A, A, None) == -2
+    assert lib.wd_route(A, 1, 2048, 8, A, A, None) == -7
+    assert lib.wd_route(A, 1, 128, 65, A, A, None) == -7
+    assert lib.wd_route(None, 1, 128, 8, A, A, None) == -1
+    assert lib.wd_route(A + 2, 1, 128, 8, A, A, None) == -3
+    assert lib.wd_route(None, 0, 128, 8, None, None, None) == 0
+
+
 def test_chunk_to_slot_division_is_exact():
     # The down kernel maps chunk c to slot c // (I/16) by (c * magic) >> 22 with
     # magic = 2^22 // nci + 1; exact for every chunk of every supported size.

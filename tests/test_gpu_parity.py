@@ -122,13 +122,24 @@ def test_dequant_probe_matches_format_definition(math):
     assert np.array_equal(np.signbit(got[core & zero]), np.signbit(exact[core & zero]))
     # NaN codes stay NaN for every scale in range
     assert np.isnan(got[(s_idx >= 1) & (s_idx <= 254) & nan_code]).all()
-    # report the remaining classes (FP32 subnormal or overflowing products, scale bytes 0 and 255)
+    # the remaining classes: FP32-overflowing and FP32-subnormal products, E8M0 bytes 0 and 255
     rest = ~core & ~nan_code
     inr = (s_idx >= 1) & (s_idx <= 254)
     for name, m in (("fp32 overflow", rest & inr & ~np.isfinite(want32)),
                     ("fp32 subnormal", rest & inr & np.isfinite(want32)),
                     ("s=0", rest & (s_idx == 0)), ("s=255", rest & (s_idx == 255))):
-        if m.any():
-            eq = (got[m] == want32[m]) | (np.isnan(got[m]) & np.isnan(want32[m]))
-            log(f"[probe] {name}: {int(m.sum())} cases, {int(eq.sum())} equal to FP32(exact); "
-                f"zeros {int((got[m] == 0).sum())}, inf {int(np.isinf(got[m]).sum())}, nan {int(np.isnan(got[m]).sum())}")
+        eq = (got[m] == want32[m]) | (np.isnan(got[m]) & np.isnan(want32[m]))
+        log(f"[probe] {name}: {int(m.sum())} cases, {int(eq.sum())} equal to FP32(exact); "
+            f"zeros {int((got[m] == 0).sum())}, inf {int(np.isinf(got[m]).sum())}, nan {int(np.isnan(got[m]).sum())}")
+    # E8M0 byte 255 is NaN for every code; overflow gives a signed infinity
+    assert np.isnan(got[s_idx == 255]).all()
+    ovf = rest & inr & ~np.isfinite(want32)
+    assert np.array_equal(got[ovf], want32[ovf])
+    sub = rest & ((s_idx == 0) | inr) & np.isfinite(want32) & ~(s_idx == 255)
+    if math == 1:
+        # FP32 conversion: exact also for subnormal products and E8M0 byte 0 (2^-127)
+        assert np.array_equal(got[sub], want32[sub])
+    else:
+        # BF16 conversion: FP32-subnormal products land on BF16 subnormals (step 2^-133),
+        # rounded to nearest
+        assert (np.abs(got[sub] - exact[sub]) <= 2.0 ** -134).all()

@@ -306,3 +306,51 @@ def test_golden_tiny_layer_regression():
     y, act = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
     assert act.ravel().tolist() == ref["act_bits"]
     assert [float(v).hex() for v in y.ravel()] == ref["y"]
+
+
+# ----------------------------------------------------------------- router --
+
+def test_route_matches_numpy_topk_and_scipy_softmax(rng):
+    import scipy.special
+    logits = rng.standard_normal((50, 128)).astype(np.float32)
+    ids, w = oracle.route(logits, 8)
+    # library top-k: stable argsort on (-logit) keeps the lower index first among equals
+    ref_ids = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :8]
+    assert np.array_equal(ids, ref_ids)
+    chosen = np.take_along_axis(logits.astype(np.float64), ref_ids, axis=1)
+    np.testing.assert_allclose(w, scipy.special.softmax(chosen, axis=1), rtol=1e-14)
+    # renormalised full softmax restricted to the chosen set is the same thing
+    full = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    sel = np.take_along_axis(full, ref_ids, axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-12)
+
+
+def test_route_ties_and_invariants():
+    logits = np.zeros((3, 16), np.float32)
+    logits[0, [3, 7, 11]] = 2.0                      # three-way tie: indices ascending
+    logits[1, :] = -1.0                               # all equal: 0, 1, 2, ...
+    logits[2, 5] = 5.0
+    ids, w = oracle.route(logits, 4)
+    assert ids[0].tolist() == [3, 7, 11, 0]
+    assert ids[1].tolist() == [0, 1, 2, 3]
+    assert ids[2, 0] == 5
+    np.testing.assert_allclose(w[1], 0.25, rtol=0)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-15)
+    # shift invariance and K = 1
+    g = np.random.default_rng(3).standard_normal((4, 32)).astype(np.float32)
+    i1, w1 = oracle.route(g, 5)
+    i2, w2 = oracle.route(g + np.float32(8.0), 5)
+    assert np.array_equal(i1, i2)
+    np.testing.assert_allclose(w1, w2, rtol=1e-6)     # FP32 inputs: the shift itself rounds
+    i3, w3 = oracle.route(g, 1)
+    assert np.array_equal(i3[:, 0], i1[:, 0]) and (w3 == 1.0).all()
+    with pytest.raises(ValueError):
+        oracle.route(g, 33)
+
+
+def test_route_agrees_with_generator_softmax_routing():
+    spec = gen.LayerSpec(E=128, K=8, H=64, I=32, seed=12)
+    t = gen.make_tokens(spec, 16)
+    ids, w = oracle.route(gen.make_logits(spec, 16), 8)
+    assert np.array_equal(ids, t.ids)                 # same draws, FP32 ranking keeps the order
+    np.testing.assert_allclose(w, t.w, rtol=1e-6)
