@@ -21,6 +21,8 @@ steps never find their expert rows in the 256 MB last-level cache.
   hbm_read_peak    best-of-10 contiguous-read bandwidth of a 16-byte-load
                    kernel over a 4 GiB buffer, measured in the same run
   cpu_baseline     the CPU oracle on this host's cores on a bounded sample
+  stack48          a 48-layer decode step (chained layers, per-layer routing
+                   from the router kernel) at B in {1, 2, 4, 8, 16, 32, 64}
 """
 from __future__ import annotations
 
@@ -160,6 +162,67 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int):
     return res
 
 
+def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64), layers=48, reps=10):
+    """A decode step through `layers` MoE layers of the layer's shape: distinct
+    device copies of the weights (about 30 GB for 48 layers), per-layer routing
+    from the router kernel on per-layer seeded logits, each layer's output
+    feeding the next layer's input, all layers captured in one HIP graph per
+    batch size and replayed `reps` times."""
+    spec = L.spec
+    base = [torch.from_numpy(a).to("cuda") for a in (L.wgu, L.sgu, L.wd, L.sd)]
+    copies = [base] + [[t.clone() for t in base] for _ in range(layers - 1)]
+    per_expert = gen.expert_bytes(spec)
+    out = []
+    for B in batches:
+        ids, ws, uniq = [], [], 0
+        for l in range(layers):
+            lspec = gen.LayerSpec(E=spec.E, K=spec.K, H=spec.H, I=spec.I, seed=gen.CONFIGS["stack"]["spec"].seed + l)
+            logits = torch.from_numpy(gen.make_logits(lspec, B)).to("cuda")
+            i, w = wd.route(logits, spec.K)
+            ids.append(i); ws.append(w)
+        torch.cuda.synchronize()
+        for i in ids:
+            uniq += int(torch.unique(i).numel())
+        x0 = torch.from_numpy(gen.make_tokens(spec, B).x.view(np.int16)).to("cuda").view(torch.bfloat16)
+        xa, xb = x0.clone(), torch.empty_like(x0)
+        act = torch.empty((B, spec.K, spec.I), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            src, dst = xa, xb
+            for l in range(layers):
+                c = copies[l]
+                wd.gate_up(src, ids[l], c[0], c[1], act=act)
+                wd.down(act, ids[l], ws[l], c[2], c[3], out=dst)
+                src, dst = dst, src
+
+        step()                                   # eager once (warm-up, device checks)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / reps
+        gbps = uniq * per_expert / (us * 1e-6) / 1e9
+        out.append(dict(B=B, step_us=us, tokens_per_s=B / (us * 1e-6), unique_experts=uniq,
+                        GBps=gbps, frac_of_measured_read_peak=gbps / read_peak))
+        eprint(f"[bench] stack B={B}: {out[-1]}")
+        del g
+    del copies, base
+    torch.cuda.empty_cache()
+    best = max(out, key=lambda r: r["GBps"])
+    return dict(layers=layers, per_B=out, peak_bandwidth_B=best["B"],
+                note="distinct weight copies per layer, per-layer routing, chained activations, one HIP graph")
+
+
 def hbm_read_peak(torch, wd, nbytes=4 << 30, reps=5):
     """Best contiguous-read bandwidth over launch shapes (GB/s), and the copy
     bandwidth of 1 GiB (read + write bytes / time)."""
@@ -230,6 +293,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="distinct weight copies (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-b32", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs the layer "
@@ -274,6 +338,8 @@ def main():
         del w32
         torch.cuda.empty_cache()
 
+    stack = None if args.no_stack else measure_stack(torch, wd, gen, L, peak)
+
     cpu = None if args.no_cpu else cpu_baseline(oracle, L, gen, 1)
 
     achieved = r1["gate_up_GBps"]
@@ -295,6 +361,7 @@ def main():
         "frac_of_measured_read_peak": r1["layer_GBps_graph"] / peak,
         "b1": r1,
         "b32": r32,
+        "stack48": stack,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }

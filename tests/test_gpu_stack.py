@@ -1,0 +1,101 @@
+"""The 48-layer decode-step stack: layers chained (each output is the next
+input), per-layer routing from the router kernel, all layers in one HIP graph.
+Parity is layer-local: the oracle gets the GPU's own BF16 input of a layer and
+that layer's routing, and its output is compared with the GPU's (chained
+magnitudes shrink roughly quadratically per layer, so only the first layers
+carry signal; the last layer is checked on a fresh N(0,1) input)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_decode_gate_amd import inputs as gen
+from tests.gpu_common import assert_output_parity, bits_of, log
+
+pytestmark = pytest.mark.gpu
+
+LAYERS = 48
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+@pytest.fixture(scope="module")
+def stack():
+    from moe_decode_gate_amd import binding as wd
+    spec = gen.CONFIGS["stack"]["spec"]
+    B = 4
+    L = gen.make_layer(spec, threads=16)
+    dev = [torch.from_numpy(a).cuda() for a in (L.wgu, L.sgu, L.wd, L.sd)]
+    ids, ws, logits = [], [], []
+    for l in range(LAYERS):
+        lspec = gen.LayerSpec(E=spec.E, K=spec.K, H=spec.H, I=spec.I, seed=spec.seed + l)
+        lg = gen.make_logits(lspec, B)
+        i, w = wd.route(torch.from_numpy(lg).cuda(), spec.K)
+        ids.append(i); ws.append(w); logits.append(lg)
+    x0 = torch.from_numpy(gen.make_tokens(spec, B).x.view(np.int16)).cuda().view(torch.bfloat16)
+    xs = [x0] + [torch.empty_like(x0) for _ in range(LAYERS)]
+    act = torch.empty((B, spec.K, spec.I), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        for l in range(LAYERS):
+            wd.gate_up(xs[l], ids[l], dev[0], dev[1], act=act)
+            wd.down(act, ids[l], ws[l], dev[2], dev[3], out=xs[l + 1])
+
+    run()
+    torch.cuda.synchronize()
+    eager = [bits_of(x) for x in xs]
+    return dict(spec=spec, B=B, L=L, dev=dev, ids=ids, ws=ws, logits=logits, xs=xs, run=run, eager=eager)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2, 5])
+def test_stack_layer_local_parity(stack, layer):
+    L, spec = stack["L"], stack["spec"]
+    ids_o, w_o = oracle.route(stack["logits"][layer], spec.K)
+    assert np.array_equal(stack["ids"][layer].cpu().numpy(), ids_o)
+    x_in = stack["eager"][layer]
+    y64, _ = oracle.moe_decode(x_in, ids_o, stack["ws"][layer].cpu().numpy(), L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
+    out = stack["eager"][layer + 1]
+    log(f"[stack] layer {layer}: max|y| {np.abs(y64).max():.3e}")
+    if np.abs(y64).max() == 0.0:
+        assert (out & 0x7FFF == 0).all()              # an all-zero input stays exactly zero
+        return
+    assert_output_parity(out, y64, f"stack layer {layer}", unit_scale=False, slack=2e-4)
+
+
+def test_stack_last_layer_on_fresh_input(stack):
+    from moe_decode_gate_amd import binding as wd
+    L, spec, B = stack["L"], stack["spec"], stack["B"]
+    t = gen.make_tokens(spec, B, step=47)
+    x = torch.from_numpy(t.x.view(np.int16)).cuda().view(torch.bfloat16)
+    l = LAYERS - 1
+    out = wd.moe_decode(x, stack["ids"][l], stack["ws"][l], *stack["dev"])
+    torch.cuda.synchronize()
+    ids_o, _ = oracle.route(stack["logits"][l], spec.K)
+    y64, _ = oracle.moe_decode(t.x, ids_o, stack["ws"][l].cpu().numpy(), L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
+    assert_output_parity(bits_of(out), y64, "stack last layer, fresh x", unit_scale=False, slack=2e-4)
+
+
+def test_stack_graph_replays_match_eager(stack):
+    """Capture all 48 layers in one HIP graph; every replay (with eager work
+    and synchronisation in between) reproduces the eager chain bit for bit."""
+    run, xs, eager = stack["run"], stack["xs"], stack["eager"]
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in xs[1:]:
+            x.fill_(float("nan"))                    # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in (1, 2, 3, 24, LAYERS):
+            assert np.array_equal(bits_of(xs[l]), eager[l]), (rep, l)
