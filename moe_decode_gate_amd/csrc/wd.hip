@@ -50,30 +50,33 @@ int check_dims(int B, int K, int E, int H, int I) {
 
 // Resolve a launch configuration: fill unset fields with the defaults for
 // this batch size, then validate.  Defaults come from sweeps of every
-// configuration on MI355X at the 128-expert / top-8 / H 2048 / I 768 layer:
-//   B < 8  (latency-bound, no row is read twice): one row per wave, 64 lanes
-//          per row, BF16-pair dot products, non-temporal weight loads;
-//   B >= 8 (tokens share experts): row-block-major order with XCD-contiguous
-//          numbering, so the tokens that share an expert row read it from the
-//          same L2 while it is resident; gate/up with 32 lanes per row and 4
-//          rows per lane group (8 rows per wave), down with 8 rows per wave.
+// configuration on MI355X at the 128-expert / top-8 / H 2048 / I 768 layer
+// for B in {1, 2, 4, 8, 16, 32, 64}:
+//   gate/up, B <= 4: one row per 64-lane wave, BF16-pair dot products,
+//          non-temporal weight loads (no row is read twice), hardware order;
+//   gate/up, B >= 5: 32 lanes per row, 4 rows per lane group (8 per wave),
+//          row-block-major order with XCD-contiguous numbering, so the tokens
+//          that share an expert row read it from the same L2 while resident;
+//   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
+//   down, B 3..5: 4 rows per wave, FP32 math; B >= 6: 8 rows per wave.
 int resolve(const wd_launch *in, int B, bool down, wd_launch *out) {
     wd_launch c = in ? *in : wd_launch{};
-    const bool batch = B >= 8;
+    const bool batch = down ? B >= 3 : B >= 5;
     if (c.form == 0) c.form = 1;
-    if (c.rows_per_wave == 0) c.rows_per_wave = !batch ? 1 : down ? 8 : c.form == 2 ? 2 : 4;
-    if (c.waves_per_block == 0) c.waves_per_block = down ? (batch ? 1 : 2) : (batch ? 4 : 1);
+    if (c.rows_per_wave == 0)
+        c.rows_per_wave = !batch ? 1 : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
+    if (c.waves_per_block == 0) c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch ? 4 : 1);
     if (c.order == 0) c.order = 1;
     if (c.xcd_remap == 0) c.xcd_remap = (!down && !batch) ? 2 : 1;
     if (c.math == 0) c.math = (down && batch) ? wd::kMathF32 : wd::kMathDot2;
-    if (c.lanes_per_row == 0)
-        c.lanes_per_row = (!down && batch && c.form == 1 && c.math == wd::kMathDot2 && c.weight_loads != 2) ? 32 : 64;
     if (c.weight_loads == 0) {
         // non-temporal where no other wave re-reads the rows and the variant is compiled
         const bool nt_ok = c.math == wd::kMathDot2 && c.form == 1 &&
-                           (down ? c.rows_per_wave == 1 : c.lanes_per_row == 64);
+                           (down ? c.rows_per_wave == 1 : (c.lanes_per_row == 0 || c.lanes_per_row == 64));
         c.weight_loads = (!batch && nt_ok) ? 2 : 1;
     }
+    if (c.lanes_per_row == 0)
+        c.lanes_per_row = (!down && batch && c.form == 1 && c.math == wd::kMathDot2 && c.weight_loads != 2) ? 32 : 64;
     if (c.rows_per_wave != 1 && c.rows_per_wave != 2 && c.rows_per_wave != 4 && c.rows_per_wave != 8)
         return WD_ERR_UNSUPPORTED;
     if (c.waves_per_block < 1 || c.waves_per_block > 4) return WD_ERR_UNSUPPORTED;
