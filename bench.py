@@ -269,6 +269,25 @@ def sampled_parity(oracle, L, work: Workload, steps_to_check):
     return cos_min, err_max
 
 
+def accuracy(oracle, L, work: Workload, steps_to_check):
+    """Errors of the GPU output and of the conventional path's numerics (x and
+    the intermediate rounded through MXFP8, per-expert outputs in BF16)
+    against the FP64 layer with unrounded activations."""
+    e_wd, e_cv, ref_sq, m_wd, m_cv = 0.0, 0.0, 0.0, 0.0, 0.0
+    for s in steps_to_check:
+        args = (work.host_x[s], work.host_ids[s], work.host_w[s], L.wgu, L.sgu, L.wd, L.sd)
+        gt = oracle.moe_decode_exact(*args)
+        cv = oracle.moe_decode_conventional(*args)
+        got = work.out[s].float().cpu().numpy().astype(np.float64)
+        e_wd += float(((got - gt) ** 2).sum()); e_cv += float(((cv - gt) ** 2).sum())
+        ref_sq += float((gt ** 2).sum())
+        m_wd += float(np.abs(got - gt).mean()); m_cv += float(np.abs(cv - gt).mean())
+    rel_wd, rel_cv = (e_wd / ref_sq) ** 0.5, (e_cv / ref_sq) ** 0.5
+    return dict(rel_l2_warp_decode_gpu=rel_wd, rel_l2_conventional=rel_cv, rel_l2_ratio=rel_cv / rel_wd,
+                mean_abs_ratio=m_cv / m_wd, steps=len(steps_to_check),
+                reference="FP64 layer, exact MXFP8 weights, unrounded intermediate and output")
+
+
 def cpu_baseline(oracle, L, gen, B, seconds=12.0):
     """The oracle as it stands, on every host core, over fresh seeded batches
     of the same workload until about `seconds` of CPU work have run."""
@@ -333,7 +352,8 @@ def main():
         r32 = measure(torch, wd, w32, steps, warmup)
         cos32, err32 = sampled_parity(oracle, L, w32, [0, steps - 1])
         r32.update(parity_cos_min=cos32, parity_max_abs_err=err32,
-                   frac_of_measured_read_peak=r32["layer_GBps_graph"] / peak)
+                   frac_of_measured_read_peak=r32["layer_GBps_graph"] / peak,
+                   accuracy=accuracy(oracle, L, w32, [0, steps - 1]))
         eprint(f"[bench] B=32: {json.dumps(r32)}")
         del w32
         torch.cuda.empty_cache()

@@ -39,6 +39,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -195,6 +196,152 @@ int oracle_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
     int rc = oracle_gate_up(x, ids, wgu, sgu, B, K, E, H, I, act, 0, 0, nthreads);
     if (rc) return rc;
     return oracle_down(act, ids, w, wd, sd, B, K, E, H, I, y, nthreads);
+}
+
+/* ---- accuracy experiment ----------------------------------------------
+
+ * The warp-decode write-ups claim their output is 1.4x closer to a full
+ * FP32 reference than the conventional path's, because the conventional
+ * path rounds BF16 activations to MXFP8 and back (p2 Key claims, section
+ * "Improved accuracy"; the Chinese summary, section 性能与精度 2), and writes
+ * per-expert outputs to a BF16 buffer that a combine step sums (p2, section
+ * "Buffer elimination").  These functions give the reference and the
+ * conventional path's numerics in FP64. */
+
+/* Nearest E4M3 "FN" code of a value already limited to |v| <= 448 (OCP 8-bit
+ * FP: subnormal step 2^-9 below 2^-6, 3 mantissa bits above), ties to even. */
+uint8_t oracle_e4m3_encode(double v) {
+    if (v != v) return 0x7F;
+    uint8_t sign = v < 0 ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a > 448.0) a = 448.0;
+    if (a < ldexp(1.0, -6)) {                       /* subnormal: m * 2^-9, m = 0..8 */
+        double q = a / ldexp(1.0, -9);
+        double m = floor(q);
+        double r = q - m;
+        if (r > 0.5 || (r == 0.5 && fmod(m, 2.0) == 1.0)) m += 1.0;
+        if (m >= 8.0) return sign | 0x08;           /* rounds up to the smallest normal 2^-6 */
+        return sign | (uint8_t)m;
+    }
+    int e;
+    double f = frexp(a, &e);                        /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;                                          /* a = (2f) * 2^e, 2f in [1, 2) */
+    double q = (2.0 * f - 1.0) * 8.0;               /* mantissa in eighths */
+    double m = floor(q);
+    double r = q - m;
+    if (r > 0.5 || (r == 0.5 && fmod(m, 2.0) == 1.0)) m += 1.0;
+    if (m >= 8.0) { m = 0.0; e += 1; }
+    if (e > 8 || (e == 8 && m > 6.0)) return sign | 0x7E;   /* saturate at 448 */
+    return sign | (uint8_t)(((e + 7) << 3) | (int)m);
+}
+
+/* OCP MX quantization of n values (n a multiple of 32): per 32-block the
+ * shared exponent floor(log2 amax) - 8 (E4M3's largest binade), stored biased
+ * by 127 and clamped to [0, 254]; an all-zero block gets byte 0.  Elements
+ * are v / 2^shared, limited to +-448 and rounded to the nearest E4M3. */
+void oracle_mxfp8_quantize(const double *v, long n, uint8_t *codes, uint8_t *scales) {
+    for (long blk = 0; blk < n / 32; ++blk) {
+        const double *p = v + blk * 32;
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(p[i]));
+        int sb = 0;
+        if (amax > 0.0) {
+            int ex;
+            frexp(amax, &ex);
+            sb = (ex - 1) - 8 + 127;
+            if (sb < 0) sb = 0;
+            if (sb > 254) sb = 254;
+        }
+        scales[blk] = (uint8_t)sb;
+        for (int i = 0; i < 32; ++i) codes[blk * 32 + i] = oracle_e4m3_encode(ldexp(p[i], -(sb - 127)));
+    }
+}
+
+/* Reference: the layer in FP64 with the exact MXFP8 weights and the given x,
+ * no rounding of the intermediate or the output. */
+int oracle_moe_decode_exact(const uint16_t *x, const int32_t *ids, const float *w,
+                            const uint8_t *wgu, const uint8_t *sgu, const uint8_t *wd, const uint8_t *sd,
+                            int B, int K, int E, int H, int I, double *y, int nthreads) {
+    int rc = check(ids, B, K, E, H, I);
+    if (rc) return rc;
+    set_threads(nthreads);
+    const long nbh = H / 32, nbi = I / 32;
+#pragma omp parallel for schedule(static)
+    for (long b = 0; b < B; ++b) {
+        for (long h = 0; h < H; ++h) y[b * H + h] = 0.0;
+        for (long k = 0; k < K; ++k) {
+            long e = ids[b * K + k];
+            double wk = (double)w[b * K + k];
+            for (long j = 0; j < I; ++j) {
+                const uint8_t *cg = wgu + (e * 2 * I + j) * (long)H, *cu = wgu + (e * 2 * I + I + j) * (long)H;
+                const uint8_t *sg = sgu + (e * 2 * I + j) * nbh, *su = sgu + (e * 2 * I + I + j) * nbh;
+                double g = 0.0, u = 0.0;
+                for (long h = 0; h < H; ++h) {
+                    double xv = oracle_bf16_value(x[b * H + h]);
+                    g += oracle_dequant(cg[h], sg[h / 32]) * xv;
+                    u += oracle_dequant(cu[h], su[h / 32]) * xv;
+                }
+                double a = oracle_silu(g) * u;
+                for (long h = 0; h < H; ++h)
+                    y[b * H + h] += wk * oracle_dequant(wd[(e * H + h) * (long)I + j], sd[(e * H + h) * nbi + j / 32]) * a;
+            }
+        }
+    }
+    return 0;
+}
+
+/* The conventional path's numerics: x rounded to MXFP8 (per 32 along H)
+ * before the gate/up projection; the intermediate rounded to BF16 and then
+ * to MXFP8 (per 32 along I) before the down projection; each expert's output
+ * rounded to BF16 (the per-expert buffer); the combine sums w_k times those
+ * in FP64 and the result is rounded to BF16.  y receives that BF16 value. */
+int oracle_moe_decode_conventional(const uint16_t *x, const int32_t *ids, const float *w,
+                                   const uint8_t *wgu, const uint8_t *sgu, const uint8_t *wd,
+                                   const uint8_t *sd, int B, int K, int E, int H, int I, double *y,
+                                   int nthreads) {
+    int rc = check(ids, B, K, E, H, I);
+    if (rc) return rc;
+    set_threads(nthreads);
+    const long nbh = H / 32, nbi = I / 32;
+    if (H > 8192 || I > 16384) return -2;
+    int bad_alloc = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad_alloc)
+    for (long b = 0; b < B; ++b) {
+        double *xv = malloc(sizeof(double) * (size_t)(2 * H + 2 * I));
+        uint8_t *xc = malloc((size_t)(H + H / 32 + I + I / 32));
+        if (!xv || !xc) { free(xv); free(xc); bad_alloc = 1; continue; }
+        double *xq = xv + H, *av = xq + H, *aq = av + I;
+        uint8_t *xs = xc + H, *ac = xs + H / 32, *as = ac + I;
+        for (long h = 0; h < H; ++h) xv[h] = oracle_bf16_value(x[b * H + h]);
+        oracle_mxfp8_quantize(xv, H, xc, xs);
+        for (long h = 0; h < H; ++h) xq[h] = oracle_dequant(xc[h], xs[h / 32]);
+        for (long h = 0; h < H; ++h) y[b * H + h] = 0.0;
+        for (long k = 0; k < K; ++k) {
+            long e = ids[b * K + k];
+            for (long j = 0; j < I; ++j) {
+                const uint8_t *cg = wgu + (e * 2 * I + j) * (long)H, *cu = wgu + (e * 2 * I + I + j) * (long)H;
+                const uint8_t *sg = sgu + (e * 2 * I + j) * nbh, *su = sgu + (e * 2 * I + I + j) * nbh;
+                double g = 0.0, u = 0.0;
+                for (long h = 0; h < H; ++h) {
+                    g += oracle_dequant(cg[h], sg[h / 32]) * xq[h];
+                    u += oracle_dequant(cu[h], su[h / 32]) * xq[h];
+                }
+                av[j] = oracle_bf16_value(oracle_bf16_rne(oracle_round_f32(oracle_silu(g) * u)));
+            }
+            oracle_mxfp8_quantize(av, I, ac, as);
+            for (long j = 0; j < I; ++j) aq[j] = oracle_dequant(ac[j], as[j / 32]);
+            for (long h = 0; h < H; ++h) {
+                double o = 0.0;
+                for (long j = 0; j < I; ++j)
+                    o += oracle_dequant(wd[(e * H + h) * (long)I + j], sd[(e * H + h) * nbi + j / 32]) * aq[j];
+                y[b * H + h] += (double)w[b * K + k] * oracle_bf16_value(oracle_bf16_rne(oracle_round_f32(o)));
+            }
+        }
+        for (long h = 0; h < H; ++h) y[b * H + h] = oracle_bf16_value(oracle_bf16_rne(oracle_round_f32(y[b * H + h])));
+        free(xv);
+        free(xc);
+    }
+    return bad_alloc ? -4 : 0;
 }
 
 /* ---- router ------------------------------------------------------------

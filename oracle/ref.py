@@ -48,6 +48,13 @@ def _load():
         L.oracle_moe_decode.restype = i
         L.oracle_moe_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, P, i]
         L.oracle_max_threads.restype = i
+        L.oracle_e4m3_encode.restype = C.c_uint8
+        L.oracle_e4m3_encode.argtypes = [C.c_double]
+        L.oracle_mxfp8_quantize.argtypes = [P, C.c_long, P, P]
+        L.oracle_moe_decode_exact.restype = i
+        L.oracle_moe_decode_exact.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i]
+        L.oracle_moe_decode_conventional.restype = i
+        L.oracle_moe_decode_conventional.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i]
         L.oracle_route.restype = i
         L.oracle_route.argtypes = [P, i, i, i, P, P]
         _lib = L
@@ -153,6 +160,43 @@ def moe_decode(x, ids, w, wgu, sgu, wd, sd, nthreads: int = 0):
     _rc(_load().oracle_moe_decode(_p(x), _p(ids), _p(w), _p(wgu), _p(sgu), _p(wd), _p(sd),
                                   B, K, E, H, I, _p(act), _p(y), nthreads))
     return y, act
+
+
+def e4m3_encode(v: float) -> int:
+    return _load().oracle_e4m3_encode(v)
+
+
+def mxfp8_quantize(v):
+    """(codes uint8, scales uint8) of FP64 values along the last axis (OCP MX rule)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    assert v.shape[-1] % 32 == 0
+    codes = np.empty(v.shape, np.uint8)
+    scales = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    _load().oracle_mxfp8_quantize(_p(v), v.size, _p(codes), _p(scales))
+    return codes, scales
+
+
+def _layer_call(fn, x, ids, w, wgu, sgu, wd, sd, nthreads):
+    x = _c(x, np.uint16); ids = _c(ids, np.int32); w = _c(w, np.float32)
+    wgu = _c(wgu, np.uint8); sgu = _c(sgu, np.uint8); wd = _c(wd, np.uint8); sd = _c(sd, np.uint8)
+    E, I2, H = wgu.shape
+    B, K = ids.shape
+    if H > 8192 or I2 // 2 > 16384:
+        raise ValueError("oracle: H <= 8192 and I <= 16384 for the accuracy functions")
+    y = np.empty((B, H), np.float64)
+    _rc(fn(_p(x), _p(ids), _p(w), _p(wgu), _p(sgu), _p(wd), _p(sd), B, K, E, H, I2 // 2, _p(y), nthreads))
+    return y
+
+
+def moe_decode_exact(x, ids, w, wgu, sgu, wd, sd, nthreads: int = 0):
+    """Reference y[B,H] in FP64 with no rounding of the intermediate or output."""
+    return _layer_call(_load().oracle_moe_decode_exact, x, ids, w, wgu, sgu, wd, sd, nthreads)
+
+
+def moe_decode_conventional(x, ids, w, wgu, sgu, wd, sd, nthreads: int = 0):
+    """y[B,H] (BF16 values) with the conventional path's activation rounding
+    (x and the intermediate through MXFP8, per-expert outputs in BF16)."""
+    return _layer_call(_load().oracle_moe_decode_conventional, x, ids, w, wgu, sgu, wd, sd, nthreads)
 
 
 def route(logits, K: int):

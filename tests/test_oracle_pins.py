@@ -354,3 +354,111 @@ def test_route_agrees_with_generator_softmax_routing():
     ids, w = oracle.route(gen.make_logits(spec, 16), 8)
     assert np.array_equal(ids, t.ids)                 # same draws, FP32 ranking keeps the order
     np.testing.assert_allclose(w, t.w, rtol=1e-6)
+
+
+# ------------------------------------------------- accuracy experiment --
+
+def test_e4m3_encode_matches_torch(rng):
+    # FP32-representable values, so torch's FP32 -> E4M3 conversion sees the same input
+    v = np.concatenate([
+        rng.uniform(-448, 448, 20000), rng.standard_normal(5000) * 0.01,
+        rng.standard_normal(2000) * 2.0 ** -8,                       # subnormal range
+    ]).astype(np.float32)
+    t = oracle.e4m3_table()
+    finite = np.sort(np.unique(t[np.isfinite(t)]))
+    mids = ((finite[1:] + finite[:-1]) / 2).astype(np.float32)     # exact ties
+    v = np.concatenate([v, mids, -mids, finite.astype(np.float32)])
+    ours = np.array([oracle.e4m3_encode(float(a)) for a in v], np.uint8)
+    lib = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # -0 vs +0 encodings of zero agree in value
+    same = (ours == lib) | ((t[ours] == 0) & (t[lib] == 0))
+    assert same.all(), v[~same][:10]
+
+
+def test_mxfp8_quantize_matches_generator(rng):
+    v = (rng.standard_normal((37, 256)) * 10.0 ** rng.integers(-3, 2, (37, 1))).astype(np.float32)
+    v[3, :32] = 0.0                                                  # an all-zero block
+    c1, s1 = oracle.mxfp8_quantize(v.astype(np.float64))
+    c2, s2 = gen.quantize_mxfp8(v)
+    assert np.array_equal(s1, s2)
+    t = oracle.e4m3_table()
+    assert np.array_equal(t[c1], t[c2])
+
+
+def _dense_exact(x, ids, w, L):
+    def deq(codes, scales):
+        v = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+        s = torch.from_numpy(scales).view(torch.float8_e8m0fnu).to(torch.float64)
+        return v * s.repeat_interleave(32, dim=-1)
+    E, I2, H = L.wgu.shape
+    I = I2 // 2
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    y = torch.zeros(ids.shape[0], H, dtype=torch.float64)
+    for b in range(ids.shape[0]):
+        for k in range(ids.shape[1]):
+            e = int(ids[b, k])
+            gu, dn = deq(L.wgu[e], L.sgu[e]), deq(L.wd[e], L.sd[e])
+            a = torch.nn.functional.silu(gu[:I] @ xf[b]) * (gu[I:] @ xf[b])
+            y[b] += float(w[b, k]) * (dn @ a)
+    return y.numpy()
+
+
+def test_exact_reference_matches_dense_torch():
+    spec, L = _tiny_layer(16, 4, 256, 96, seed=71, std=0.1)
+    t = gen.make_tokens(spec, 3)
+    y = oracle.moe_decode_exact(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    np.testing.assert_allclose(y, _dense_exact(t.x, t.ids, t.w, L), rtol=1e-12, atol=1e-15)
+
+
+def test_conventional_numerics_match_torch_composition():
+    """The conventional path rebuilt from library routines: torch's FP8 and
+    BF16 conversions (via the generator's quantizer) and float64 matmuls."""
+    spec, L = _tiny_layer(16, 4, 256, 96, seed=72, std=0.1)
+    t = gen.make_tokens(spec, 3)
+    y = oracle.moe_decode_conventional(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+
+    def deq(codes, scales):
+        v = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+        s = torch.from_numpy(scales).view(torch.float8_e8m0fnu).to(torch.float64)
+        return v * s.repeat_interleave(32, dim=-1)
+
+    def bf16(a):
+        return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    I = spec.I
+    xf = torch.from_numpy(t.x.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    xq = deq(*gen.quantize_mxfp8(xf))
+    ref = torch.zeros(3, spec.H, dtype=torch.float64)
+    for b in range(3):
+        for k in range(spec.K):
+            e = int(t.ids[b, k])
+            gu, dn = deq(L.wgu[e], L.sgu[e]), deq(L.wd[e], L.sd[e])
+            a = bf16(torch.nn.functional.silu(gu[:I] @ xq[b]) * (gu[I:] @ xq[b]))
+            aq = deq(*gen.quantize_mxfp8(a.to(torch.float32).numpy()))
+            ref[b] += float(t.w[b, k]) * bf16(dn @ aq)
+    ref = bf16(ref).numpy()
+    # BF16 decisions taken on sums in a different order: allow one-ulp flips, mostly exact
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert (np.abs(y - ref) <= ulp * 1.01).all()
+    assert (y == ref).mean() > 0.97
+
+
+def test_conventional_equals_plain_when_activations_are_mxfp8_exact():
+    """If x and every intermediate are already MXFP8 values and the expert
+    outputs are BF16-exact, the conventional path's roundings are identities:
+    the fingerprint layer (integer activations) gives the closed form."""
+    E, K, H, I = 6, 3, 32, 32
+    wgu = np.zeros((E, 2 * I, H), np.uint8); sgu = np.full((E, 2 * I, 1), 127, np.uint8)
+    wgu[:, :I, :] = 0x40
+    for e in range(E):
+        wgu[e, I:, 0] = [0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C][e]
+    wd = np.zeros((E, H, I), np.uint8); sd = np.full((E, H, 1), 127, np.uint8)
+    for h in range(H):
+        wd[:, h, h % I] = 0x38
+    x = np.full((2, H), 0x3F80, np.uint16)
+    ids = np.array([[0, 3, 5], [2, 1, 4]], np.int32)
+    w = np.array([[0.5, 0.25, 0.125], [0.5, 0.25, 0.25]], np.float32)
+    yc = oracle.moe_decode_conventional(x, ids, w, wgu, sgu, wd, sd)
+    ye = oracle.moe_decode_exact(x, ids, w, wgu, sgu, wd, sd)
+    expect = np.array([sum(float(w[b, k]) * 64 * (ids[b, k] + 1) for k in range(K)) for b in range(2)])
+    np.testing.assert_array_equal(yc, np.repeat(expect[:, None], H, axis=1))
+    np.testing.assert_allclose(ye, yc, rtol=1e-14)
