@@ -223,6 +223,91 @@ def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64)
                 note="distinct weight copies per layer, per-layer routing, chained activations, one HIP graph")
 
 
+def measure_comparison(torch, wd, gen, L, batches=(1, 2, 4, 8, 16, 32, 64), steps=40, copies=16):
+    """Warp decode against the expert-centric path on the same inputs: for each
+    batch size, `steps` layer steps (fresh routing and x per step, weight copies
+    cycled so that consecutive steps do not hit the same cached weights)
+    captured in one HIP graph per path and replayed; plus the expert-centric
+    stages' own kernel durations from HIP events."""
+    spec = L.spec
+    base = [torch.from_numpy(a).to("cuda") for a in (L.wgu, L.sgu, L.wd, L.sd)]
+    cps = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    stage_names = ("align", "gather", "gate_up", "down", "combine")
+    out = []
+    for B in batches:
+        xs, ids, ws = [], [], []
+        for s in range(steps):
+            t = gen.make_tokens(gen.LayerSpec(E=spec.E, K=spec.K, H=spec.H, I=spec.I, seed=spec.seed + 7), B, step=s)
+            xs.append(torch.from_numpy(t.x.view(np.int16)).to("cuda").view(torch.bfloat16))
+            ids.append(torch.from_numpy(t.ids).to("cuda")); ws.append(torch.from_numpy(t.w).to("cuda"))
+        act = torch.empty((B, spec.K, spec.I), dtype=torch.bfloat16, device="cuda")
+        y_wd = torch.empty((steps, B, spec.H), dtype=torch.bfloat16, device="cuda")
+        y_ec = torch.empty_like(y_wd)
+        wsp = torch.empty(wd.ec_workspace_bytes(B, spec.K, spec.E, spec.H, spec.I), dtype=torch.uint8, device="cuda")
+
+        def run_wd(s, stream=None):
+            c = cps[s % copies]
+            wd.gate_up(xs[s], ids[s], c[0], c[1], act=act, stream=stream)
+            wd.down(act, ids[s], ws[s], c[2], c[3], out=y_wd[s], stream=stream)
+
+        def run_ec(s, stream=None, cfg=None):
+            c = cps[s % copies]
+            wd.ec_moe_decode(xs[s], ids[s], ws[s], c[0], c[1], c[2], c[3], out=y_ec[s], workspace=wsp, cfg=cfg,
+                             stream=stream)
+
+        res = dict(B=B)
+        for name, fn in (("warp_decode", run_wd), ("expert_centric", run_ec)):
+            for s in range(steps):
+                fn(s)                                 # eager pass: warm-up and device checks
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    for s in range(steps):
+                        fn(s, stream=cap)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            res[f"{name}_us_per_step"] = (time.perf_counter() - t0) * 1e6 / steps
+            del g
+        # stage kernel durations of the expert-centric path
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
+        for row in evs:
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        wd.gpu_sleep(20000)
+        for s in range(steps):
+            cfg = wd.ECLaunch()
+            for i in range(5):
+                cfg.start_event[i] = evs[s][2 * i].cuda_event
+                cfg.stop_event[i] = evs[s][2 * i + 1].cuda_event
+            run_ec(s, cfg=cfg)
+        torch.cuda.synchronize()
+        res["expert_centric_stage_us"] = {
+            n: float(np.mean([evs[s][2 * i].elapsed_time(evs[s][2 * i + 1]) for s in range(steps)]) * 1e3)
+            for i, n in enumerate(stage_names)}
+        res["speedup_warp_decode"] = res["expert_centric_us_per_step"] / res["warp_decode_us_per_step"]
+        # both paths computed the same layer: their outputs agree to the conventional path's rounding
+        a, b = y_wd.float(), y_ec.float()
+        res["outputs_cos"] = float((a * b).sum() / (a.norm() * b.norm()))
+        eprint(f"[bench] compare B={B}: {json.dumps(res)}")
+        out.append(res)
+        del xs, ids, ws, act, y_wd, y_ec, wsp
+    del cps, base
+    torch.cuda.empty_cache()
+    faster = [r["B"] for r in out if r["speedup_warp_decode"] < 1.0]
+    return dict(per_B=out, steps=steps, weight_copies=copies,
+                crossover_B=min(faster) if faster else None,
+                note="both paths graph-replayed on the same inputs; speedup = expert-centric time / warp-decode "
+                     "time; crossover_B = smallest measured B where the expert-centric path is faster")
+
+
 def hbm_read_peak(torch, wd, nbytes=4 << 30, reps=5):
     """Best contiguous-read bandwidth over launch shapes (GB/s), and the copy
     bandwidth of 1 GiB (read + write bytes / time)."""
@@ -313,6 +398,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-b32", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-compare", action="store_true", help="skip the expert-centric comparison")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs the layer "
@@ -360,6 +446,8 @@ def main():
 
     stack = None if args.no_stack else measure_stack(torch, wd, gen, L, peak)
 
+    compare = None if args.no_compare else measure_comparison(torch, wd, gen, L)
+
     cpu = None if args.no_cpu else cpu_baseline(oracle, L, gen, 1)
 
     achieved = r1["gate_up_GBps"]
@@ -382,6 +470,7 @@ def main():
         "b1": r1,
         "b32": r32,
         "stack48": stack,
+        "vs_expert_centric": compare,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }

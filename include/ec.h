@@ -1,0 +1,129 @@
+/* Expert-centric MoE decode layer: the conventional path that warp decode is
+ * measured against, built for MI355X (gfx950) with MX-scaled FP8 matrix cores.
+ *
+ * The write-ups describe this path as a pipeline that routes and dispatches
+ * tokens to experts, pads each expert's token list, gathers activations into
+ * an expert-major layout, runs a batched GEMM per expert, scatters the
+ * per-expert outputs back to token order and combines them with a weighted
+ * reduction ("Better MoE model inference with warp decode", Key claims,
+ * section "The conventional MoE path", and Method; the Chinese summary,
+ * section 传统路径的困境).  Its numerics follow the same pages' account of the
+ * conventional path (Key claims, section "Improved accuracy"; section
+ * "Buffer elimination"): activations go BF16 -> MXFP8 before each projection,
+ * and every expert's output is rounded to a BF16 buffer before the combine.
+ *
+ * Stages, one kernel each, all on the caller's stream:
+ *   1 align:    count tokens per expert, pad each expert's list to a multiple
+ *               of 16 rows (the M of the 16x16x128 MX matrix instruction),
+ *               write the expert of every 16-row tile and the (token, slot)
+ *               pair of every row (-1 for padding);
+ *   2 gather:   copy each row's token x into an expert-major buffer, rounded
+ *               to MXFP8 (E4M3 codes, one E8M0 scale per 32 along H);
+ *   3 gate/up:  per tile, [16 x H] x [H x 2I] on the matrix cores (MXFP8 x
+ *               MXFP8 -> FP32), then a = SiLU(g) * u rounded to BF16;
+ *   4 down:     per tile, a rounded to MXFP8 (per 32 along I), [16 x I] x
+ *               [I x H] on the matrix cores, each row's output rounded to BF16
+ *               and written to that (token, slot)'s row (the scatter);
+ *   5 combine:  y[b] = BF16( sum_k w[b,k] * o[b,k] ), FP32, slots in order.
+ *
+ * Weight layouts are those of include/wd.h.  Rounding rules: MXFP8 uses the
+ * OCP MX scale rule (shared exponent floor(log2 amax) - 8, stored biased by
+ * 127 and clamped to [0, 254]; an all-zero block gets byte 0) and E4M3
+ * round-to-nearest-even saturating at +-448; BF16 is round-to-nearest-even.
+ *
+ * Entry points return the status codes of include/wd.h.  Every argument check
+ * runs before the first HIP call.  Calls enqueue work and return without
+ * synchronising, allocating or freeing. */
+#ifndef EC_H
+#define EC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "wd.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Regions of the workspace, in order; ec_workspace_layout returns the byte
+ * offset of each, plus the total in EC_WS_TOTAL.  Every region starts on a
+ * 256-byte boundary.  T is the tile bound floor((B*K + 15*min(E, B*K)) / 16),
+ * S = 16*T rows.
+ *   EC_WS_HEADER       int32[64]: [0] = tiles in use (written by stage 1)
+ *   EC_WS_TILE_EXPERT  int32[T]: expert of each tile, tiles in expert order
+ *   EC_WS_ROW_PAIR     int32[S]: b*K + k of each row, -1 for a padding row
+ *   EC_WS_XQ           uint8[S][H]: gathered x, E4M3 codes
+ *   EC_WS_XS           uint8[S][H/32]: gathered x, E8M0 scales
+ *   EC_WS_ACT          uint16[S][I]: BF16 bits of SiLU(g) * u
+ *   EC_WS_AQ           uint8[S][I] codes then uint8[S][I/32] scales: the MXFP8
+ *                      intermediate, written only when ec_launch.keep_intermediate
+ *   EC_WS_OUT_PAIR     uint16[B*K][H]: BF16 bits of each (token, slot)'s expert output
+ * The order of the rows of one expert inside its tiles is not fixed (stage 1
+ * places them with atomic counters); nothing downstream depends on it. */
+enum {
+    EC_WS_HEADER = 0, EC_WS_TILE_EXPERT, EC_WS_ROW_PAIR, EC_WS_XQ, EC_WS_XS, EC_WS_ACT, EC_WS_AQ,
+    EC_WS_OUT_PAIR, EC_WS_TOTAL, EC_WS_REGIONS
+};
+
+/* Workspace bytes for a call with these sizes; 0 for invalid or unsupported
+ * sizes and for B = 0. */
+size_t ec_workspace_bytes(int B, int K, int E, int H, int I);
+
+/* Writes the EC_WS_REGIONS byte offsets described above to offsets[].
+ * Returns WD_OK, WD_ERR_NULL, WD_ERR_DIMS or WD_ERR_UNSUPPORTED. */
+int ec_workspace_layout(int B, int K, int E, int H, int I, size_t *offsets);
+
+/* Optional launch settings.  last_stage: run stages 1..last_stage (0 = all
+ * five; out is not touched and may be NULL when last_stage < 5).
+ * keep_intermediate: nonzero makes stage 4 also write the MXFP8 intermediate
+ * to EC_WS_AQ.  start_event[i] / stop_event[i] (hipEvent_t, may be NULL) are
+ * recorded around stage i+1's kernel. */
+typedef struct ec_launch {
+    int last_stage;
+    int keep_intermediate;
+    void *start_event[5];
+    void *stop_event[5];
+} ec_launch;
+
+/* The whole layer, expert-centric.
+ * x    [B][H] BF16 bits; ids [B][K] int32 experts; w [B][K] float routing weights.
+ * wgu  [E][2I][H] E4M3 codes (gate rows 0..I-1, up rows I..2I-1); sgu [E][2I][H/32] E8M0.
+ * wd   [E][H][I] E4M3 codes; sd [E][H][I/32] E8M0.
+ * workspace: device memory of at least ec_workspace_bytes(B, K, E, H, I) bytes,
+ *      256-byte aligned, owned by the caller, not shared with a concurrent call.
+ * out  [B][H] BF16 bits.
+ * Sizes: H, I multiples of 32, 1 <= K <= E <= 1024, B*K <= 4096, H <= 8192,
+ * I <= 2048 (else WD_ERR_UNSUPPORTED).  B = 0 returns WD_OK and launches
+ * nothing.  All pointers are device pointers: x, ids, w, out and the E4M3
+ * arrays 16-byte aligned.  A token with an expert id outside [0, E) gets a
+ * row of NaN; its other slots are not computed. */
+int ec_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
+                  const uint8_t *wgu, const uint8_t *sgu, const uint8_t *wd, const uint8_t *sd,
+                  void *workspace, size_t workspace_bytes, uint16_t *out,
+                  int B, int K, int E, int H, int I, void *stream);
+
+/* ec_moe_decode with launch settings (cfg may be NULL). */
+int ec_moe_decode_ex(const uint16_t *x, const int32_t *ids, const float *w,
+                     const uint8_t *wgu, const uint8_t *sgu, const uint8_t *wd, const uint8_t *sd,
+                     void *workspace, size_t workspace_bytes, uint16_t *out,
+                     int B, int K, int E, int H, int I, const ec_launch *cfg, void *stream);
+
+/* Diagnostic: n independent products C_i = A_i B_i^T on the MX-scaled FP8
+ * matrix instruction the two projections use, so that its arithmetic can be
+ * measured against exact values.  a, b: [n][16][128] E4M3 codes (16-byte
+ * aligned); sa, sb: [n][16][4] E8M0 bytes, one per row per 32 along K;
+ * out: [n][16][16] FP32, out[i][m][c] = sum_k A_i[m][k] B_i[c][k] with each
+ * element times its block scale.  0 <= n <= 65536 (else WD_ERR_UNSUPPORTED).
+ * Measured on MI355X: the instruction sums the 128 products in groups of 8
+ * consecutive k, each group in fixed point truncated 13 bits below the
+ * group's largest exponent sum (the sum of the two operands' exponents),
+ * and adds the group sums in FP32. */
+int ec_mma_probe(const uint8_t *a, const uint8_t *b, const uint8_t *sa, const uint8_t *sb, float *out, int n,
+                 void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EC_H */

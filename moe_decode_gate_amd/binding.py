@@ -1,4 +1,4 @@
-"""Python binding of libwd.so (the C ABI in include/wd.h).
+"""Python binding of libwd.so (the C ABI in include/wd.h and include/ec.h).
 
 Argument marshalling only: the functions check dtypes, devices, contiguity
 and shapes of torch tensors, then pass raw device pointers, sizes and the
@@ -18,6 +18,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libwd.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "wd.h")
+EC_HEADER = os.path.join(os.path.dirname(_PKG), "include", "ec.h")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
@@ -46,6 +47,16 @@ class Launch(C.Structure):
                 ("lanes_per_row", C.c_int), ("form", C.c_int), ("weight_loads", C.c_int)]
 
 
+class ECLaunch(C.Structure):
+    """Expert-centric launch settings (ec_launch): last_stage (0 = all five),
+    keep_intermediate, and per-stage start/stop hipEvent_t handles."""
+    _fields_ = [("last_stage", C.c_int), ("keep_intermediate", C.c_int),
+                ("start_event", C.c_void_p * 5), ("stop_event", C.c_void_p * 5)]
+
+
+# Workspace regions of the expert-centric path (enum in include/ec.h).
+EC_WS = ("header", "tile_expert", "row_pair", "xq", "xs", "act", "aq", "out_pair", "total")
+
 _P, _I, _S = C.c_void_p, C.c_int, C.c_size_t
 _sig = {
     "wd_gate_up": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -61,16 +72,25 @@ _sig = {
     "wd_stream_blocks": (_I, []),
     "wd_stream_copy": (_I, [_P, _P, _S, _I, _P]),
     "wd_gpu_sleep": (_I, [_I, _P]),
+    "ec_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "ec_workspace_layout": (_I, [_I, _I, _I, _I, _I, C.POINTER(C.c_size_t)]),
+    "ec_moe_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _I, _I, _I, _I, _I, _P]),
+    "ec_mma_probe": (_I, [_P, _P, _P, _P, _P, _I, _P]),
+    "ec_moe_decode_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _I, _I, _I, _I, _I,
+                              C.POINTER(ECLaunch), _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
     _f.restype, _f.argtypes = _res, _args
 
 
-def header_functions(path: str = HEADER):
-    """Names of the functions include/wd.h declares."""
-    text = open(path).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(wd_[a-z_0-9]+)\s*\(", text, re.M)))
+def header_functions(paths=(HEADER, EC_HEADER)):
+    """Names of the functions include/wd.h and include/ec.h declare."""
+    names = set()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        text = open(path).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*((?:wd|ec)_[a-z_0-9]+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def _check(rc: int, where: str):
@@ -222,6 +242,53 @@ def stream_copy(dst: torch.Tensor, src: torch.Tensor, blocks: int = 0, stream=No
 
 def gpu_sleep(units: int, stream=None):
     _check(_lib.wd_gpu_sleep(units, _stream(stream)), "wd_gpu_sleep")
+
+
+def ec_workspace_bytes(B: int, K: int, E: int, H: int, I: int) -> int:
+    return _lib.ec_workspace_bytes(B, K, E, H, I)
+
+
+def ec_workspace_layout(B: int, K: int, E: int, H: int, I: int) -> dict:
+    """Byte offsets of the expert-centric workspace regions (EC_WS names)."""
+    off = (C.c_size_t * len(EC_WS))()
+    _check(_lib.ec_workspace_layout(B, K, E, H, I, off), "ec_workspace_layout")
+    return dict(zip(EC_WS, list(off)))
+
+
+def ec_moe_decode(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, out=None, workspace=None, cfg=None, stream=None):
+    """The expert-centric layer (align, gather, gate/up, down, combine); returns out[B,H] bf16.
+    cfg: an ECLaunch (or None).  With cfg.last_stage in 1..4 out is left untouched."""
+    E, H, I = _dims(w_gu)
+    B, K = topk_ids.shape
+    _dev(x, "x", _BF16, (B, H)); _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,), (B, K))
+    _dev(w_gu, "w_gu", _U8, (E, 2 * I, H)); _dev(s_gu, "s_gu", _U8, (E, 2 * I, H // 32))
+    _dev(w_d, "w_d", _U8, (E, H, I)); _dev(s_d, "s_d", _U8, (E, H, I // 32))
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", _BF16, (B, H))
+    need = ec_workspace_bytes(B, K, E, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", (torch.uint8,))
+    args = (_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gu), _ptr(s_gu), _ptr(w_d), _ptr(s_d),
+            _ptr(workspace), workspace.numel(), _ptr(out), B, K, E, H, I)
+    if cfg is None:
+        rc = _lib.ec_moe_decode(*args, _stream(stream))
+    else:
+        rc = _lib.ec_moe_decode_ex(*args, C.byref(cfg), _stream(stream))
+    _check(rc, "ec_moe_decode")
+    return out
+
+
+def ec_mma_probe(a, b, sa, sb, stream=None) -> torch.Tensor:
+    """out[n,16,16] fp32 from one MX matrix instruction per block (see ec.h)."""
+    n = a.shape[0]
+    _dev(a, "a", _U8, (n, 16, 128)); _dev(b, "b", _U8, (n, 16, 128))
+    _dev(sa, "sa", _U8, (n, 16, 4)); _dev(sb, "sb", _U8, (n, 16, 4))
+    out = torch.empty((n, 16, 16), dtype=torch.float32, device=a.device)
+    _check(_lib.ec_mma_probe(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), _ptr(out), n, _stream(stream)), "ec_mma_probe")
+    return out
 
 
 # Raw entry points for callers that manage pointers themselves (tests, bench).

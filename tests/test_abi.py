@@ -123,3 +123,57 @@ def test_chunk_to_slot_division_is_exact():
         K_max = 16384 // (16 * nci)
         for c in range(min(1024, K_max * nci)):
             assert (c * magic) >> 22 == c // nci
+
+
+# ---- expert-centric path (include/ec.h) -----------------------------------
+
+def ec(ws_bytes=1 << 30, ws=A, cfg=None, **kw):
+    d = dict(x=A, ids=A, tw=A, wgu=A, sgu=A, wd=A, sd=A, out=A, B=1, K=8, E=128, H=2048, I=768)
+    d.update(kw)
+    args = (d["x"], d["ids"], d["tw"], d["wgu"], d["sgu"], d["wd"], d["sd"], ws, ws_bytes, d["out"],
+            d["B"], d["K"], d["E"], d["H"], d["I"])
+    if cfg is None:
+        return lib.ec_moe_decode(*args, None)
+    return lib.ec_moe_decode_ex(*args, C.byref(cfg), None)
+
+
+def test_ec_workspace_layout():
+    for B, K, E, H, I in [(1, 8, 128, 2048, 768), (32, 8, 128, 2048, 768), (64, 8, 128, 4096, 1536),
+                          (7, 4, 16, 160, 96), (512, 8, 128, 2048, 768)]:
+        lay = wd.ec_workspace_layout(B, K, E, H, I)
+        offs = [lay[n] for n in wd.EC_WS]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert lay["total"] == lib.ec_workspace_bytes(B, K, E, H, I)
+        pairs = B * K
+        tiles = (pairs + 15 * min(E, pairs)) // 16
+        rows = 16 * tiles
+        assert lay["row_pair"] - lay["tile_expert"] >= 4 * tiles
+        assert lay["xs"] - lay["xq"] >= rows * H
+        assert lay["aq"] - lay["act"] >= 2 * rows * I
+        assert lay["out_pair"] - lay["aq"] >= rows * I + rows * I // 32
+        assert lay["total"] - lay["out_pair"] >= 2 * pairs * H
+
+
+def test_ec_tile_bound_is_tight_enough():
+    # sum over experts of ceil(count/16) never exceeds the bound, whatever the routing
+    import numpy as np
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        E = int(rng.integers(1, 300)); pairs = int(rng.integers(1, 4097))
+        counts = np.bincount(rng.integers(0, E, pairs), minlength=E)
+        assert int(((counts + 15) // 16).sum()) <= (pairs + 15 * min(E, pairs)) // 16
+
+
+def test_ec_rejects_bad_arguments():
+    assert lib.ec_workspace_bytes(0, 8, 128, 2048, 768) == 0
+    assert lib.ec_workspace_bytes(1, 8, 128, 100, 768) == 0
+    assert ec(H=100) == -2 and ec(I=48) == -2 and ec(K=0) == -2 and ec(K=9, E=8) == -2 and ec(B=-1) == -2
+    assert ec(E=1025) == -7 and ec(H=8192 + 32) == -7 and ec(I=2048 + 32) == -7 and ec(B=513) == -7
+    assert ec(x=None) == -1 and ec(ws=None) == -1 and ec(sd=None) == -1 and ec(out=None) == -1
+    assert ec(x=A + 8) == -3 and ec(ws=A + 16) == -3 and ec(out=A + 2) == -3
+    assert ec(ws_bytes=lib.ec_workspace_bytes(1, 8, 128, 2048, 768) - 1) == -4
+    assert ec(cfg=wd.ECLaunch(last_stage=6)) == -7
+    # out is optional when the last stage run is not the combine
+    assert ec(out=None, cfg=wd.ECLaunch(last_stage=9)) == -7
+    assert ec(B=0, x=None, ids=None, tw=None, out=None, ws=None, ws_bytes=0) == 0
+    assert lib.ec_workspace_layout(1, 8, 128, 2048, 768, None) == -1
