@@ -355,20 +355,30 @@ def sampled_parity(oracle, L, work: Workload, steps_to_check):
 
 
 def accuracy(oracle, L, work: Workload, steps_to_check):
-    """Errors of the GPU output and of the conventional path's numerics (x and
-    the intermediate rounded through MXFP8, per-expert outputs in BF16)
-    against the FP64 layer with unrounded activations."""
-    e_wd, e_cv, ref_sq, m_wd, m_cv = 0.0, 0.0, 0.0, 0.0, 0.0
+    """Errors against the FP64 layer with unrounded activations of: the GPU
+    warp-decode output; the oracle's conventional-path numerics (x and the
+    intermediate rounded through MXFP8, per-expert outputs in BF16); and the
+    GPU expert-centric path, which adds its matrix instruction's arithmetic."""
+    import torch
+    wd = work.wd
+    spec = work.spec
+    ws = torch.empty(wd.ec_workspace_bytes(work.B, spec.K, spec.E, spec.H, spec.I), dtype=torch.uint8, device="cuda")
+    e_wd, e_cv, e_ec, ref_sq, m_wd, m_cv = 0.0, 0.0, 0.0, 0.0, 0.0, 0.0
     for s in steps_to_check:
         args = (work.host_x[s], work.host_ids[s], work.host_w[s], L.wgu, L.sgu, L.wd, L.sd)
         gt = oracle.moe_decode_exact(*args)
         cv = oracle.moe_decode_conventional(*args)
         got = work.out[s].float().cpu().numpy().astype(np.float64)
+        c = work.copies[0]
+        ec = wd.ec_moe_decode(work.x[s], work.ids[s], work.w[s], c[0], c[1], c[2], c[3], workspace=ws)
+        ec = ec.float().cpu().numpy().astype(np.float64)
         e_wd += float(((got - gt) ** 2).sum()); e_cv += float(((cv - gt) ** 2).sum())
+        e_ec += float(((ec - gt) ** 2).sum())
         ref_sq += float((gt ** 2).sum())
         m_wd += float(np.abs(got - gt).mean()); m_cv += float(np.abs(cv - gt).mean())
-    rel_wd, rel_cv = (e_wd / ref_sq) ** 0.5, (e_cv / ref_sq) ** 0.5
+    rel_wd, rel_cv, rel_ec = (e_wd / ref_sq) ** 0.5, (e_cv / ref_sq) ** 0.5, (e_ec / ref_sq) ** 0.5
     return dict(rel_l2_warp_decode_gpu=rel_wd, rel_l2_conventional=rel_cv, rel_l2_ratio=rel_cv / rel_wd,
+                rel_l2_expert_centric_gpu=rel_ec, rel_l2_ratio_gpu_paths=rel_ec / rel_wd,
                 mean_abs_ratio=m_cv / m_wd, steps=len(steps_to_check),
                 reference="FP64 layer, exact MXFP8 weights, unrounded intermediate and output")
 

@@ -20,10 +20,11 @@
  *   2 gather:   copy each row's token x into an expert-major buffer, rounded
  *               to MXFP8 (E4M3 codes, one E8M0 scale per 32 along H);
  *   3 gate/up:  per tile, [16 x H] x [H x 2I] on the matrix cores (MXFP8 x
- *               MXFP8 -> FP32), then a = SiLU(g) * u rounded to BF16;
- *   4 down:     per tile, a rounded to MXFP8 (per 32 along I), [16 x I] x
- *               [I x H] on the matrix cores, each row's output rounded to BF16
- *               and written to that (token, slot)'s row (the scatter);
+ *               MXFP8 -> FP32), then a = SiLU(g) * u rounded to BF16 and
+ *               that rounded to MXFP8 (per 32 along I);
+ *   4 down:     per tile, [16 x I] x [I x H] on the matrix cores, each row's
+ *               output rounded to BF16 and written to that (token, slot)'s
+ *               row (the scatter);
  *   5 combine:  y[b] = BF16( sum_k w[b,k] * o[b,k] ), FP32, slots in order.
  *
  * Weight layouts are those of include/wd.h.  Rounding rules: MXFP8 uses the
@@ -51,13 +52,16 @@ extern "C" {
  * 256-byte boundary.  T is the tile bound floor((B*K + 15*min(E, B*K)) / 16),
  * S = 16*T rows.
  *   EC_WS_HEADER       int32[64]: [0] = tiles in use (written by stage 1)
- *   EC_WS_TILE_EXPERT  int32[T]: expert of each tile, tiles in expert order
- *   EC_WS_ROW_PAIR     int32[S]: b*K + k of each row, -1 for a padding row
+ *   EC_WS_TILE_EXPERT  int32[T]: expert of each tile, tiles in expert order,
+ *                      then -1 for every tile past the ones in use
+ *   EC_WS_ROW_PAIR     int32[S]: b*K + k of each row, -1 for a padding row of
+ *                      a tile in use, -2 for the rows of tiles past those
  *   EC_WS_XQ           uint8[S][H]: gathered x, E4M3 codes
  *   EC_WS_XS           uint8[S][H/32]: gathered x, E8M0 scales
- *   EC_WS_ACT          uint16[S][I]: BF16 bits of SiLU(g) * u
+ *   EC_WS_ACT          uint16[S][I]: BF16 bits of SiLU(g) * u, written only
+ *                      when ec_launch.keep_intermediate is set
  *   EC_WS_AQ           uint8[S][I] codes then uint8[S][I/32] scales: the MXFP8
- *                      intermediate, written only when ec_launch.keep_intermediate
+ *                      intermediate
  *   EC_WS_OUT_PAIR     uint16[B*K][H]: BF16 bits of each (token, slot)'s expert output
  * The order of the rows of one expert inside its tiles is not fixed (stage 1
  * places them with atomic counters); nothing downstream depends on it. */
@@ -76,8 +80,8 @@ int ec_workspace_layout(int B, int K, int E, int H, int I, size_t *offsets);
 
 /* Optional launch settings.  last_stage: run stages 1..last_stage (0 = all
  * five; out is not touched and may be NULL when last_stage < 5).
- * keep_intermediate: nonzero makes stage 4 also write the MXFP8 intermediate
- * to EC_WS_AQ.  start_event[i] / stop_event[i] (hipEvent_t, may be NULL) are
+ * keep_intermediate: nonzero makes stage 3 also write the BF16 intermediate
+ * to EC_WS_ACT.  start_event[i] / stop_event[i] (hipEvent_t, may be NULL) are
  * recorded around stage i+1's kernel. */
 typedef struct ec_launch {
     int last_stage;
@@ -94,7 +98,7 @@ typedef struct ec_launch {
  *      256-byte aligned, owned by the caller, not shared with a concurrent call.
  * out  [B][H] BF16 bits.
  * Sizes: H, I multiples of 32, 1 <= K <= E <= 1024, B*K <= 4096, H <= 8192,
- * I <= 2048 (else WD_ERR_UNSUPPORTED).  B = 0 returns WD_OK and launches
+ * I <= 8192 (else WD_ERR_UNSUPPORTED).  B = 0 returns WD_OK and launches
  * nothing.  All pointers are device pointers: x, ids, w, out and the E4M3
  * arrays 16-byte aligned.  A token with an expert id outside [0, E) gets a
  * row of NaN; its other slots are not computed. */

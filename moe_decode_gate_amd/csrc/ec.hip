@@ -33,10 +33,13 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kTile = 16;          // rows per tile (M of the matrix instruction)
 constexpr int kStepK = 128;        // K per matrix instruction
 constexpr int kBatch = 4;          // K steps whose loads are issued together
-constexpr int kMaxE = 1024, kMaxPairs = 4096, kMaxH = 8192, kMaxI = 2048;
+constexpr int kMaxE = 1024, kMaxPairs = 4096, kMaxH = 8192, kMaxI = 8192;
 constexpr int kAlignThreads = 1024;
-constexpr int kGemmThreads = 256;  // 4 waves
-constexpr int kGuCols = 16;        // gate (and up) columns per gate/up workgroup
+constexpr int kGemmThreads = 256;  // down: 4 waves
+constexpr int kGuWaves = 8;        // gate/up: 8 waves splitting K
+constexpr int kGuThreads = 64 * kGuWaves;
+constexpr int kGuBatch = 1;        // gate/up K steps per wave whose loads are issued together
+constexpr int kGuCols = 32;        // intermediate columns per gate/up workgroup (one MX block)
 constexpr int kDnCols = 64;        // output columns per down workgroup (16 per wave)
 
 // ---- MXFP8 rounding ------------------------------------------------------
@@ -127,9 +130,11 @@ __device__ __forceinline__ Frag load_frag(const uint8_t *codes, const uint8_t *s
 struct AlignArgs {
     const int32_t *ids;
     int32_t *header, *tile_expert, *row_pair;
-    int pairs, E;
+    int pairs, E, max_tiles;
 };
 
+// One workgroup.  Tiles past the ones in use get expert -1 and their rows
+// pair -2, so later stages find the end of the list with the load they make anyway.
 __global__ void __launch_bounds__(kAlignThreads) align_kernel(AlignArgs a) {
     __shared__ int cnt[kMaxE], fill[kMaxE], base[kMaxE];
     __shared__ int wave_tot[kAlignThreads / 64];
@@ -163,6 +168,8 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(AlignArgs a) {
         for (int i = 0; i < tiles; ++i) a.tile_expert[b + i] = t;
         for (int r = cnt[t]; r < tiles * kTile; ++r) a.row_pair[b * kTile + r] = -1;
     }
+    for (int i = total + t; i < a.max_tiles; i += kAlignThreads) a.tile_expert[i] = -1;
+    for (int i = total * kTile + t; i < a.max_tiles * kTile; i += kAlignThreads) a.row_pair[i] = -2;
     if (t == 0) a.header[0] = total;
     __syncthreads();
     for (int p = t; p < a.pairs; p += kAlignThreads) {
@@ -175,7 +182,7 @@ __global__ void __launch_bounds__(kAlignThreads) align_kernel(AlignArgs a) {
 
 struct GatherArgs {
     const uint16_t *x;
-    const int32_t *header, *row_pair;
+    const int32_t *row_pair;
     uint8_t *xq, *xs;
     int K, H, max_rows;
 };
@@ -185,8 +192,9 @@ struct GatherArgs {
 __global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (row >= a.max_rows || row >= a.header[0] * kTile) return;
+    if (row >= a.max_rows) return;
     const int p = a.row_pair[row];
+    if (p == -2) return;                                   // past the tiles in use
     const int nb = a.H / 32;
     uint8_t *q = a.xq + (size_t)row * a.H;
     uint8_t *s = a.xs + (size_t)row * nb;
@@ -205,128 +213,132 @@ __global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
     }
 }
 
-// ---- stage 3: grouped gate/up GEMM + SiLU(g) * u ----------------------------
+// ---- stage 3: grouped gate/up GEMM + SiLU(g) * u + MXFP8 -------------------
 
 struct GateUpArgs {
     const uint8_t *xq, *xs, *w, *ws;   // gathered x; gate/up codes [E][2I][H], scales [E][2I][H/32]
-    const int32_t *header, *tile_expert;
-    uint16_t *act;                      // [rows][I] BF16
+    const int32_t *tile_expert;
+    uint8_t *aq, *as;                   // MXFP8 intermediate [rows][I], [rows][I/32]
+    uint16_t *act;                      // optional BF16 intermediate [rows][I]
     int H, I, nblocks, ncolblk;
 };
 
-// Workgroup = (tile, 16 gate columns + the matching 16 up columns); its four
-// waves split the K steps (wave w takes steps w, w+4, ...) and the partial
-// tiles are summed through LDS in wave order.
-__global__ void __launch_bounds__(kGemmThreads) gate_up_kernel(GateUpArgs a) {
-    __shared__ float part[4][2][4][64];
+// Workgroup = (tile, 32 columns: the gate rows and the up rows of one MX
+// block of the intermediate).  The eight waves split the K steps (wave w takes
+// steps w, w+8, ...); their partial tiles are summed through LDS in wave
+// order, and the epilogue rounds the block to BF16 and then to MXFP8.
+__global__ void __launch_bounds__(kGuThreads) gate_up_kernel(GateUpArgs a) {
+    __shared__ float part[kGuWaves][4][4][64];
     const int lb = wd::xcd_logical(blockIdx.x, a.nblocks);
     const int tile = lb / a.ncolblk, cb = lb % a.ncolblk;
-    if (tile >= a.header[0]) return;
+    const int e = a.tile_expert[tile];
+    if (e < 0) return;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int e = a.tile_expert[tile];
     const int H = a.H, I = a.I, nbh = H / 32;
     const size_t xrow = (size_t)tile * kTile + r;
     const uint8_t *xc = a.xq + xrow * H, *xsr = a.xs + xrow * nbh;
-    const size_t grow = (size_t)e * 2 * I + (size_t)cb * kGuCols + r;
-    const uint8_t *gc = a.w + grow * H, *gs = a.ws + grow * nbh;
-    const uint8_t *uc = gc + (size_t)I * H, *us = gs + (size_t)I * nbh;
-    v4f cg = {0.f, 0.f, 0.f, 0.f}, cu = cg;
-    const int nks = (H + kStepK - 1) / kStepK;
-    for (int s0 = wv; s0 < nks; s0 += 4 * kBatch) {
-        Frag fx[kBatch], fg[kBatch], fu[kBatch];
+    // result tiles: gate columns +0 / +16, up columns +0 / +16 of this block
+    const uint8_t *wc[4], *wsr[4];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int k0 = (s0 + 4 * i) * kStepK;      // past H: all segments read as zero
+    for (int t = 0; t < 4; ++t) {
+        const size_t wrow = (size_t)e * 2 * I + (t >= 2 ? I : 0) + (size_t)cb * kGuCols + 16 * (t & 1) + r;
+        wc[t] = a.w + wrow * H;
+        wsr[t] = a.ws + wrow * nbh;
+    }
+    v4f c[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int nks = (H + kStepK - 1) / kStepK;
+    for (int s0 = wv; s0 < nks; s0 += kGuWaves * kGuBatch) {
+        Frag fx[kGuBatch], fw[kGuBatch][4];
+#pragma unroll
+        for (int i = 0; i < kGuBatch; ++i) {
+            const int k0 = (s0 + kGuWaves * i) * kStepK;   // past H: all segments read as zero
             fx[i] = load_frag(xc, xsr, H, k0, g);
-            fg[i] = load_frag(gc, gs, H, k0, g);
-            fu[i] = load_frag(uc, us, H, k0, g);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) fw[i][t] = load_frag(wc[t], wsr[t], H, k0, g);
         }
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
+        for (int i = 0; i < kGuBatch; ++i) {
             const v8i ax = make_operand(fx[i].lo, fx[i].hi);
-            cg = mfma_mx(ax, make_operand(fg[i].lo, fg[i].hi), cg, fx[i].s, fg[i].s);
-            cu = mfma_mx(ax, make_operand(fu[i].lo, fu[i].hi), cu, fx[i].s, fu[i].s);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                c[t] = mfma_mx(ax, make_operand(fw[i][t].lo, fw[i][t].hi), c[t], fx[i].s, fw[i][t].s);
         }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) { part[wv][0][q][lane] = cg[q]; part[wv][1][q][lane] = cu[q]; }
-    __syncthreads();
-    // thread (q, l) finishes element rows 4*(l/16) + q, column l % 16
-    const int q = threadIdx.x >> 6, l = threadIdx.x & 63;
-    float gs_ = part[0][0][q][l], us_ = part[0][1][q][l];
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int w = 1; w < 4; ++w) { gs_ += part[w][0][q][l]; us_ += part[w][1][q][l]; }
-    const float en = expf(-fabsf(gs_));
-    const float sig = gs_ >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
-    const size_t orow = (size_t)tile * kTile + 4 * (l >> 4) + q;
-    a.act[orow * I + (size_t)cb * kGuCols + (l & 15)] = wd::to_bf16(gs_ * sig * us_);
+        for (int q = 0; q < 4; ++q) part[wv][t][q][lane] = c[t][q];
+    __syncthreads();
+    // thread -> row m, column j of the block; its value sits in result lane
+    // n + 16 * (m / 4), element m % 4, of tile j / 16 (gate) and 2 + j / 16 (up)
+    const int m = threadIdx.x >> 5, j = threadIdx.x & 31;
+    const int nt = j >> 4, l = (j & 15) + 16 * (m >> 2), q = m & 3;
+    float gsum = part[0][nt][q][l], usum = part[0][2 + nt][q][l];
+#pragma unroll
+    for (int w = 1; w < kGuWaves; ++w) { gsum += part[w][nt][q][l]; usum += part[w][2 + nt][q][l]; }
+    const float en = expf(-fabsf(gsum));
+    const float sig = gsum >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
+    const uint16_t ab = wd::to_bf16(gsum * sig * usum);
+    const float av = __uint_as_float((uint32_t)ab << 16);
+    // the block's 32 values are lanes [0, 32) or [32, 64) of this wave
+    float amax = fabsf(av);
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 32));
+    const uint32_t sb = scale_byte(amax);
+    const size_t row = (size_t)tile * kTile + m;
+    a.aq[row * I + (size_t)cb * kGuCols + j] = (uint8_t)e4m3_code(av * inv_scale(sb));
+    if (j == 0) a.as[row * (I / 32) + cb] = (uint8_t)sb;
+    if (a.act) a.act[row * I + (size_t)cb * kGuCols + j] = ab;
 }
 
-// ---- stage 4: MXFP8 intermediate + grouped down GEMM + scatter --------------
+// ---- stage 4: grouped down GEMM + scatter -----------------------------------
 
 struct DownArgs {
-    const uint16_t *act;
+    const uint8_t *aq, *as;             // MXFP8 intermediate
     const uint8_t *w, *ws;              // down codes [E][H][I], scales [E][H][I/32]
-    const int32_t *header, *tile_expert, *row_pair;
-    uint8_t *aq, *as;                   // optional copy of the MXFP8 intermediate
+    const int32_t *tile_expert, *row_pair;
     uint16_t *out_pair;                 // [B*K][H] BF16
-    int H, I, nblocks, ncolblk, max_rows;
+    int H, I, nblocks, ncolblk;
 };
 
-// Workgroup = (tile, 64 output columns).  All 256 threads first round the
-// tile's 16 x I intermediate to MXFP8 into LDS; each wave then owns 16 output
-// columns over the whole I.
+// Workgroup = (tile, 64 output columns), one 16-column result tile per wave
+// over the whole I; both operands are loaded straight into the matrix
+// instruction's layout.
 __global__ void __launch_bounds__(kGemmThreads) down_kernel(DownArgs a) {
-    extern __shared__ __align__(16) uint8_t lds[];
     const int lb = wd::xcd_logical(blockIdx.x, a.nblocks);
     const int tile = lb / a.ncolblk, cb = lb % a.ncolblk;
-    if (tile >= a.header[0]) return;
-    const int I = a.I, H = a.H, nbi = I / 32;
-    const int stride = I + 16;                         // LDS row pitch (bytes), 16-aligned
-    uint8_t *lc = lds, *ls = lds + kTile * stride;
-    for (int blk = threadIdx.x; blk < kTile * nbi; blk += kGemmThreads) {
-        const int m = blk / nbi, jb = blk % nbi;
-        const size_t row = (size_t)tile * kTile + m;
-        float v[32];
-        load_bf16x32(a.act + row * I + 32 * jb, v);
-        uint32_t codes[8];
-        const uint32_t sb = quantize32(v, codes);
-        u32x4 c0 = {codes[0], codes[1], codes[2], codes[3]}, c1 = {codes[4], codes[5], codes[6], codes[7]};
-        *reinterpret_cast<u32x4 *>(lc + m * stride + 32 * jb) = c0;
-        *reinterpret_cast<u32x4 *>(lc + m * stride + 32 * jb + 16) = c1;
-        ls[m * nbi + jb] = (uint8_t)sb;
-        if (a.aq && cb == 0) {
-            *reinterpret_cast<u32x4 *>(a.aq + row * I + 32 * jb) = c0;
-            *reinterpret_cast<u32x4 *>(a.aq + row * I + 32 * jb + 16) = c1;
-            a.as[row * nbi + jb] = (uint8_t)sb;
-        }
-    }
-    __syncthreads();
+    const int e = a.tile_expert[tile];
+    if (e < 0) return;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
+    const int I = a.I, H = a.H, nbi = I / 32;
     const int col0 = cb * kDnCols + 16 * wv;
     if (col0 >= H) return;
-    const int e = a.tile_expert[tile];
+    const u32x4 pairs = wd::ld16(a.row_pair + (size_t)tile * kTile + 4 * g);   // rows 4g .. 4g+3
+    const size_t arow = (size_t)tile * kTile + r;
+    const uint8_t *ac = a.aq + arow * I, *asr = a.as + arow * nbi;
     const size_t wrow = (size_t)e * H + col0 + r;
     const uint8_t *wc = a.w + wrow * I, *wsr = a.ws + wrow * nbi;
-    const uint8_t *ac = lc + r * stride, *asr = ls + r * nbi;
     v4f c = {0.f, 0.f, 0.f, 0.f};
     const int nks = (I + kStepK - 1) / kStepK;
     for (int s0 = 0; s0 < nks; s0 += kBatch) {
-        Frag fw[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) fw[i] = load_frag(wc, wsr, I, (s0 + i) * kStepK, g);
+        Frag fa[kBatch], fw[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
-            const Frag fa = load_frag(ac, asr, I, (s0 + i) * kStepK, g);
-            c = mfma_mx(make_operand(fa.lo, fa.hi), make_operand(fw[i].lo, fw[i].hi), c, fa.s, fw[i].s);
+            fa[i] = load_frag(ac, asr, I, (s0 + i) * kStepK, g);
+            fw[i] = load_frag(wc, wsr, I, (s0 + i) * kStepK, g);
         }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            c = mfma_mx(make_operand(fa[i].lo, fa[i].hi), make_operand(fw[i].lo, fw[i].hi), c, fa[i].s, fw[i].s);
     }
-    // scatter: result rows 4*(lane/16) + q of column col0 + lane % 16
+    // scatter: result rows 4g + q of column col0 + r
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int p = a.row_pair[tile * kTile + 4 * g + q];
+        const int p = (int)pairs[q];
         if (p >= 0) a.out_pair[(size_t)p * H + col0 + r] = wd::to_bf16(c[q]);
     }
 }
@@ -500,25 +512,23 @@ int ec_moe_decode_ex(const uint16_t *x, const int32_t *ids, const float *w,
     uint16_t *out_pair = reinterpret_cast<uint16_t *>(ws + off[EC_WS_OUT_PAIR]);
     const int rows = tiles * ec::kTile;
 
-    ec::AlignArgs aa{ids, header, tile_expert, row_pair, B * K, E};
+    ec::AlignArgs aa{ids, header, tile_expert, row_pair, B * K, E, tiles};
     if ((rc = launch(ec::align_kernel, 1, ec::kAlignThreads, 0, aa, c, 1, s)) != WD_OK || last == 1) return rc;
 
-    ec::GatherArgs ga{x, header, row_pair, xq, xs, K, H, rows};
+    ec::GatherArgs ga{x, row_pair, xq, xs, K, H, rows};
     if ((rc = launch(ec::gather_kernel, (rows + 3) / 4, 256, 0, ga, c, 2, s)) != WD_OK || last == 2) return rc;
 
     const int gu_cols = I / ec::kGuCols;
-    ec::GateUpArgs gua{xq, xs, wgu, sgu, header, tile_expert, act, H, I, tiles * gu_cols, gu_cols};
-    if ((rc = launch(ec::gate_up_kernel, tiles * gu_cols, ec::kGemmThreads, 0, gua, c, 3, s)) != WD_OK ||
+    ec::GateUpArgs gua{xq, xs, wgu, sgu, tile_expert, aq, aq + (size_t)rows * I,
+                       c.keep_intermediate ? act : nullptr, H, I, tiles * gu_cols, gu_cols};
+    if ((rc = launch(ec::gate_up_kernel, tiles * gu_cols, ec::kGuThreads, 0, gua, c, 3, s)) != WD_OK ||
         last == 3)
         return rc;
 
     const int dn_cols = (H + ec::kDnCols - 1) / ec::kDnCols;
-    const size_t lds = (size_t)ec::kTile * (I + 16) + (size_t)ec::kTile * (I / 32);
-    ec::DownArgs da{act, wdn, sd, header, tile_expert, row_pair,
-                    c.keep_intermediate ? aq : nullptr, c.keep_intermediate ? aq + (size_t)rows * I : nullptr,
-                    out_pair, H, I, tiles * dn_cols, dn_cols, rows};
-    if ((rc = launch(ec::down_kernel, tiles * dn_cols, ec::kGemmThreads, lds, da, c, 4, s)) != WD_OK ||
-        last == 4)
+    ec::DownArgs da{aq, aq + (size_t)rows * I, wdn, sd, tile_expert, row_pair, out_pair, H, I, tiles * dn_cols,
+                    dn_cols};
+    if ((rc = launch(ec::down_kernel, tiles * dn_cols, ec::kGemmThreads, 0, da, c, 4, s)) != WD_OK || last == 4)
         return rc;
 
     ec::CombineArgs ca{out_pair, ids, w, out, B, K, E, H};

@@ -168,7 +168,7 @@ def test_ec_rejects_bad_arguments():
     assert lib.ec_workspace_bytes(0, 8, 128, 2048, 768) == 0
     assert lib.ec_workspace_bytes(1, 8, 128, 100, 768) == 0
     assert ec(H=100) == -2 and ec(I=48) == -2 and ec(K=0) == -2 and ec(K=9, E=8) == -2 and ec(B=-1) == -2
-    assert ec(E=1025) == -7 and ec(H=8192 + 32) == -7 and ec(I=2048 + 32) == -7 and ec(B=513) == -7
+    assert ec(E=1025) == -7 and ec(H=8192 + 32) == -7 and ec(I=8192 + 32) == -7 and ec(B=513) == -7
     assert ec(x=None) == -1 and ec(ws=None) == -1 and ec(sd=None) == -1 and ec(out=None) == -1
     assert ec(x=A + 8) == -3 and ec(ws=A + 16) == -3 and ec(out=A + 2) == -3
     assert ec(ws_bytes=lib.ec_workspace_bytes(1, 8, 128, 2048, 768) - 1) == -4

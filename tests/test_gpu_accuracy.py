@@ -9,6 +9,7 @@ import torch
 
 import oracle
 from moe_decode_gate_amd import inputs as gen
+from moe_decode_gate_amd import binding as wd
 from tests.gpu_common import DevLayer, DevTokens, bf16_bits_to_f64, bits_of, log, run_layer
 
 pytestmark = pytest.mark.gpu
@@ -35,9 +36,14 @@ def test_accuracy_vs_unrounded_reference(name, B, routing):
                                           np.uint16)).reshape(y_wd.shape)
     cv = oracle.moe_decode_conventional(*args, nthreads=16)
     got = bf16_bits_to_f64(bits_of(out))
+    dt = DevTokens(t)
+    ec = bf16_bits_to_f64(bits_of(wd.ec_moe_decode(dt.x, dt.ids, dt.w, dl.wgu, dl.sgu, dl.wd, dl.sd)))
     n = float(np.linalg.norm(gt))
-    e_gpu, e_wd, e_cv = (float(np.linalg.norm(a - gt)) / n for a in (got, y_wd_bf16, cv))
+    e_gpu, e_wd, e_cv, e_ec = (float(np.linalg.norm(a - gt)) / n for a in (got, y_wd_bf16, cv, ec))
     log(f"[accuracy] {name} B={B}: rel L2 error gpu {e_gpu:.3e}, oracle warp-decode {e_wd:.3e}, "
-        f"conventional {e_cv:.3e}, conventional / gpu = {e_cv / e_gpu:.2f}")
+        f"conventional {e_cv:.3e} (GPU expert-centric path {e_ec:.3e}), conventional / gpu = {e_cv / e_gpu:.2f}")
     assert abs(e_gpu - e_wd) <= 0.05 * e_wd          # same roundings, FP32 vs FP64 sums
     assert e_cv > e_gpu
+    # the GPU expert-centric path has the conventional roundings plus its matrix instruction's
+    # truncated sums (relative error ~2^-14, far below the MXFP8 activation rounding)
+    assert abs(e_ec - e_cv) <= 0.05 * e_cv

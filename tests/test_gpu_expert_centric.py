@@ -43,6 +43,7 @@ def _cuda():
 
 
 def run_ec(dl: DevLayer, dt: DevTokens, keep: bool = True, last_stage: int = 0):
+    """One call with a poisoned workspace; keep also writes the BF16 intermediate."""
     E, H, I = dl.spec.E, dl.spec.H, dl.spec.I
     B, K = dt.ids.shape
     lay = wd.ec_workspace_layout(B, K, E, H, I)
