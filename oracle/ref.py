@@ -12,7 +12,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB points the front end at another build of oracle.c (the mutation
+# check of the pins runs the pin suite against deliberately broken copies).
+lib_path = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
