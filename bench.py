@@ -409,6 +409,9 @@ def main():
     ap.add_argument("--no-b32", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip the expert-centric comparison")
+    ap.add_argument("--only-compare", action="store_true",
+                    help="run only the expert-centric comparison and print its JSON object (for profiling)")
+    ap.add_argument("--compare-batches", default="1,2,4,8,16,32,64", help="batch sizes of the comparison")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs the layer "
@@ -427,6 +430,10 @@ def main():
     t0 = time.time()
     L = gen.make_layer(spec, threads=16)
     eprint(f"[bench] layer generated in {time.time() - t0:.1f} s")
+    compare_batches = tuple(int(b) for b in args.compare_batches.split(","))
+    if args.only_compare:
+        print(json.dumps({"vs_expert_centric": measure_comparison(torch, wd, gen, L, compare_batches)}), flush=True)
+        return
 
     peak, peak_cfg, copy_bw = hbm_read_peak(torch, wd)
     eprint(f"[bench] contiguous-read peak {peak:.0f} GB/s (unroll, blocks = {peak_cfg}); copy {copy_bw:.0f} GB/s")
@@ -456,7 +463,7 @@ def main():
 
     stack = None if args.no_stack else measure_stack(torch, wd, gen, L, peak)
 
-    compare = None if args.no_compare else measure_comparison(torch, wd, gen, L)
+    compare = None if args.no_compare else measure_comparison(torch, wd, gen, L, compare_batches)
 
     cpu = None if args.no_cpu else cpu_baseline(oracle, L, gen, 1)
 
