@@ -97,7 +97,16 @@ enum wd_status {
  *                    routed to that expert, each weight row read and
  *                    converted once (requires lanes_per_row 64, math 2,
  *                    weight_loads 1); both forms give bit-identical results
- *                    for lanes_per_row 64 and math 2 (down: 1)
+ *                    for lanes_per_row 64 and math 2;
+ *                    3 = one wave per (expert, block of 16 rows) on the BF16
+ *                    matrix cores (v_mfma_f32_16x16x32_bf16): weights
+ *                    converted exactly to BF16, x as stored, FP32
+ *                    accumulation in the matrix core's summation order
+ *                    (rows_per_wave 1, lanes_per_row 64, math 2,
+ *                    weight_loads 1; waves_per_block and order apply as for
+ *                    the other forms).  Default: 3 when B >= 32 and none of
+ *                    rows_per_wave, lanes_per_row, math, weight_loads is set,
+ *                    else 1.  (down: 1)
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
  *                    streamed once and not kept in the caches)
  *   start_event,     optional hipEvent_t handles (created by the caller); when

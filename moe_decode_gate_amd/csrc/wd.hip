@@ -54,15 +54,21 @@ int check_dims(int B, int K, int E, int H, int I) {
 // for B in {1, 2, 4, 8, 16, 32, 64}:
 //   gate/up, B <= 4: one row per 64-lane wave, BF16-pair dot products,
 //          non-temporal weight loads (no row is read twice), hardware order;
-//   gate/up, B >= 5: 32 lanes per row, 4 rows per lane group (8 per wave),
+//   gate/up, B 5..31: 32 lanes per row, 4 rows per lane group (8 per wave),
 //          row-block-major order with XCD-contiguous numbering, so the tokens
 //          that share an expert row read it from the same L2 while resident;
+//   gate/up, B >= 32: the expert form on the matrix cores (one wave per
+//          expert row block; 80-90 us at B = 32-64 against 85-135 us);
 //   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
 //   down, B 3..5: 4 rows per wave, FP32 math; B >= 6: 8 rows per wave.
 int resolve(const wd_launch *in, int B, bool down, wd_launch *out) {
     wd_launch c = in ? *in : wd_launch{};
     const bool batch = down ? B >= 3 : B >= 5;
-    if (c.form == 0) c.form = 1;
+    // B >= 32: gate/up in the expert form on the matrix cores, whose weight stream
+    // is read once per expert however many tokens share it
+    if (c.form == 0) c.form = (!down && B >= 32 && c.rows_per_wave == 0 && c.lanes_per_row == 0 &&
+                               c.math == 0 && c.weight_loads == 0) ? 3 : 1;
+    if (c.form == 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
     if (c.rows_per_wave == 0)
         c.rows_per_wave = !batch ? 1 : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
     if (c.waves_per_block == 0) c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch ? 4 : 1);
@@ -84,10 +90,14 @@ int resolve(const wd_launch *in, int B, bool down, wd_launch *out) {
     if (c.xcd_remap != 1 && c.xcd_remap != 2) return WD_ERR_UNSUPPORTED;
     if (c.math != wd::kMathF32 && c.math != wd::kMathDot2) return WD_ERR_UNSUPPORTED;
     if (c.lanes_per_row != 16 && c.lanes_per_row != 32 && c.lanes_per_row != 64) return WD_ERR_UNSUPPORTED;
-    if (c.form != 1 && c.form != 2) return WD_ERR_UNSUPPORTED;
+    if (c.form < 1 || c.form > 3) return WD_ERR_UNSUPPORTED;
     if (c.weight_loads != 1 && c.weight_loads != 2) return WD_ERR_UNSUPPORTED;
     if (down && (c.lanes_per_row != 64 || c.form != 1)) return WD_ERR_UNSUPPORTED;
     if (c.form == 2 && (c.lanes_per_row != 64 || c.math != wd::kMathDot2 || c.weight_loads != 1))
+        return WD_ERR_UNSUPPORTED;
+    // matrix-core expert form: fixed 16-row blocks and lane layout, BF16 operands, cached loads
+    if (c.form == 3 && (c.rows_per_wave != 1 || c.lanes_per_row != 64 || c.math != wd::kMathDot2 ||
+                        c.weight_loads != 1))
         return WD_ERR_UNSUPPORTED;
     *out = c;
     return WD_OK;
@@ -211,11 +221,12 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     const int lpr = c.lanes_per_row;
     const int cpl = round_cpl_gate_up((H / 16 + lpr - 1) / lpr);
     if (cpl < 0) return WD_ERR_UNSUPPORTED;
-    const int rows_per_wave = (64 / lpr) * c.rows_per_wave;
+    const int rows_per_wave = c.form == 3 ? 16 : (64 / lpr) * c.rows_per_wave;
     if (I % rows_per_wave) return WD_ERR_UNSUPPORTED;
     const bool tail = (H / 16) % (lpr * cpl) != 0;
-    KernelFn fn = c.form == 2 ? gate_up_expert_fn(cpl, c.rows_per_wave, tail)
-                              : gate_up_fn(cpl, c.rows_per_wave, lpr, tail, c.math, c.weight_loads == 2);
+    KernelFn fn = c.form == 3   ? wd::gate_up_mfma_kernel
+                  : c.form == 2 ? gate_up_expert_fn(cpl, c.rows_per_wave, tail)
+                                : gate_up_fn(cpl, c.rows_per_wave, lpr, tail, c.math, c.weight_loads == 2);
     if (!fn) return WD_ERR_UNSUPPORTED;
     if (B == 0) return WD_OK;
     if (!checked_device && (rc = check_device())) return rc;
@@ -223,7 +234,7 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     a.x = x; a.ids = ids; a.w = w_gu; a.s = s_gu; a.out = act;
     a.B = B; a.K = K; a.E = E; a.H = H; a.I = I;
     a.nrowblk = I / rows_per_wave;
-    a.nwaves = (c.form == 2 ? E : B * K) * a.nrowblk;
+    a.nwaves = (c.form == 1 ? B * K : E) * a.nrowblk;
     a.order = c.order; a.remap = c.xcd_remap;
     return launch(fn, a, c, (hipStream_t)stream);
 }

@@ -281,6 +281,209 @@ __global__ __launch_bounds__(256) void gate_up_expert_kernel(LayerArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Gate/up, expert form on the matrix cores: one wave per (expert e, block of 16
+// intermediate rows j0 .. j0+15), serving the slots routed to e in groups of up
+// to 16.  The wave issues its first weight loads before it reads topk_ids (they
+// do not depend on the routing), scans the ids 512 slots at a time with
+// independent loads, and keeps one batch of weight loads in flight ahead of
+// the batch it computes.
+//
+// For a group of T slots the wave forms the 16 x T tiles G = Wg[e, j0:j0+16, :] X
+// and U = Wu[e, j0:j0+16, :] X, whose columns are the x rows of the group's
+// tokens, with v_mfma_f32_16x16x32_bf16: the weights are converted MXFP8 ->
+// BF16 in registers (exact for every normal product), x is used as stored
+// (BF16) and the matrix core accumulates the products in FP32 (measured on
+// MI355X to within a few 2^-24 of the sum of |products|, like sequential FP32
+// addition).  Operand layout: lane l holds weight row l % 16 (A) and the
+// group's column l % 16 (B), elements 8 (l / 16) + 0..7 of the instruction's
+// 32.  One 16-byte code load per lane and row covers elements
+// 64 s + 16 (l / 16) + 0..15 of step s and feeds two instructions (first 8,
+// last 8); x is loaded with the same mapping, so each product pairs the weight
+// and the x element of the same h.  The result lane l holds column l % 16,
+// rows 4 (l / 16) + 0..3: SiLU(g) * u in FP32, rounded to BF16, one 8-byte
+// store per lane.  The slots are found by a ballot over topk_ids as in the
+// expert form above; slots with an id outside [0, E) get NaN rows from expert
+// 0's waves.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaSteps = 4;    // 64-element steps whose loads are issued together
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+struct MfmaBatch {                      // one wave's loads for kMfmaSteps 64-element steps
+    u32x4 wg[kMfmaSteps], wu[kMfmaSteps];
+    uint64_t sg, su;                    // the row's 2 * kMfmaSteps E8M0 bytes of these steps
+};
+static_assert(kMfmaSteps == 4, "one 8-byte scale load covers a batch");
+
+__global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int unit = logical_wave(a);
+    if (unit >= a.nwaves) return;
+    const int e = unit / a.nrowblk, jb = unit % a.nrowblk;
+    const int BK = a.B * a.K, H = a.H, I = a.I;
+    const int r16 = lane & 15, q = lane >> 4;
+
+    const size_t nbr = (size_t)(H >> 5);
+    const size_t grow = (size_t)e * 2 * I + (size_t)jb * 16 + r16;
+    const uint8_t *pg = a.w + grow * (size_t)H;
+    const uint8_t *pu = pg + (size_t)I * H;
+    const uint8_t *sg = a.s + grow * nbr;
+    const uint8_t *su = sg + (size_t)I * nbr;
+    const int s_lo = 0, s_hi = (H + 63) >> 6;        // 64-element steps
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // Weight and scale loads are unconditional (offsets outside the wave's range are
+    // clamped to its start; the selects in the compute step zero them), so no branch,
+    // and no wait inside one, separates them.
+    // The E8M0 bytes of a batch (blocks 2 s0 .. 2 s0 + 7 of the lane's row) come in
+    // one 8-byte load when the row holds them all (always when H is a multiple of
+    // 256), else byte by byte.
+    auto load_batch = [&](int s0, MfmaBatch &bt) {
+#pragma unroll
+        for (int i = 0; i < kMfmaSteps; ++i) {
+            const int k = 64 * (s0 + i) + 16 * q;
+            const int kc = (s0 + i < s_hi && k < H) ? k : 64 * s_lo;
+            bt.wg[i] = ld16(pg + kc);
+            bt.wu[i] = ld16(pu + kc);
+        }
+        if (2 * s0 + 8 <= (int)nbr) {
+            bt.sg = *reinterpret_cast<const uint64_t *>(sg + 2 * s0);
+            bt.su = *reinterpret_cast<const uint64_t *>(su + 2 * s0);
+        } else {
+            bt.sg = 0;
+            bt.su = 0;
+            for (int b = 0; b < 8 && 2 * s0 + b < (int)nbr; ++b) {
+                bt.sg |= (uint64_t)sg[2 * s0 + b] << (8 * b);
+                bt.su |= (uint64_t)su[2 * s0 + b] << (8 * b);
+            }
+        }
+    };
+    // The first batch does not depend on the routing: issue it before reading topk_ids.
+    MfmaBatch cur;
+    load_batch(s_lo, cur);
+
+    if (e == 0) {              // NaN rows for slots whose id is outside [0, E)
+        for (int base = 0; base < BK; base += 64) {
+            const int sl = base + lane;
+            const int id = sl < BK ? a.ids[sl] : 0;
+            uint64_t m = __builtin_amdgcn_ballot_w64(sl < BK && (unsigned)id >= (unsigned)a.E);
+            while (m) {
+                const int s0 = base + (int)__builtin_ctzll(m);
+                m &= m - 1;
+                if (lane < 16) a.out[(size_t)s0 * I + (size_t)jb * 16 + lane] = 0x7FC0;
+            }
+        }
+    }
+
+    // Slots routed to e, found 512 at a time: eight independent id loads, then ballots.
+    uint64_t mk[8];
+    int chunk = 0, next_chunk = 0;
+    auto refill = [&]() {
+        int idv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = next_chunk + 64 * u + lane;
+            idv[u] = sl < BK ? a.ids[sl] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mk[u] = __builtin_amdgcn_ballot_w64(idv[u] == e);
+        chunk = next_chunk;
+        next_chunk += 512;
+    };
+    refill();
+
+    for (;;) {
+        // the next up-to-16 slots routed to e, in slot order, one per lane 0..15
+        int my_slot = 0, cnt = 0;
+        for (;;) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                while (mk[u] != 0 && cnt < 16) {
+                    const int s0 = chunk + 64 * u + (int)__builtin_ctzll(mk[u]);
+                    mk[u] &= mk[u] - 1;
+                    if (lane == cnt) my_slot = s0;
+                    ++cnt;
+                }
+            }
+            if (cnt == 16 || next_chunk >= BK) break;
+            refill();
+        }
+        if (cnt == 0) break;
+        const int slot = __shfl(my_slot, r16);
+        const bool live = r16 < cnt;
+        const uint16_t *xr = a.x + (size_t)(live ? slot / a.K : 0) * H;
+
+        f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = cg;
+        for (int s0 = s_lo; s0 < s_hi; s0 += kMfmaSteps) {
+            u32x4 x0[kMfmaSteps], x1[kMfmaSteps];
+#pragma unroll
+            for (int i = 0; i < kMfmaSteps; ++i) {
+                const int k = 64 * (s0 + i) + 16 * q;
+                const int kc = (s0 + i < s_hi && k < H) ? k : 64 * s_lo;
+                x0[i] = zero;
+                x1[i] = zero;
+                if (live) {                            // only the lanes of live columns read x
+                    x0[i] = ld16(xr + kc);
+                    x1[i] = ld16(xr + kc + 8);
+                }
+            }
+            // prefetch: the next batch, or this wave's first batch again for a further group
+            MfmaBatch nxt;
+            const bool more = s0 + kMfmaSteps < s_hi;
+            if (more || cnt == 16) load_batch(more ? s0 + kMfmaSteps : s_lo, nxt);
+#pragma unroll
+            for (int i = 0; i < kMfmaSteps; ++i) {
+                const int k = 64 * (s0 + i) + 16 * q;
+                const bool ok = s0 + i < s_hi && k < H;
+                const bool xo = ok && live;
+                const int sh = 8 * (2 * i + (q >> 1));      // byte of block 2 (s0 + i) + q / 2
+                const uint32_t bg = (uint32_t)(cur.sg >> sh) & 0xFFu, bu = (uint32_t)(cur.su >> sh) & 0xFFu;
+                const float fg = e8m0_operand(ok ? bg : 127u), fu = e8m0_operand(ok ? bu : 127u);
+                const u32x4 wgi = ok ? cur.wg[i] : zero, wui = ok ? cur.wu[i] : zero;
+                const u32x4 xa = xo ? x0[i] : zero, xb = xo ? x1[i] : zero;
+                uint32_t gw[8], uw[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    mx_word_bf16(wgi[d], fg, gw[2 * d], gw[2 * d + 1]);
+                    mx_word_bf16(wui[d], fu, uw[2 * d], uw[2 * d + 1]);
+                }
+                const u32x4 g0 = {gw[0], gw[1], gw[2], gw[3]}, g1 = {gw[4], gw[5], gw[6], gw[7]};
+                const u32x4 u0 = {uw[0], uw[1], uw[2], uw[3]}, u1 = {uw[4], uw[5], uw[6], uw[7]};
+                cg = mfma_bf16(g0, xa, cg);
+                cg = mfma_bf16(g1, xb, cg);
+                cu = mfma_bf16(u0, xa, cu);
+                cu = mfma_bf16(u1, xb, cu);
+            }
+            if (more || cnt == 16) cur = nxt;
+        }
+        if (live) {
+            uint32_t packed[2];
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+                uint32_t h2 = 0;
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const float gv = cg[r + d], uv = cu[r + d];
+                    const float en = expf(-__builtin_fabsf(gv));
+                    const float sig = gv >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
+                    h2 |= (uint32_t)to_bf16(gv * sig * uv) << (16 * d);
+                }
+                packed[r >> 1] = h2;
+            }
+            *reinterpret_cast<uint2 *>(a.out + (size_t)slot * I + (size_t)jb * 16 + 4 * q) =
+                make_uint2(packed[0], packed[1]);
+        }
+        if (cnt < 16) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Down: one wave per (token b, block of R output dims).
 //
 // The K routed rows Wd[e_k, h, 0:I] of one output dim are cut into 16-element

@@ -177,3 +177,16 @@ def test_ec_rejects_bad_arguments():
     assert ec(out=None, cfg=wd.ECLaunch(last_stage=9)) == -7
     assert ec(B=0, x=None, ids=None, tw=None, out=None, ws=None, ws_bytes=0) == 0
     assert lib.ec_workspace_layout(1, 8, 128, 2048, 768, None) == -1
+
+
+def test_matrix_core_form_limits():
+    # form 3 (gate/up on the matrix cores) has a fixed lane layout, BF16 operands and cached loads
+    def gux(**kw):
+        return lib.wd_gate_up_ex(A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(wd.Launch(**kw)), None)
+
+    assert gux(form=3, rows_per_wave=2) == -7
+    assert gux(form=3, lanes_per_row=32) == -7
+    assert gux(form=3, math=1) == -7
+    assert gux(form=3, weight_loads=2) == -7
+    assert gux(form=4) == -7
+    assert lib.wd_down_ex(A, A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(wd.Launch(form=3)), None) == -7

@@ -10,8 +10,10 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from moe_decode_gate_amd import inputs as gen
-from tests.gpu_common import DevLayer, DevTokens, bits_of, log, run_layer, shifted
+from tests.gpu_common import DevLayer, DevTokens, act_flip_stats, bits_of, log, run_layer, shifted
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +85,7 @@ FINGERPRINT_CFGS = {
     "token-dot2": (dict(form=1, math=2), dict(math=2)),
     "expert": (dict(form=2), dict(math=2, rows_per_wave=8)),
     "lanes16": (dict(form=1, lanes_per_row=16, rows_per_wave=2), dict(math=1, rows_per_wave=4)),
+    "matrix-cores": (dict(form=3), None),
 }
 
 
@@ -230,6 +233,44 @@ def test_gate_up_expert_form_bad_ids():
     ids = t.ids.copy(); ids[3, 2] = 16; ids[7, 0] = -5
     dt = DevTokens(gen.Tokens(x=t.x, ids=ids, w=t.w))
     a, o = run_layer(dl, dt, cfg_gu=dict(form=2))
+    af = a.float().cpu().numpy()
+    assert np.isnan(af[3, 2]).all() and np.isnan(af[7, 0]).all()
+    assert np.isfinite(np.delete(af.reshape(-1, spec.I), [3 * 4 + 2, 7 * 4 + 0], axis=0)).all()
+    of = o.float().cpu().numpy()
+    assert np.isnan(of[3]).all() and np.isnan(of[7]).all()
+
+
+@pytest.mark.parametrize("B", [3, 40, 64])
+def test_gate_up_matrix_core_form(B):
+    """The expert form on the matrix cores sums in another order than the token
+    form (the matrix core's FP32 accumulation), so it is held to the oracle:
+    rare one-ulp flips only.  Zipf routing over 16 experts puts more than 16
+    slots on popular experts (several slot groups per wave), and one token
+    repeats an expert; reruns are bit-identical."""
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=93)
+    L = gen.make_layer(spec, threads=16)
+    dl = DevLayer(L)
+    t = gen.make_tokens(spec, B, routing="zipf")
+    t.ids[0, 1] = t.ids[0, 0]
+    dt = DevTokens(t)
+    a, _ = run_layer(dl, dt, cfg_gu=dict(form=3))
+    ref = oracle.gate_up(t.x, t.ids, L.wgu, L.sgu, nthreads=16)
+    frac, ulps, within = act_flip_stats(bits_of(a), ref)
+    log(f"[mfma form] B={B}: max slots per expert {np.bincount(t.ids.ravel()).max()}, flips {frac:.2e}, "
+        f"max {ulps:.1f} ulp")
+    assert frac <= 2e-3 and within, (frac, ulps)
+    for _ in range(2):
+        a2, _ = run_layer(dl, dt, cfg_gu=dict(form=3))
+        assert np.array_equal(bits_of(a2), bits_of(a))
+
+
+def test_gate_up_matrix_core_form_bad_ids():
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=94)
+    dl = DevLayer(gen.make_layer(spec, threads=16))
+    t = gen.make_tokens(spec, 12)
+    ids = t.ids.copy(); ids[3, 2] = 16; ids[7, 0] = -5
+    dt = DevTokens(gen.Tokens(x=t.x, ids=ids, w=t.w))
+    a, o = run_layer(dl, dt, cfg_gu=dict(form=3))
     af = a.float().cpu().numpy()
     assert np.isnan(af[3, 2]).all() and np.isnan(af[7, 0]).all()
     assert np.isfinite(np.delete(af.reshape(-1, spec.I), [3 * 4 + 2, 7 * 4 + 0], axis=0)).all()

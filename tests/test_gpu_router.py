@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from moe_decode_gate_amd import inputs as gen
-from tests.gpu_common import DevLayer, assert_output_parity, bits_of, log, shifted, unit_shift
+from tests.gpu_common import DevLayer, act_flip_propagation, assert_output_parity, bits_of, log, shifted, unit_shift
 
 pytestmark = pytest.mark.gpu
 
@@ -57,11 +57,14 @@ def test_routed_layer_end_to_end():
     L = gen.make_layer(spec, experts=ids_o.ravel(), threads=16)
     dl = DevLayer(L)
     t = gen.make_tokens(spec, B, step=5)
-    y64, _ = oracle.moe_decode(t.x, ids_o, w_o.astype(np.float32), L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
+    y64, act_o = oracle.moe_decode(t.x, ids_o, w_o.astype(np.float32), L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
     k = unit_shift(y64)
     x = torch.from_numpy(t.x.view(np.int16)).cuda().view(torch.bfloat16)
     ids, w = wd.route(torch.from_numpy(logits).cuda(), spec.K)
     out = wd.moe_decode(x, ids, w, dl.wgu, dl.sgu, dl.wd, shifted(dl.sd, k))
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ids_o)
-    assert_output_parity(bits_of(out), y64 * 2.0 ** k, "routed qwen3 B=32", slack=2e-4)
+    act = wd.gate_up(x, ids, dl.wgu, dl.sgu)            # the intermediate wd_moe_decode formed
+    torch.cuda.synchronize()
+    prop = act_flip_propagation(bits_of(act), act_o, ids_o, w_o, L.wd, L.sd)
+    assert_output_parity(bits_of(out), y64 * 2.0 ** k, "routed qwen3 B=32", extra=prop * 2.0 ** k)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from moe_decode_gate_amd import inputs as gen
-from tests.gpu_common import assert_output_parity, bits_of, log
+from tests.gpu_common import act_flip_propagation, assert_output_parity, bits_of, log
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,15 @@ def test_stack_layer_local_parity(stack, layer):
     if np.abs(y64).max() == 0.0:
         assert (out & 0x7FFF == 0).all()              # an all-zero input stays exactly zero
         return
-    assert_output_parity(out, y64, f"stack layer {layer}", unit_scale=False, slack=2e-4)
+    # the layer's intermediate, recomputed (the kernels are deterministic), bounds how far the
+    # GPU's rare intermediate flips move the exact output
+    from moe_decode_gate_amd import binding as wd
+    act = wd.gate_up(stack["xs"][layer], stack["ids"][layer], stack["dev"][0], stack["dev"][1])
+    torch.cuda.synchronize()
+    w_np = stack["ws"][layer].cpu().numpy()
+    _, act_o = oracle.moe_decode(x_in, ids_o, w_np, L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
+    prop = act_flip_propagation(bits_of(act), act_o, ids_o, w_np, L.wd, L.sd)
+    assert_output_parity(out, y64, f"stack layer {layer}", unit_scale=False, extra=prop)
 
 
 def test_stack_last_layer_on_fresh_input(stack):
@@ -76,8 +84,12 @@ def test_stack_last_layer_on_fresh_input(stack):
     out = wd.moe_decode(x, stack["ids"][l], stack["ws"][l], *stack["dev"])
     torch.cuda.synchronize()
     ids_o, _ = oracle.route(stack["logits"][l], spec.K)
-    y64, _ = oracle.moe_decode(t.x, ids_o, stack["ws"][l].cpu().numpy(), L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
-    assert_output_parity(bits_of(out), y64, "stack last layer, fresh x", unit_scale=False, slack=2e-4)
+    w_np = stack["ws"][l].cpu().numpy()
+    y64, act_o = oracle.moe_decode(t.x, ids_o, w_np, L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
+    act = wd.gate_up(x, stack["ids"][l], stack["dev"][0], stack["dev"][1])
+    torch.cuda.synchronize()
+    prop = act_flip_propagation(bits_of(act), act_o, ids_o, w_np, L.wd, L.sd)
+    assert_output_parity(bits_of(out), y64, "stack last layer, fresh x", unit_scale=False, extra=prop)
 
 
 def test_stack_graph_replays_match_eager(stack):
