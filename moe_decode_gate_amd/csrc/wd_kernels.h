@@ -342,8 +342,9 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     // clamped to its start; the selects in the compute step zero them), so no branch,
     // and no wait inside one, separates them.
     // The E8M0 bytes of a batch (blocks 2 s0 .. 2 s0 + 7 of the lane's row) come in
-    // one 8-byte load when the row holds them all (always when H is a multiple of
-    // 256), else byte by byte.
+    // one 8-byte load when the row holds them all and rows start on 4-byte
+    // boundaries (H a multiple of 128; always for H a multiple of 256), else byte
+    // by byte.
     auto load_batch = [&](int s0, MfmaBatch &bt) {
 #pragma unroll
         for (int i = 0; i < kMfmaSteps; ++i) {
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
             bt.wg[i] = ld16(pg + kc);
             bt.wu[i] = ld16(pu + kc);
         }
-        if (2 * s0 + 8 <= (int)nbr) {
+        if ((nbr & 3) == 0 && 2 * s0 + 8 <= (int)nbr) {      // dword-aligned: row bases are multiples of 4
             bt.sg = *reinterpret_cast<const uint64_t *>(sg + 2 * s0);
             bt.su = *reinterpret_cast<const uint64_t *>(su + 2 * s0);
         } else {

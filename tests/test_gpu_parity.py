@@ -55,6 +55,8 @@ CASES = {
     "wide_h8192": (gen.LayerSpec(E=4, K=2, H=8192, I=64, seed=503), 2, "softmax", False),
     "deep_ki16384": (gen.LayerSpec(E=6, K=4, H=64, I=4096, seed=504), 2, "softmax", False),
     "b64": (gen.LayerSpec(E=16, K=4, H=256, I=96, seed=505), 64, "softmax", False),
+    # H/32 = 9 scale bytes per row: rows start off 4-byte boundaries (byte-wise scale loads)
+    "h288": (gen.LayerSpec(E=6, K=2, H=288, I=64, seed=506), 3, "softmax", False),
 }
 
 
