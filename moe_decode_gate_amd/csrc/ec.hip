@@ -32,13 +32,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 16;          // rows per tile (M of the matrix instruction)
 constexpr int kStepK = 128;        // K per matrix instruction
-constexpr int kBatch = 4;          // K steps whose loads are issued together
+constexpr int kBatch = 2;          // K steps whose loads are issued together (down)
 constexpr int kMaxE = 1024, kMaxPairs = 4096, kMaxH = 8192, kMaxI = 8192;
 constexpr int kAlignThreads = 1024;
 constexpr int kGemmThreads = 256;  // down: 4 waves
 constexpr int kGuWaves = 8;        // gate/up: 8 waves splitting K
 constexpr int kGuThreads = 64 * kGuWaves;
-constexpr int kGuBatch = 1;        // gate/up K steps per wave whose loads are issued together
 constexpr int kGuCols = 32;        // intermediate columns per gate/up workgroup (one MX block)
 constexpr int kDnCols = 64;        // output columns per down workgroup (16 per wave)
 
@@ -124,6 +123,34 @@ __device__ __forceinline__ Frag load_frag(const uint8_t *codes, const uint8_t *s
     f.s = ks < n ? (int)scales[ks / 32] : 127;
     return f;
 }
+
+// The codes of one K step without branches: both halves loaded at offsets
+// clamped into the row, then zeroed past n (a branch around a load tends to
+// end in a wait for it, which would serialise the batch).
+struct Codes { u32x4 lo, hi; };
+
+__device__ __forceinline__ Codes load_codes(const uint8_t *codes, int n, int k0, int g) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int klo = k0 + 16 * g, khi = k0 + 64 + 16 * g;
+    Codes c;
+    c.lo = wd::ld16(codes + (klo < n ? klo : 0));
+    c.hi = wd::ld16(codes + (khi < n ? khi : 0));
+    c.lo = klo < n ? c.lo : z;
+    c.hi = khi < n ? c.hi : z;
+    return c;
+}
+
+// E8M0 bytes of blocks blk0 .. blk0+7 of a row of nb blocks (two K steps), byte
+// 127 past the row: one 8-byte load when the row starts on a 4-byte boundary and
+// holds all eight, else byte by byte.  Step i's byte for lane group g is byte 4i + g.
+__device__ __forceinline__ uint64_t load_scales8(const uint8_t *srow, int nb, int blk0) {
+    if ((nb & 3) == 0 && blk0 + 8 <= nb) return *reinterpret_cast<const uint64_t *>(srow + blk0);
+    uint64_t v = 0;
+    for (int c = 0; c < 8; ++c) v |= (uint64_t)(blk0 + c < nb ? srow[blk0 + c] : 127u) << (8 * c);
+    return v;
+}
+
+__device__ __forceinline__ int scale_of(uint64_t v, int i, int g) { return (int)((v >> (8 * (4 * i + g))) & 0xFFu); }
 
 // ---- stage 1: align / pad ----------------------------------------------------
 
@@ -224,8 +251,8 @@ struct GateUpArgs {
 };
 
 // Workgroup = (tile, 32 columns: the gate rows and the up rows of one MX
-// block of the intermediate).  The eight waves split the K steps (wave w takes
-// steps w, w+8, ...); their partial tiles are summed through LDS in wave
+// block of the intermediate).  The eight waves split the K steps into
+// contiguous ranges; their partial tiles are summed through LDS in wave
 // order, and the epilogue rounds the block to BF16 and then to MXFP8.
 __global__ void __launch_bounds__(kGuThreads) gate_up_kernel(GateUpArgs a) {
     __shared__ float part[kGuWaves][4][4][64];
@@ -249,22 +276,27 @@ __global__ void __launch_bounds__(kGuThreads) gate_up_kernel(GateUpArgs a) {
     v4f c[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) c[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // wave wv takes an even-length contiguous range of K steps, two at a time, so one
+    // 8-byte load brings a row's scale bytes for both
     const int nks = (H + kStepK - 1) / kStepK;
-    for (int s0 = wv; s0 < nks; s0 += kGuWaves * kGuBatch) {
-        Frag fx[kGuBatch], fw[kGuBatch][4];
+    const int per = 2 * ((nks + 2 * kGuWaves - 1) / (2 * kGuWaves));
+    const int s_hi = min(nks, (wv + 1) * per);
+    for (int s0 = wv * per; s0 < s_hi; s0 += 2) {
+        const uint64_t sx = load_scales8(xsr, nbh, 4 * s0);
+        uint64_t sw[4];
 #pragma unroll
-        for (int i = 0; i < kGuBatch; ++i) {
-            const int k0 = (s0 + kGuWaves * i) * kStepK;   // past H: all segments read as zero
-            fx[i] = load_frag(xc, xsr, H, k0, g);
+        for (int t = 0; t < 4; ++t) sw[t] = load_scales8(wsr[t], nbh, 4 * s0);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) fw[i][t] = load_frag(wc[t], wsr[t], H, k0, g);
-        }
+        for (int i = 0; i < 2; ++i) {
+            const int k0 = (s0 + i) * kStepK;          // past H: codes read as zero
+            const Codes fx = load_codes(xc, H, k0, g);
+            Codes fw[4];
 #pragma unroll
-        for (int i = 0; i < kGuBatch; ++i) {
-            const v8i ax = make_operand(fx[i].lo, fx[i].hi);
+            for (int t = 0; t < 4; ++t) fw[t] = load_codes(wc[t], H, k0, g);
+            const v8i ax = make_operand(fx.lo, fx.hi);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                c[t] = mfma_mx(ax, make_operand(fw[i][t].lo, fw[i][t].hi), c[t], fx[i].s, fw[i][t].s);
+                c[t] = mfma_mx(ax, make_operand(fw[t].lo, fw[t].hi), c[t], scale_of(sx, i, g), scale_of(sw[t], i, g));
         }
     }
 #pragma unroll
@@ -324,16 +356,24 @@ __global__ void __launch_bounds__(kGemmThreads) down_kernel(DownArgs a) {
     const uint8_t *wc = a.w + wrow * I, *wsr = a.ws + wrow * nbi;
     v4f c = {0.f, 0.f, 0.f, 0.f};
     const int nks = (I + kStepK - 1) / kStepK;
+    static_assert(kBatch % 2 == 0, "scale bytes come two K steps per load");
     for (int s0 = 0; s0 < nks; s0 += kBatch) {
-        Frag fa[kBatch], fw[kBatch];
+        Codes fa[kBatch], fw[kBatch];
+        uint64_t sa[kBatch / 2], sw[kBatch / 2];
+#pragma unroll
+        for (int i = 0; i < kBatch / 2; ++i) {
+            sa[i] = load_scales8(asr, nbi, 4 * (s0 + 2 * i));
+            sw[i] = load_scales8(wsr, nbi, 4 * (s0 + 2 * i));
+        }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
-            fa[i] = load_frag(ac, asr, I, (s0 + i) * kStepK, g);
-            fw[i] = load_frag(wc, wsr, I, (s0 + i) * kStepK, g);
+            fa[i] = load_codes(ac, I, (s0 + i) * kStepK, g);
+            fw[i] = load_codes(wc, I, (s0 + i) * kStepK, g);
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            c = mfma_mx(make_operand(fa[i].lo, fa[i].hi), make_operand(fw[i].lo, fw[i].hi), c, fa[i].s, fw[i].s);
+            c = mfma_mx(make_operand(fa[i].lo, fa[i].hi), make_operand(fw[i].lo, fw[i].hi), c,
+                        scale_of(sa[i / 2], i % 2, g), scale_of(sw[i / 2], i % 2, g));
     }
     // scatter: result rows 4g + q of column col0 + r
 #pragma unroll
