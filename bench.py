@@ -162,6 +162,36 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int):
     return res
 
 
+def one_shot_read(torch, wd, nbytes, copies=16, reps=16):
+    """The shortest kernel-own time (HIP events from the dispatch) to read nbytes
+    once, over one-pass launch shapes of the stream-read kernel (every lane's
+    loads issued together, no grid-stride loop), each launch on its own buffer
+    copy so that none finds the bytes in the MALL: the floor a kernel that
+    streams nbytes in one launch can reach on this GPU."""
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(wd.stream_blocks(), dtype=torch.int32, device="cuda")
+    best, best_cfg = float("inf"), None
+    for unroll in (1, 2, 4, 8):
+        blocks = -(-(nbytes // 16) // (256 * unroll))
+        if blocks > wd.stream_blocks():
+            continue
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in evs:
+            for x in e:
+                x.record()
+        torch.cuda.synchronize()
+        wd.gpu_sleep(20000)
+        for r in range(reps):
+            wd.stream_read(bufs[r % copies], sink, blocks=blocks, unroll=unroll,
+                           start_event=evs[r][0].cuda_event, stop_event=evs[r][1].cuda_event)
+        torch.cuda.synchronize()
+        us = float(np.median([evs[r][0].elapsed_time(evs[r][1]) for r in range(2, reps)])) * 1e3
+        if us < best:
+            best, best_cfg = us, (unroll, blocks)
+    del bufs
+    return best, best_cfg
+
+
 def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64), layers=48, reps=10):
     """A decode step through `layers` MoE layers of the layer's shape: distinct
     device copies of the weights (about 30 GB for 48 layers), per-layer routing
@@ -437,6 +467,12 @@ def main():
 
     peak, peak_cfg, copy_bw = hbm_read_peak(torch, wd)
     eprint(f"[bench] contiguous-read peak {peak:.0f} GB/s (unroll, blocks = {peak_cfg}); copy {copy_bw:.0f} GB/s")
+    gu_b1_bytes = 8 * (2 * spec.I * spec.H + 2 * spec.I * (spec.H // 32))      # gate/up bytes of 8 experts
+    dn_b1_bytes = 8 * (spec.H * spec.I + spec.H * (spec.I // 32))              # down bytes of 8 experts
+    floor_us, floor_cfg = one_shot_read(torch, wd, gu_b1_bytes)
+    floor_dn_us, floor_dn_cfg = one_shot_read(torch, wd, dn_b1_bytes)
+    eprint(f"[bench] one-shot read of {gu_b1_bytes} B: {floor_us:.2f} us (unroll, blocks = {floor_cfg}); "
+           f"of {dn_b1_bytes} B: {floor_dn_us:.2f} us ({floor_dn_cfg})")
 
     steps, warmup = args.steps, args.warmup
     copies1 = args.copies or 16
@@ -445,7 +481,9 @@ def main():
     eprint(f"[bench] B=1: {json.dumps(r1)}")
     import oracle
     cos1, err1 = sampled_parity(oracle, L, w1, [0, steps // 2, steps - 1])
-    r1.update(parity_cos_min=cos1, parity_max_abs_err=err1)
+    r1.update(parity_cos_min=cos1, parity_max_abs_err=err1,
+              gate_up_over_one_shot_read=r1["gate_up_us"] / floor_us,
+              down_over_one_shot_read=r1["down_us"] / floor_dn_us)
     del w1
     torch.cuda.empty_cache()
 
@@ -480,6 +518,12 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS, "kernel": "gate_up",
                      "traffic": load_traffic("gate_up_qwen3_b1")},
         "hbm_read_peak_GBps": peak,
+        "one_shot_read": {"gate_up_bytes": gu_b1_bytes, "gate_up_us": floor_us,
+                          "gate_up_GBps": gu_b1_bytes / (floor_us * 1e-6) / 1e9, "gate_up_unroll_blocks": floor_cfg,
+                          "down_bytes": dn_b1_bytes, "down_us": floor_dn_us,
+                          "down_GBps": dn_b1_bytes / (floor_dn_us * 1e-6) / 1e9, "down_unroll_blocks": floor_dn_cfg,
+                          "note": "a plain read of the B=1 kernels' bytes in one launch (kernel-own events, "
+                                  "distinct buffers): the floor for a one-launch stream of that size"},
         "hbm_copy_GBps": copy_bw,
         "layer_GBps": r1["layer_GBps_graph"],
         "frac_of_8TBps": r1["layer_GBps_graph"] / PEAK_HBM_GBPS,

@@ -189,8 +189,10 @@ int wd_dequant_probe(float *out, void *stream);
  * `buf` with 16-byte loads in a grid-stride loop, `unroll` (1, 2, 4 or 8)
  * independent loads in flight per lane, and keeps every load live through a
  * conditional write to sink[0 .. blocks).  blocks <= 0 picks a default; sink
- * must hold wd_stream_blocks() uint32. */
-int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int unroll, void *stream);
+ * must hold wd_stream_blocks() uint32.  start_event / stop_event (hipEvent_t,
+ * may be NULL) receive the kernel's own start and end, as in wd_launch. */
+int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int unroll, void *start_event,
+                   void *stop_event, void *stream);
 int wd_stream_blocks(void);
 
 /* Contiguous copy with 16-byte loads and stores (bytes a multiple of 16). */

@@ -68,7 +68,7 @@ _sig = {
     "wd_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "wd_status_string": (C.c_char_p, [_I]),
     "wd_dequant_probe": (_I, [_P, _P]),
-    "wd_stream_read": (_I, [_P, _S, _P, _I, _I, _P]),
+    "wd_stream_read": (_I, [_P, _S, _P, _I, _I, _P, _P, _P]),
     "wd_stream_blocks": (_I, []),
     "wd_stream_copy": (_I, [_P, _P, _S, _I, _P]),
     "wd_gpu_sleep": (_I, [_I, _P]),
@@ -228,9 +228,12 @@ def stream_blocks() -> int:
     return _lib.wd_stream_blocks()
 
 
-def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0, unroll: int = 4, stream=None):
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, blocks: int = 0, unroll: int = 4, start_event=None,
+                stop_event=None, stream=None):
+    """start_event / stop_event: raw hipEvent_t handles that receive the kernel's own start and end."""
     nbytes = buf.numel() * buf.element_size()
-    _check(_lib.wd_stream_read(_ptr(buf), nbytes, _ptr(sink), blocks, unroll, _stream(stream)), "wd_stream_read")
+    _check(_lib.wd_stream_read(_ptr(buf), nbytes, _ptr(sink), blocks, unroll, start_event, stop_event,
+                               _stream(stream)), "wd_stream_read")
 
 
 def stream_copy(dst: torch.Tensor, src: torch.Tensor, blocks: int = 0, stream=None):

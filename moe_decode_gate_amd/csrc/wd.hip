@@ -372,7 +372,8 @@ int wd_dequant_probe(float *out, void *stream) {
 
 int wd_stream_blocks(void) { return 256 * 32; }
 
-int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int unroll, void *stream) {
+int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, int unroll, void *start_event,
+                   void *stop_event, void *stream) {
     if (!buf || !sink) return WD_ERR_NULL;
     if (bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return WD_ERR_ALIGN;
     if (blocks <= 0) blocks = wd_stream_blocks();
@@ -387,8 +388,12 @@ int wd_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks, in
     }
     int rc = check_device();
     if (rc) return rc;
-    hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
-                       static_cast<const wd::u32x4 *>(buf), bytes / 16, sink, 0x9E3779B9u);
+    const wd::u32x4 *b16 = static_cast<const wd::u32x4 *>(buf);
+    if (start_event || stop_event)
+        hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (hipEvent_t)start_event,
+                              (hipEvent_t)stop_event, 0, b16, bytes / 16, sink, 0x9E3779B9u);
+    else
+        hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, (hipStream_t)stream, b16, bytes / 16, sink, 0x9E3779B9u);
     return launched();
 }
 

@@ -97,9 +97,9 @@ def test_lanes_per_row_limits():
 def test_helpers_reject_bad_arguments():
     assert lib.wd_dequant_probe(None, None) == -1
     assert lib.wd_dequant_probe(A + 4, None) == -3
-    assert lib.wd_stream_read(A, 15, A, 0, 4, None) == -3
-    assert lib.wd_stream_read(A, 16, A, lib.wd_stream_blocks() + 1, 4, None) == -7
-    assert lib.wd_stream_read(A, 16, A, 0, 3, None) == -7
+    assert lib.wd_stream_read(A, 15, A, 0, 4, None, None, None) == -3
+    assert lib.wd_stream_read(A, 16, A, lib.wd_stream_blocks() + 1, 4, None, None, None) == -7
+    assert lib.wd_stream_read(A, 16, A, 0, 3, None, None, None) == -7
     assert lib.wd_stream_copy(None, A, 16, 0, None) == -1
     assert lib.wd_gpu_sleep(-1, None) == -7
 
