@@ -104,7 +104,7 @@ enum wd_status {
  *                    accumulation in the matrix core's summation order
  *                    (rows_per_wave 1, lanes_per_row 64, math 2,
  *                    weight_loads 1; waves_per_block and order apply as for
- *                    the other forms).  Default: 3 when B >= 32 and none of
+ *                    the other forms).  Default: 3 when B >= 24 and none of
  *                    rows_per_wave, lanes_per_row, math, weight_loads is set,
  *                    else 1.  (down: 1)
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are

@@ -54,19 +54,20 @@ int check_dims(int B, int K, int E, int H, int I) {
 // for B in {1, 2, 4, 8, 16, 32, 64}:
 //   gate/up, B <= 4: one row per 64-lane wave, BF16-pair dot products,
 //          non-temporal weight loads (no row is read twice), hardware order;
-//   gate/up, B 5..31: 32 lanes per row, 4 rows per lane group (8 per wave),
+//   gate/up, B 5..23: 32 lanes per row, 4 rows per lane group (8 per wave),
 //          row-block-major order with XCD-contiguous numbering, so the tokens
 //          that share an expert row read it from the same L2 while resident;
-//   gate/up, B >= 32: the expert form on the matrix cores (one wave per
-//          expert row block; 80-90 us at B = 32-64 against 85-135 us);
+//   gate/up, B >= 24: the expert form on the matrix cores (one wave per
+//          expert row block; equal at B = 24, 70 against 85 us at B = 32 and
+//          75 against 136 us at B = 64);
 //   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
 //   down, B 3..5: 4 rows per wave, FP32 math; B >= 6: 8 rows per wave.
 int resolve(const wd_launch *in, int B, bool down, wd_launch *out) {
     wd_launch c = in ? *in : wd_launch{};
     const bool batch = down ? B >= 3 : B >= 5;
-    // B >= 32: gate/up in the expert form on the matrix cores, whose weight stream
+    // B >= 24: gate/up in the expert form on the matrix cores, whose weight stream
     // is read once per expert however many tokens share it
-    if (c.form == 0) c.form = (!down && B >= 32 && c.rows_per_wave == 0 && c.lanes_per_row == 0 &&
+    if (c.form == 0) c.form = (!down && B >= 24 && c.rows_per_wave == 0 && c.lanes_per_row == 0 &&
                                c.math == 0 && c.weight_loads == 0) ? 3 : 1;
     if (c.form == 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
     if (c.rows_per_wave == 0)

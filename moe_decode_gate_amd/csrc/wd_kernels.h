@@ -316,42 +316,50 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 struct MfmaBatch {                      // one wave's loads for kMfmaSteps 64-element steps
-    u32x4 wg[kMfmaSteps], wu[kMfmaSteps];
-    uint64_t sg, su;                    // the row's 2 * kMfmaSteps E8M0 bytes of these steps
+    u32x4 v[8];                         // codes, coalesced: instruction j holds 4 rows x 256 B
+    uint64_t sg, su;                    // the lane's row's 2 * kMfmaSteps E8M0 bytes of these steps
 };
-static_assert(kMfmaSteps == 4, "one 8-byte scale load covers a batch");
+static_assert(kMfmaSteps == 4, "one 8-byte scale load and 256 bytes per row cover a batch");
 
 __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
+    // per wave: the batch's 16 gate and 16 up rows x 256 bytes, 16-byte slots XOR-swizzled by row
+    __shared__ u32x4 tile[4][2][16][16];
     const int lane = threadIdx.x & 63;
     const int unit = logical_wave(a);
     if (unit >= a.nwaves) return;
     const int e = unit / a.nrowblk, jb = unit % a.nrowblk;
     const int BK = a.B * a.K, H = a.H, I = a.I;
     const int r16 = lane & 15, q = lane >> 4;
+    u32x4(*wt)[16][16] = tile[threadIdx.x >> 6];
 
     const size_t nbr = (size_t)(H >> 5);
     const size_t grow = (size_t)e * 2 * I + (size_t)jb * 16 + r16;
-    const uint8_t *pg = a.w + grow * (size_t)H;
-    const uint8_t *pu = pg + (size_t)I * H;
     const uint8_t *sg = a.s + grow * nbr;
     const uint8_t *su = sg + (size_t)I * nbr;
     const int s_lo = 0, s_hi = (H + 63) >> 6;        // 64-element steps
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    // Weight and scale loads are unconditional (offsets outside the wave's range are
-    // clamped to its start; the selects in the compute step zero them), so no branch,
-    // and no wait inside one, separates them.
+    // Weight and scale loads are unconditional (offsets past H are clamped; the selects
+    // in the compute step zero what they brought), so no branch, and no wait inside one,
+    // separates them.
     // The E8M0 bytes of a batch (blocks 2 s0 .. 2 s0 + 7 of the lane's row) come in
     // one 8-byte load when the row holds them all and rows start on 4-byte
     // boundaries (H a multiple of 128; always for H a multiple of 256), else byte
     // by byte.
+    // Codes come coalesced: instruction j reads rows 4 (j % 4) + l / 16 of the gate
+    // (j < 4) or up (j >= 4) block, 16 bytes per lane, the 16 lanes of a row covering its
+    // 256 bytes of the batch in slot order p = l % 16 holding segment p ^ row (the swizzle
+    // that makes the operand-layout reads from LDS conflict-free).
+    const uint8_t *pg0 = a.w + ((size_t)e * 2 * I + (size_t)jb * 16) * (size_t)H;
+    const uint8_t *pu0 = pg0 + (size_t)I * H;
+    const int wrow = lane >> 4, wslot = lane & 15;
     auto load_batch = [&](int s0, MfmaBatch &bt) {
 #pragma unroll
-        for (int i = 0; i < kMfmaSteps; ++i) {
-            const int k = 64 * (s0 + i) + 16 * q;
-            const int kc = (s0 + i < s_hi && k < H) ? k : 64 * s_lo;
-            bt.wg[i] = ld16(pg + kc);
-            bt.wu[i] = ld16(pu + kc);
+        for (int j = 0; j < 8; ++j) {
+            const int r = 4 * (j & 3) + wrow;
+            const int k = 64 * s0 + 16 * (wslot ^ r);
+            const uint8_t *base = (j < 4 ? pg0 : pu0) + (size_t)r * H;
+            bt.v[j] = ld16(base + (k < H ? k : 0));       // past H: clamped, zeroed when read
         }
         if ((nbr & 3) == 0 && 2 * s0 + 8 <= (int)nbr) {      // dword-aligned: row bases are multiples of 4
             bt.sg = *reinterpret_cast<const uint64_t *>(sg + 2 * s0);
@@ -422,6 +430,11 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
 
         f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = cg;
         for (int s0 = s_lo; s0 < s_hi; s0 += kMfmaSteps) {
+            // the batch's codes into the wave's LDS tile (LDS operations of one wave complete
+            // in order, so the previous batch's reads are done)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wt[j >> 2][4 * (j & 3) + wrow][wslot] = cur.v[j];
+            const uint64_t sgb = cur.sg, sub = cur.su;       // this batch's scale bytes
             u32x4 x0[kMfmaSteps], x1[kMfmaSteps];
 #pragma unroll
             for (int i = 0; i < kMfmaSteps; ++i) {
@@ -434,19 +447,20 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
                     x1[i] = ld16(xr + kc + 8);
                 }
             }
-            // prefetch: the next batch, or this wave's first batch again for a further group
-            MfmaBatch nxt;
+            // prefetch into the same registers (their codes are in LDS now): the next batch, or
+            // this wave's first batch again for a further group
             const bool more = s0 + kMfmaSteps < s_hi;
-            if (more || cnt == 16) load_batch(more ? s0 + kMfmaSteps : s_lo, nxt);
+            if (more || cnt == 16) load_batch(more ? s0 + kMfmaSteps : s_lo, cur);
 #pragma unroll
             for (int i = 0; i < kMfmaSteps; ++i) {
                 const int k = 64 * (s0 + i) + 16 * q;
                 const bool ok = s0 + i < s_hi && k < H;
                 const bool xo = ok && live;
                 const int sh = 8 * (2 * i + (q >> 1));      // byte of block 2 (s0 + i) + q / 2
-                const uint32_t bg = (uint32_t)(cur.sg >> sh) & 0xFFu, bu = (uint32_t)(cur.su >> sh) & 0xFFu;
+                const uint32_t bg = (uint32_t)(sgb >> sh) & 0xFFu, bu = (uint32_t)(sub >> sh) & 0xFFu;
                 const float fg = e8m0_operand(ok ? bg : 127u), fu = e8m0_operand(ok ? bu : 127u);
-                const u32x4 wgi = ok ? cur.wg[i] : zero, wui = ok ? cur.wu[i] : zero;
+                const int slot = (4 * i + q) ^ r16;         // segment 4 i + q of row r16
+                const u32x4 wgi = ok ? wt[0][r16][slot] : zero, wui = ok ? wt[1][r16][slot] : zero;
                 const u32x4 xa = xo ? x0[i] : zero, xb = xo ? x1[i] : zero;
                 uint32_t gw[8], uw[8];
 #pragma unroll
@@ -461,7 +475,6 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
                 cu = mfma_bf16(u0, xa, cu);
                 cu = mfma_bf16(u1, xb, cu);
             }
-            if (more || cnt == 16) cur = nxt;
         }
         if (live) {
             uint32_t packed[2];
