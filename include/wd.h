@@ -77,7 +77,8 @@ enum wd_status {
  *   rows_per_wave    1, 2, 4 (or 8 for down): rows each lane group computes in
  *                    turn (a wave computes rows_per_wave * 64 / lanes_per_row
  *                    rows)
- *   waves_per_block  1..4: waves per workgroup
+ *   waves_per_block  1..4: waves per workgroup (down on the matrix cores:
+ *                    8 or 16)
  *   order            1 = row-block major (the waves of all tokens and slots
  *                    for one block of rows are adjacent, so tokens that share
  *                    an expert re-read its rows while they are in cache);
@@ -106,7 +107,21 @@ enum wd_status {
  *                    weight_loads 1; waves_per_block and order apply as for
  *                    the other forms).  Default: 3 when B >= 24 and none of
  *                    rows_per_wave, lanes_per_row, math, weight_loads is set,
- *                    else 1.  (down: 1)
+ *                    else 1.
+ *                    down: 1 = one wave per (token, block of output dims);
+ *                    3 = one workgroup of 8 or 16 waves (waves_per_block)
+ *                    per block of 16 output dims serving every token: each
+ *                    wave takes every 8th (16th) routed expert, forms the
+ *                    16 x slots tile on the BF16 matrix cores (weights
+ *                    converted exactly, act as stored, FP32 accumulation),
+ *                    folds each slot's router weight into its token's FP32
+ *                    accumulator, and the workgroup adds its waves'
+ *                    accumulators in wave order (rows_per_wave 1,
+ *                    lanes_per_row 64, math 2, weight_loads 1; B <= 64, or
+ *                    32 with 16 waves; B * K <= 512; E <= 1024).  Default: 3
+ *                    when 56 <= B <= 64, B * K <= 512, E <= 1024 and none of
+ *                    rows_per_wave, lanes_per_row, math, weight_loads,
+ *                    waves_per_block is set, else 1.
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
  *                    streamed once and not kept in the caches)
  *   start_event,     optional hipEvent_t handles (created by the caller); when
@@ -144,7 +159,9 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
  * "Down Kernel"): one wave per (token b, output dim h).  The wave walks the K
  * routed experts' rows Wd[e_k, h, :], folds topk_w[b,k] into one FP32
  * accumulator, reduces across its 64 lanes with DPP row operations and one
- * lane read (no LDS) and writes out[b,h] = BF16(acc). */
+ * lane read (no LDS) and writes out[b,h] = BF16(acc).  From B = 56 the
+ * default is the expert form on the matrix cores (wd_launch.form 3), which
+ * reads each Wd row block once for all the tokens routed to its expert. */
 int wd_down(const uint16_t *act, const int32_t *topk_ids, const float *topk_w,
             const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
             int B, int K, int E, int H, int I, void *stream);

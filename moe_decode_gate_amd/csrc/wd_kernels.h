@@ -569,6 +569,321 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Down, expert form on the matrix cores: one workgroup of W waves per block of
+// 16 output dims h, serving every token of the batch.
+//
+// Wave w takes the experts e = w, w + W, w + 2W, ... that at least one slot is
+// routed to.  For each it forms, G slots at a time (slot order), the tile
+// P[h][c] = sum_i Wd[e][h][i] * act[slot c][i] with v_mfma_f32_16x16x32_bf16
+// (weight codes converted exactly to BF16, act as stored, FP32 accumulation;
+// A = the 16 weight rows, B = the slots' act rows), and folds the router
+// weight in, acc[token][h] = fma(w_slot, P[h][c], acc[token][h]), into FP32
+// accumulators in LDS that belong to the wave (the token form's routing-weight
+// fold, with the expert's dot products done once for all its slots).  At the
+// end the workgroup adds its waves' accumulators in wave order and writes
+// out[b][h] = BF16(sum).  Each output is owned by one workgroup: no atomic, no
+// buffer besides the output.  Every Wd byte is read once per call.
+//
+// At the start each wave lists its routed experts and their slots (slot
+// order) in LDS.  Its work is then a sequence of tasks (expert, group of up to
+// G slots, batch of 4 64-element steps).  The loads of a task (the 16 rows'
+// codes, coalesced as in the matrix-core gate/up; the rows' E8M0 bytes; the
+// group's act, coalesced, two slots per instruction) go to one of three
+// register sets (two with 16 waves) that many tasks ahead of the compute; a
+// task's compute first copies its set into the wave's LDS tiles (codes
+// XOR-swizzled by row, act rows padded to start 4 banks apart), refills the
+// set, then reads its operands from LDS.  Router weights come through scalar
+// loads, whose waits do not count the vector loads in flight.  The task state
+// is wave-uniform (scalar registers), and every refill issues the same loads
+// in one straight block, so each wait names exactly the set it needs.
+// Limits: B <= 64 (32 with 16 waves) and B * K <= 512 (the wave keeps every
+// slot's id in registers, 8 per lane), E <= 1024.
+// ---------------------------------------------------------------------------
+constexpr int kDnMfmaMaxB = 64;
+constexpr int kDnMfmaMaxSlots = 512;
+constexpr int kDnMfmaMaxE = 1024;
+constexpr int kDnIdRegs = kDnMfmaMaxSlots / 64;
+
+template <int G>
+struct DownSet {
+    u32x4 v[4];        // codes: instruction j holds rows 4 j + l / 16, 16-byte slot l % 16 = segment (l % 16) ^ row
+    uint64_t sc;       // the E8M0 bytes of the lane's row l % 16 for the batch's 8 blocks
+    u32x4 x[G / 2];    // act: instruction j holds group slot 2 j + l / 32, elements 8 (l % 32) .. + 7 of the batch
+};
+
+struct DownCursor {    // position in a wave's task sequence
+    int x, grp, sb;    // index in the wave's expert list, group of the expert's slots, batch
+    int e, start, cnt; // that expert, its first entry in the wave's slot list, its slot count
+};
+
+template <int W, int G, bool SC8>
+__global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
+    constexpr int kXRow = 33;                          // u32x4 per act row in LDS: 256 bf16 + 16 bytes of padding
+    constexpr int kMaxExp = (kDnMfmaMaxE + W - 1) / W; // experts one wave can be given
+    constexpr int kMaxB = W >= 16 ? 32 : kDnMfmaMaxB;  // tokens the per-wave accumulators hold (LDS)
+    __shared__ u32x4 tile[W][16][16];                  // per wave: 16 rows x 256 bytes of codes, swizzled
+    __shared__ u32x4 xtile[W][G][kXRow];               // per wave: the group's act for the batch
+    __shared__ f32x4 accs[W][kMaxB][4];                // per wave: [token][rows 4 q .. 4 q + 3]
+    __shared__ int16_t lslot[W][kDnMfmaMaxSlots];      // per wave: slots of its experts, expert by expert
+    __shared__ uint32_t lexp[W][kMaxExp];              // per wave: e | first entry << 10 | count << 20
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
+    const int hb = (int)blockIdx.x;
+    const int BK = a.B * a.K, H = a.H, I = a.I, E = a.E;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int wrow = lane >> 4, wslot = lane & 15;
+    u32x4(*wt)[16] = tile[wv];
+    u32x4(*xt)[kXRow] = xtile[wv];
+    const int nbr = I >> 5;
+    const int s_hi = (I + 63) >> 6;                    // 64-element steps
+    const int s_full = I >> 6;                         // steps with all 64 elements inside the row
+    const int nsb = (s_hi + kMfmaSteps - 1) / kMfmaSteps;   // batches per expert
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    int idv[kDnIdRegs];                                // id of slot 64 u + lane
+#pragma unroll
+    for (int u = 0; u < kDnIdRegs; ++u) {
+        const int sl = 64 * u + lane;
+        idv[u] = sl < BK ? a.ids[sl] : -1;
+    }
+    for (int t = lane; t < a.B * 4; t += 64) accs[wv][t >> 2][t & 3] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
+    uint64_t bad_tok = 0;
+#pragma unroll
+    for (int u = 0; u < kDnIdRegs; ++u) {
+        uint64_t m = __builtin_amdgcn_ballot_w64(64 * u + lane < BK && (unsigned)idv[u] >= (unsigned)E);
+        while (m) {
+            const int sl = 64 * u + (int)__builtin_ctzll(m);
+            m &= m - 1;
+            bad_tok |= 1ull << (sl / a.K);
+        }
+    }
+
+    // the wave's experts and their slots, in expert then slot order
+    int nx = 0;
+    {
+        int ns = 0;
+        for (int e = wv; e < E; e += W) {
+            bool any = false;
+#pragma unroll
+            for (int u = 0; u < kDnIdRegs; ++u) any |= idv[u] == e;
+            if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+            const int first = ns;
+#pragma unroll
+            for (int u = 0; u < kDnIdRegs; ++u) {
+                const bool m = idv[u] == e;
+                const uint64_t bm = __builtin_amdgcn_ballot_w64(m);
+                const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+                if (m) lslot[wv][ns + rank] = (int16_t)(64 * u + lane);
+                ns += __builtin_popcountll(bm);
+            }
+            if (lane == 0) lexp[wv][nx] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)(ns - first) << 20;
+            ++nx;
+        }
+    }
+
+    // ---- task sequence ----
+    auto fetch = [&](DownCursor &cu) {                 // the expert at list index x
+        if (cu.x < nx) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lexp[wv][cu.x]);
+            cu.e = (int)(v & 1023u);
+            cu.start = (int)((v >> 10) & 1023u);
+            cu.cnt = (int)(v >> 20);
+        }
+    };
+    auto advance = [&](DownCursor &cu) {
+        if (++cu.sb < nsb) return;
+        cu.sb = 0;
+        if (++cu.grp * G < cu.cnt) return;
+        cu.grp = 0;
+        ++cu.x;
+        fetch(cu);
+    };
+
+    // per-lane offsets that do not change from task to task
+    int coff[4];                                       // code instruction j: row 4 j + l / 16, segment (l % 16) ^ row
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * j + wrow;
+        coff[j] = r * I + 16 * (wslot ^ r);
+    }
+    const int soff = r16 * nbr;                        // the lane's row's E8M0 bytes
+
+    // ---- load side: three tasks ahead ----
+    DownCursor ld{0, 0, 0, 0, 0, 0};
+    fetch(ld);
+    DownCursor cp = ld;
+    int xo[G / 2];                                     // act row offset (elements) of instruction j for this lane
+#pragma unroll
+    for (int j = 0; j < G / 2; ++j) xo[j] = 0;
+    // Every call issues the same loads, in one straight block, so the wait before a set is
+    // used counts exactly the younger sets' loads.  Past the end of the sequence the cursor
+    // keeps naming the last expert (and expert 0 for a wave with none), so the loads stay
+    // in bounds; their data is never used.
+    auto issue = [&](DownSet<G> &st) {
+        if (ld.sb == 0) {                              // a new group: this lane's act rows
+            const int gn = min(G, ld.cnt - ld.grp * G);
+            const int base = ld.start + ld.grp * G;
+#pragma unroll
+            for (int j = 0; j < G / 2; ++j) {
+                const int col = 2 * j + (lane >> 5);
+                xo[j] = col < gn ? (int)lslot[wv][base + col] * I : 0;
+            }
+        }
+        const int e = ld.e;
+        const int s0 = ld.sb * kMfmaSteps;
+        const uint8_t *pw = a.w + ((size_t)e * H + (size_t)hb * 16) * (size_t)I + 64 * s0;
+        const int lim = I - 64 * s0;                   // bytes of each row left from this batch on
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int seg = 16 * (wslot ^ (4 * j + wrow));
+            st.v[j] = ld16(pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0));   // past I: the row's start, zeroed when read
+        }
+        const uint8_t *ps = a.s + ((size_t)e * H + (size_t)hb * 16) * (size_t)nbr + soff;
+        if constexpr (SC8) {       // rows of E8M0 bytes start on 4-byte boundaries: one 8-byte load
+            st.sc = *reinterpret_cast<const uint64_t *>(ps + (2 * s0 + 8 <= nbr ? 2 * s0 : 0));
+        } else {
+            st.sc = 0;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) st.sc |= (uint64_t)ps[2 * s0 + b < nbr ? 2 * s0 + b : 0] << (8 * b);
+        }
+        const int kx = 64 * s0 + 8 * (lane & 31);
+        const int kxc = kx < I ? kx : 0;
+#pragma unroll
+        for (int j = 0; j < G / 2; ++j) st.x[j] = ld16(a.act_in + xo[j] + kxc);
+        advance(ld);
+    };
+
+    // ---- compute side ----
+    const __attribute__((address_space(4))) float *twc = (const __attribute__((address_space(4))) float *)a.tw;
+    int slot = 0;
+    bool live = false;
+    float wk = 0.f;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    const int xr = r16 < G ? r16 : 0;
+    // One task: its data into the wave's LDS tiles, the set refilled with the task three
+    // ahead, then (for a real task) the 4 steps on the matrix cores and, at a group's last
+    // batch, the fold.  Past the end of the sequence only the first two run, so the loop
+    // below has no exit between its three calls and each set keeps its registers.
+    auto process = [&](DownSet<G> &st) {
+        const bool real = cp.x < nx;
+        if (real && cp.sb == 0) {
+            const int gn = min(G, cp.cnt - cp.grp * G);
+            live = r16 < gn;
+            slot = live ? (int)lslot[wv][cp.start + cp.grp * G + r16] : 0;
+            wk = 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {              // scalar loads: their waits do not count vector loads
+                const float t = twc[__builtin_amdgcn_readlane(slot, g)];
+                wk = r16 == g ? t : wk;
+            }
+            c = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // the task's data into the wave's LDS tiles (the wave's reads of the previous task are
+        // complete: LDS operations of one wave execute in order)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wt[4 * j + wrow][wslot] = st.v[j];
+#pragma unroll
+        for (int j = 0; j < G / 2; ++j) xt[2 * j + (lane >> 5)][lane & 31] = st.x[j];
+        const uint64_t scb = st.sc;
+        const int s0 = cp.sb * kMfmaSteps;
+        issue(st);                                     // refill the set with the task three ahead
+        if (!real) return;
+        // Columns past the group's slots hold stale act; each result column depends only
+        // on its own act column, and those columns are never folded.
+        if (s0 + kMfmaSteps <= s_full) {               // all 4 steps inside the row
+            // with registers to spare, every LDS read of the task first, so their latencies overlap
+            constexpr int kPre = W < 16 ? kMfmaSteps : 1;
+            u32x4 wqs[kPre], xas[kPre], xbs[kPre];
+            if constexpr (W < 16) {
+#pragma unroll
+                for (int i = 0; i < kMfmaSteps; ++i) {
+                    wqs[i] = wt[r16][(4 * i + q) ^ r16];
+                    xas[i] = xt[xr][8 * i + 2 * q];
+                    xbs[i] = xt[xr][8 * i + 2 * q + 1];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < kMfmaSteps; ++i) {
+                const float f = e8m0_operand((uint32_t)(scb >> (8 * (2 * i + (q >> 1)))) & 0xFFu);
+                const int ip = W < 16 ? i : 0;
+                if constexpr (W >= 16) {
+                    wqs[0] = wt[r16][(4 * i + q) ^ r16];    // segment 4 i + q of row r16
+                    xas[0] = xt[xr][8 * i + 2 * q];         // elements 64 i + 16 q .. + 7
+                    xbs[0] = xt[xr][8 * i + 2 * q + 1];     // .. + 8 .. + 15
+                }
+                const u32x4 wq = wqs[ip], xa = xas[ip], xb = xbs[ip];
+                uint32_t ww[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) mx_word_bf16(wq[d], f, ww[2 * d], ww[2 * d + 1]);
+                const u32x4 w0 = {ww[0], ww[1], ww[2], ww[3]}, w1 = {ww[4], ww[5], ww[6], ww[7]};
+                c = mfma_bf16(w0, xa, c);
+                c = mfma_bf16(w1, xb, c);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMfmaSteps; ++i) {
+                const int k = 64 * (s0 + i) + 16 * q;
+                const bool ok = s0 + i < s_hi && k < I;
+                const uint32_t bs = (uint32_t)(scb >> (8 * (2 * i + (q >> 1)))) & 0xFFu;
+                const float f = e8m0_operand(ok ? bs : 127u);
+                const u32x4 wq = ok ? wt[r16][(4 * i + q) ^ r16] : zero;
+                const u32x4 xa = ok ? xt[xr][8 * i + 2 * q] : zero;
+                const u32x4 xb = ok ? xt[xr][8 * i + 2 * q + 1] : zero;
+                uint32_t ww[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) mx_word_bf16(wq[d], f, ww[2 * d], ww[2 * d + 1]);
+                const u32x4 w0 = {ww[0], ww[1], ww[2], ww[3]}, w1 = {ww[4], ww[5], ww[6], ww[7]};
+                c = mfma_bf16(w0, xa, c);
+                c = mfma_bf16(w1, xb, c);
+            }
+        }
+        if (cp.sb == nsb - 1) {
+            // lane (column r16, quad q) holds P[4 q + j][r16]: fold into the slot's token
+            const int tok = live ? slot / a.K : -1;
+            const int tprev = __shfl(tok, (lane & 48) | ((r16 + 15) & 15));
+            const bool dup = live && r16 > 0 && tprev == tok;     // same token as the previous column
+            f32x4 *dst = &accs[wv][live ? tok : 0][q];
+            auto fold = [&]() {
+                f32x4 v = *dst;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(wk, c[j], v[j]);
+                *dst = v;
+            };
+            if (__builtin_amdgcn_ballot_w64(dup) == 0) {
+                if (live) fold();
+            } else {                                   // a token routed to the expert twice: columns in order
+                for (int col = 0; col < G; ++col)
+                    if (r16 == col && live) fold();
+            }
+        }
+        advance(cp);
+    };
+
+    DownSet<G> sa, sb, sc;
+    issue(sa);
+    issue(sb);
+    if constexpr (W < 16) issue(sc);
+    while (cp.x < nx) {
+        process(sa);
+        process(sb);
+        if constexpr (W < 16) process(sc);     // 16 waves: two sets (register budget 128)
+    }
+
+    __syncthreads();
+    for (int t = (int)threadIdx.x; t < a.B * 16; t += 64 * W) {
+        const int b = t >> 4, r = t & 15;
+        float y = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) y += accs[w][b][r >> 2][r & 3];
+        if ((bad_tok >> b) & 1) y = __builtin_nanf("");
+        a.out[(size_t)b * H + (size_t)hb * 16 + r] = to_bf16(y);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Router: top-k gating ahead of the layer.  One wave per token; lane l holds
 // logits l + 64 r (r < RPL).  K rounds: each finds the largest remaining logit
 // (wave max) and, among lanes holding that value, the lowest expert index

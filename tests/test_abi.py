@@ -189,4 +189,24 @@ def test_matrix_core_form_limits():
     assert gux(form=3, math=1) == -7
     assert gux(form=3, weight_loads=2) == -7
     assert gux(form=4) == -7
-    assert lib.wd_down_ex(A, A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(wd.Launch(form=3)), None) == -7
+
+    # down on the matrix cores: 8 or 16 waves per workgroup, B <= 64 (32 with 16 waves),
+    # B * K <= 512, E <= 1024; accepted configurations get as far as the device check (-5 here)
+    def dnx(B=1, K=8, E=128, **kw):
+        return lib.wd_down_ex(A, A, A, A, A, A, B, K, E, 2048, 768, C.byref(wd.Launch(**kw)), None)
+
+    assert dnx(form=3) == -5
+    assert dnx(B=64, form=3) == -5
+    assert dnx(B=32, form=3, waves_per_block=16) == -5
+    assert dnx(B=33, form=3, waves_per_block=16) == -7
+    assert dnx(B=65, form=3) == -7
+    assert dnx(B=40, K=16, form=3) == -7           # 640 slots
+    assert dnx(E=1025, K=8, form=3) == -7
+    assert dnx(form=3, waves_per_block=4) == -7
+    assert dnx(form=3, rows_per_wave=2) == -7
+    assert dnx(form=3, math=1) == -7
+    assert dnx(form=3, lanes_per_row=32) == -7
+    assert dnx(form=3, weight_loads=2) == -7
+    assert dnx(form=2) == -7
+    # the default picks it only where it applies; a tuned field keeps the token form
+    assert dnx(B=64, E=2048) == -5 and dnx(B=64, K=16) == -5 and dnx(B=64, waves_per_block=2) == -5

@@ -13,7 +13,8 @@ import torch
 import oracle
 
 from moe_decode_gate_amd import inputs as gen
-from tests.gpu_common import DevLayer, DevTokens, act_flip_stats, bits_of, log, run_layer, shifted
+from tests.gpu_common import (DevLayer, DevTokens, act_flip_stats, assert_output_parity, bits_of, log,
+                              run_layer, shifted)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +87,8 @@ FINGERPRINT_CFGS = {
     "expert": (dict(form=2), dict(math=2, rows_per_wave=8)),
     "lanes16": (dict(form=1, lanes_per_row=16, rows_per_wave=2), dict(math=1, rows_per_wave=4)),
     "matrix-cores": (dict(form=3), None),
+    "matrix-cores-both": (dict(form=3), dict(form=3)),
+    "matrix-core-down-16w": (None, dict(form=3, waves_per_block=16)),
 }
 
 
@@ -278,6 +281,73 @@ def test_gate_up_matrix_core_form_bad_ids():
     assert np.isnan(of[3]).all() and np.isnan(of[7]).all()
 
 
+def _down(act, ids, w, dl, cfg):
+    from moe_decode_gate_amd import binding as wd
+    out = wd.down(act, ids, w, dl.wd, dl.sd, cfg=cfg)
+    torch.cuda.synchronize()
+    return bits_of(out)
+
+
+@pytest.mark.parametrize("B,W", [(3, 8), (32, 16), (40, 8), (64, 8)])
+def test_down_matrix_core_form(B, W):
+    """Down on the matrix cores sums in another order than the token form (the
+    matrix core's FP32 accumulation; experts folded wave by wave), so it is held
+    to the oracle's down projection of the same intermediate.  Zipf routing over
+    16 experts puts more slots on popular experts than one slot group holds, and
+    two tokens repeat an expert (one of them three times).  Reruns are
+    bit-identical; permuting the tokens permutes the output rows exactly (each
+    result column of the matrix instruction depends only on its own slot), and
+    so does reversing the top-k order of tokens without a repeated expert."""
+    from moe_decode_gate_amd import binding as wd
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=96)
+    L = gen.make_layer(spec, threads=16)
+    dl = DevLayer(L)
+    t = gen.make_tokens(spec, B, routing="zipf")
+    t.ids[0, 1] = t.ids[0, 0]
+    if B > 2:
+        t.ids[2, 1] = t.ids[2, 2] = t.ids[2, 0]
+    dt = DevTokens(t)
+    cfg = dict(form=3, waves_per_block=W)
+    act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu)
+    torch.cuda.synchronize()
+    ob = _down(act, dt.ids, dt.w, dl, cfg)
+    y64 = oracle.down(bits_of(act), t.ids, t.w, L.wd, L.sd, nthreads=16)
+    log(f"[mfma down] B={B} W={W}: max slots per expert {np.bincount(t.ids.ravel()).max()}")
+    assert_output_parity(ob, y64, f"down matrix cores B={B} W={W}", unit_scale=False)
+    for _ in range(2):
+        assert np.array_equal(_down(act, dt.ids, dt.w, dl, cfg), ob)
+    perm = np.random.default_rng(B).permutation(B)
+    pt = torch.from_numpy(perm).cuda()
+    assert np.array_equal(_down(act[pt].contiguous(), dt.ids[pt].contiguous(), dt.w[pt].contiguous(), dl, cfg),
+                          ob[perm])
+    rev = _down(act.flip(1).contiguous(), dt.ids.flip(1).contiguous(), dt.w.flip(1).contiguous(), dl, cfg)
+    plain = np.array([len(set(r)) == spec.K for r in t.ids])
+    assert np.array_equal(rev[plain], ob[plain])
+
+
+def test_down_matrix_core_form_bad_ids():
+    """A token with an id outside [0, E) gets a NaN row; every other token's
+    row is bit-identical to a run where that slot names a valid expert."""
+    from moe_decode_gate_amd import binding as wd
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=97)
+    dl = DevLayer(gen.make_layer(spec, threads=16))
+    t = gen.make_tokens(spec, 24)
+    dt = DevTokens(t)
+    act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu)
+    ids = t.ids.copy()
+    ids[3, 2] = 16
+    ids[7, 0] = -5
+    for W in (8, 16):
+        cfg = dict(form=3, waves_per_block=W)
+        ok = _down(act, dt.ids, dt.w, dl, cfg)
+        bad = _down(act, torch.from_numpy(ids).cuda(), dt.w, dl, cfg)
+        yb = (bad.astype(np.uint32) << 16).view(np.float32)
+        assert np.isnan(yb[3]).all() and np.isnan(yb[7]).all()
+        keep = np.ones(24, bool)
+        keep[[3, 7]] = False
+        assert np.array_equal(bad[keep], ok[keep])
+
+
 def test_weight_load_modes_agree_bitwise(mid):
     """Cached and non-temporal weight loads read the same bytes."""
     dl, t = mid
@@ -313,15 +383,16 @@ def test_side_stream(mid):
     assert np.array_equal(bits_of(out), bits_of(o))
 
 
-def test_graph_replays_match_eager_at_b32():
-    """The B=32 defaults (gate/up on the matrix cores, down with 8 rows per wave)
-    captured in a HIP graph: every replay, with eager work and synchronisation
-    in between and the outputs cleared first, reproduces the eager result bit
-    for bit."""
+@pytest.mark.parametrize("B", [32, 64])
+def test_graph_replays_match_eager(B):
+    """The defaults (B=32: gate/up on the matrix cores, down with 8 rows per
+    wave; B=64: both on the matrix cores) captured in a HIP graph: every replay,
+    with eager work and synchronisation in between and the outputs cleared
+    first, reproduces the eager result bit for bit."""
     from moe_decode_gate_amd import binding as wd
     spec = gen.LayerSpec(E=32, K=4, H=1536, I=320, seed=95)
     dl = DevLayer(gen.make_layer(spec, threads=16))
-    t = gen.make_tokens(spec, 32)
+    t = gen.make_tokens(spec, B)
     dt = DevTokens(t)
     eager_act, eager_out = run_layer(dl, dt)
     act = torch.empty_like(eager_act)
