@@ -239,7 +239,9 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     const int rows_per_wave = c.form == 3 ? 16 : (64 / lpr) * c.rows_per_wave;
     if (I % rows_per_wave) return WD_ERR_UNSUPPORTED;
     const bool tail = (H / 16) % (lpr * cpl) != 0;
-    KernelFn fn = c.form == 3   ? wd::gate_up_mfma_kernel
+    // E8M0 rows start on 4-byte boundaries: each batch's 8 bytes per row in one load
+    const bool sc8 = (H / 32) % 4 == 0 && aligned(s_gu, 4);
+    KernelFn fn = c.form == 3   ? (sc8 ? wd::gate_up_mfma_kernel<true> : wd::gate_up_mfma_kernel<false>)
                   : c.form == 2 ? gate_up_expert_fn(cpl, c.rows_per_wave, tail)
                                 : gate_up_fn(cpl, c.rows_per_wave, lpr, tail, c.math, c.weight_loads == 2);
     if (!fn) return WD_ERR_UNSUPPORTED;

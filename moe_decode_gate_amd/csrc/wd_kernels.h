@@ -321,9 +321,13 @@ struct MfmaBatch {                      // one wave's loads for kMfmaSteps 64-el
 };
 static_assert(kMfmaSteps == 4, "one 8-byte scale load and 256 bytes per row cover a batch");
 
+template <bool SC8>
 __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
-    // per wave: the batch's 16 gate and 16 up rows x 256 bytes, 16-byte slots XOR-swizzled by row
+    // per wave: the batch's 16 gate and 16 up rows x 256 bytes, 16-byte slots XOR-swizzled by row,
+    // and each lane's E8M0 bytes of the batch (kept in LDS: a register copy of the prefetched
+    // bytes would make the compute wait for the whole prefetch)
     __shared__ u32x4 tile[4][2][16][16];
+    __shared__ uint64_t stile[4][2][64];
     const int lane = threadIdx.x & 63;
     const int unit = logical_wave(a);
     if (unit >= a.nwaves) return;
@@ -340,12 +344,11 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
     // Weight and scale loads are unconditional (offsets past H are clamped; the selects
-    // in the compute step zero what they brought), so no branch, and no wait inside one,
-    // separates them.
+    // in the compute step zero what they brought) and every batch issues the same loads,
+    // so no branch separates them and each wait counts exactly the loads it needs.
     // The E8M0 bytes of a batch (blocks 2 s0 .. 2 s0 + 7 of the lane's row) come in
-    // one 8-byte load when the row holds them all and rows start on 4-byte
-    // boundaries (H a multiple of 128; always for H a multiple of 256), else byte
-    // by byte.
+    // one 8-byte load when rows start on 4-byte boundaries (SC8: H a multiple of 128
+    // and the scale array 4-byte aligned), else byte by byte.
     // Codes come coalesced: instruction j reads rows 4 (j % 4) + l / 16 of the gate
     // (j < 4) or up (j >= 4) block, 16 bytes per lane, the 16 lanes of a row covering its
     // 256 bytes of the batch in slot order p = l % 16 holding segment p ^ row (the swizzle
@@ -361,15 +364,18 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
             const uint8_t *base = (j < 4 ? pg0 : pu0) + (size_t)r * H;
             bt.v[j] = ld16(base + (k < H ? k : 0));       // past H: clamped, zeroed when read
         }
-        if ((nbr & 3) == 0 && 2 * s0 + 8 <= (int)nbr) {      // dword-aligned: row bases are multiples of 4
-            bt.sg = *reinterpret_cast<const uint64_t *>(sg + 2 * s0);
-            bt.su = *reinterpret_cast<const uint64_t *>(su + 2 * s0);
+        if constexpr (SC8) {
+            const int o = 2 * s0 + 8 <= (int)nbr ? 2 * s0 : 0;   // a batch past the row end uses none of them
+            bt.sg = *reinterpret_cast<const uint64_t *>(sg + o);
+            bt.su = *reinterpret_cast<const uint64_t *>(su + o);
         } else {
             bt.sg = 0;
             bt.su = 0;
-            for (int b = 0; b < 8 && 2 * s0 + b < (int)nbr; ++b) {
-                bt.sg |= (uint64_t)sg[2 * s0 + b] << (8 * b);
-                bt.su |= (uint64_t)su[2 * s0 + b] << (8 * b);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int o = 2 * s0 + b < (int)nbr ? 2 * s0 + b : 0;
+                bt.sg |= (uint64_t)sg[o] << (8 * b);
+                bt.su |= (uint64_t)su[o] << (8 * b);
             }
         }
     };
@@ -426,7 +432,9 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
         if (cnt == 0) break;
         const int slot = __shfl(my_slot, r16);
         const bool live = r16 < cnt;
-        const uint16_t *xr = a.x + (size_t)(live ? slot / a.K : 0) * H;
+        // lanes of empty columns read column 0's token (their products are never stored)
+        const int slot_any = live ? slot : __shfl(my_slot, 0);
+        const uint16_t *xr = a.x + (size_t)(slot_any / a.K) * H;
 
         f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = cg;
         for (int s0 = s_lo; s0 < s_hi; s0 += kMfmaSteps) {
@@ -434,29 +442,29 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
             // in order, so the previous batch's reads are done)
 #pragma unroll
             for (int j = 0; j < 8; ++j) wt[j >> 2][4 * (j & 3) + wrow][wslot] = cur.v[j];
-            const uint64_t sgb = cur.sg, sub = cur.su;       // this batch's scale bytes
+            stile[threadIdx.x >> 6][0][lane] = cur.sg;        // this batch's scale bytes
+            stile[threadIdx.x >> 6][1][lane] = cur.su;
+            // keep the prefetch below after these reads of cur, so it can reuse cur's registers
+            __builtin_amdgcn_sched_barrier(0);
             u32x4 x0[kMfmaSteps], x1[kMfmaSteps];
 #pragma unroll
             for (int i = 0; i < kMfmaSteps; ++i) {
                 const int k = 64 * (s0 + i) + 16 * q;
                 const int kc = (s0 + i < s_hi && k < H) ? k : 64 * s_lo;
-                x0[i] = zero;
-                x1[i] = zero;
-                if (live) {                            // only the lanes of live columns read x
-                    x0[i] = ld16(xr + kc);
-                    x1[i] = ld16(xr + kc + 8);
-                }
+                x0[i] = ld16(xr + kc);
+                x1[i] = ld16(xr + kc + 8);
             }
             // prefetch into the same registers (their codes are in LDS now): the next batch, or
-            // this wave's first batch again for a further group
+            // this wave's first batch again (for a further group, or unused)
             const bool more = s0 + kMfmaSteps < s_hi;
-            if (more || cnt == 16) load_batch(more ? s0 + kMfmaSteps : s_lo, cur);
+            load_batch(more ? s0 + kMfmaSteps : s_lo, cur);
 #pragma unroll
             for (int i = 0; i < kMfmaSteps; ++i) {
                 const int k = 64 * (s0 + i) + 16 * q;
                 const bool ok = s0 + i < s_hi && k < H;
                 const bool xo = ok && live;
                 const int sh = 8 * (2 * i + (q >> 1));      // byte of block 2 (s0 + i) + q / 2
+                const uint64_t sgb = stile[threadIdx.x >> 6][0][lane], sub = stile[threadIdx.x >> 6][1][lane];
                 const uint32_t bg = (uint32_t)(sgb >> sh) & 0xFFu, bu = (uint32_t)(sub >> sh) & 0xFFu;
                 const float fg = e8m0_operand(ok ? bg : 127u), fu = e8m0_operand(ok ? bu : 127u);
                 const int slot = (4 * i + q) ^ r16;         // segment 4 i + q of row r16
@@ -771,13 +779,15 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         if (real && cp.sb == 0) {
             const int gn = min(G, cp.cnt - cp.grp * G);
             live = r16 < gn;
-            slot = live ? (int)lslot[wv][cp.start + cp.grp * G + r16] : 0;
-            wk = 0.f;
+            // every lane reads a slot of the group (lanes past its end: the first), so the
+            // read and the scalar loads below need no branch and go out together
+            slot = (int)lslot[wv][cp.start + cp.grp * G + (live ? r16 : 0)];
+            float t[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {              // scalar loads: their waits do not count vector loads
-                const float t = twc[__builtin_amdgcn_readlane(slot, g)];
-                wk = r16 == g ? t : wk;
-            }
+            for (int g = 0; g < G; ++g) t[g] = twc[__builtin_amdgcn_readlane(slot, g)];
+            wk = t[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) wk = r16 == g ? t[g] : wk;
             c = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         // the task's data into the wave's LDS tiles (the wave's reads of the previous task are
