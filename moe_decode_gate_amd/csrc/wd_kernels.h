@@ -454,10 +454,12 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
                 x0[i] = ld16(xr + kc);
                 x1[i] = ld16(xr + kc + 8);
             }
-            // prefetch into the same registers (their codes are in LDS now): the next batch, or
-            // this wave's first batch again (for a further group, or unused)
+            // prefetch into the same registers (their codes are in LDS now): the next batch, this
+            // wave's first batch again for a further group, or else this batch again (unused; its
+            // lines are still in the cache, so the load that keeps every batch alike costs no
+            // HBM traffic)
             const bool more = s0 + kMfmaSteps < s_hi;
-            load_batch(more ? s0 + kMfmaSteps : s_lo, cur);
+            load_batch(more ? s0 + kMfmaSteps : cnt == 16 ? s_lo : s0, cur);
 #pragma unroll
             for (int i = 0; i < kMfmaSteps; ++i) {
                 const int k = 64 * (s0 + i) + 16 * q;
