@@ -117,13 +117,24 @@ enum wd_status {
  *                    folds each slot's router weight into its token's FP32
  *                    accumulator, and the workgroup adds its waves'
  *                    accumulators in wave order (rows_per_wave 1,
- *                    lanes_per_row 64, math 2, weight_loads 1; B <= 64, or
- *                    32 with 16 waves; B * K <= 512; E <= 1024).  Default: 3
- *                    when 56 <= B <= 64, B * K <= 512, E <= 1024 and none of
+ *                    lanes_per_row 64, math 2, weight_loads 1; B <= 64;
+ *                    at most 32 tokens per workgroup with 16 waves, see
+ *                    token_split; B * K <= 512; E <= 1024).  Default: 3
+ *                    when B <= 64, B * K <= 512, E <= 1024, none of
  *                    rows_per_wave, lanes_per_row, math, weight_loads,
- *                    waves_per_block is set, else 1.
+ *                    waves_per_block is set and B >= 32 (B >= 8 when
+ *                    K * I > 6144), else 1; with form 3 the default is
+ *                    16 waves when a token range holds at most 32 tokens,
+ *                    else 8.
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
  *                    streamed once and not kept in the caches)
+ *   token_split      down, form 3 only: 1, 2 or 4 workgroups per block of 16
+ *                    output dims, each serving its own contiguous range of
+ *                    ceil(B / token_split) tokens (an expert shared by
+ *                    several ranges is read once per range; the output does
+ *                    not depend on it bit for bit); ceil(B / token_split)
+ *                    must be <= 64 (32 with 16 waves).  0 = default: 2 when
+ *                    H / 16 < 256 (fewer blocks than the 256 CUs), else 1.
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end
  *                    time into them (hipExtLaunchKernelGGL), so the elapsed
@@ -140,6 +151,7 @@ typedef struct wd_launch {
     int lanes_per_row;
     int form;
     int weight_loads;
+    int token_split;
 } wd_launch;
 
 /* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section

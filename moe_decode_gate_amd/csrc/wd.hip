@@ -62,29 +62,45 @@ int check_dims(int B, int K, int E, int H, int I) {
 //          75 against 136 us at B = 64);
 //   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
 //   down, B 3..5: 4 rows per wave, FP32 math; B 6..55: 8 rows per wave;
-//   down, B 56..64 (B * K <= 512): the expert form on the matrix cores (one
-//          8-wave workgroup per 16 outputs; 72 against 82 us at B = 64, 68
-//          against 66 us at B = 48).
-int resolve(const wd_launch *in, int B, int K, int E, bool down, wd_launch *out) {
+//   down, B 32..64 (B * K <= 512): the expert form on the matrix cores, one
+//          16-wave workgroup per 16 outputs and token range, the batch cut in
+//          two ranges when H / 16 workgroups would leave CUs idle (47 against
+//          49 us at B = 32, 51 against 60 at B = 40, 60 against 84 at B = 64;
+//          at B = 24 the token form wins, 39 against 42 us).
+// The token-form down keeps K * I / 1024 act chunks per lane in registers; past
+// 6 (K * I > 6144) its FP32-math variants need more than 200 VGPRs (one or two
+// waves per SIMD), so there it takes the BF16-pair math, two rows per wave at
+// B <= 2 (the 128-expert / top-8 / H 4096 / I 1536 layer: 10.0 against 12.4 us
+// at B = 1) and, from B = 8, the matrix-core form (46 against 49 us at B = 8,
+// where the FP32 math took 225 us).
+int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, wd_launch *out) {
     wd_launch c = in ? *in : wd_launch{};
     const bool batch = down ? B >= 3 : B >= 5;
+    const bool wide = (long long)K * I > 6144;      // down: more than 6 act chunks per lane
     // B >= 24: gate/up in the expert form on the matrix cores, whose weight stream
     // is read once per expert however many tokens share it
     const bool untuned = c.rows_per_wave == 0 && c.lanes_per_row == 0 && c.math == 0 && c.weight_loads == 0;
     if (c.form == 0) {
-        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= 56 && B <= wd::kDnMfmaMaxB &&
+        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 32) && B <= wd::kDnMfmaMaxB &&
                                      (long long)B * K <= wd::kDnMfmaMaxSlots && E <= wd::kDnMfmaMaxE
                                : untuned && B >= 24;
         c.form = mfma ? 3 : 1;
     }
     if (c.form == 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
     if (c.rows_per_wave == 0)
-        c.rows_per_wave = !batch ? 1 : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
+        c.rows_per_wave = !batch ? (down && wide ? 2 : 1) : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
+    if (down && c.form == 3) {
+        // two token ranges when one workgroup per 16 outputs would leave CUs idle; 16 waves
+        // (the most issue slots per CU) whenever a range fits their 32-token accumulators
+        if (c.token_split == 0) c.token_split = (H / 16 < 256 && B >= 2) ? 2 : 1;
+        if (c.waves_per_block == 0 && c.token_split > 0)
+            c.waves_per_block = (B + c.token_split - 1) / c.token_split <= 32 ? 16 : 8;
+    }
     if (c.waves_per_block == 0)
-        c.waves_per_block = (down && c.form == 3) ? 8 : down ? (B == 1 ? 2 : 1) : (batch ? 4 : 1);
+        c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch ? 4 : 1);
     if (c.order == 0) c.order = 1;
     if (c.xcd_remap == 0) c.xcd_remap = (!down && !batch) ? 2 : 1;
-    if (c.math == 0) c.math = (down && batch && c.form != 3) ? wd::kMathF32 : wd::kMathDot2;
+    if (c.math == 0) c.math = (down && batch && !wide && c.form != 3) ? wd::kMathF32 : wd::kMathDot2;
     if (c.weight_loads == 0) {
         // non-temporal where no other wave re-reads the rows and the variant is compiled
         const bool nt_ok = c.math == wd::kMathDot2 && c.form == 1 &&
@@ -114,6 +130,10 @@ int resolve(const wd_launch *in, int B, int K, int E, bool down, wd_launch *out)
     if (c.form == 3 && (c.rows_per_wave != 1 || c.lanes_per_row != 64 || c.math != wd::kMathDot2 ||
                         c.weight_loads != 1))
         return WD_ERR_UNSUPPORTED;
+    // token ranges per 16-output block: the matrix-core down only
+    if (c.token_split == 0) c.token_split = 1;
+    if (c.token_split != 1 && c.token_split != 2 && c.token_split != 4) return WD_ERR_UNSUPPORTED;
+    if (c.token_split != 1 && !(down && c.form == 3)) return WD_ERR_UNSUPPORTED;
     *out = c;
     return WD_OK;
 }
@@ -232,7 +252,7 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     if (!aligned(w_gu, 16) || (B > 0 && (!aligned(x, 16) || !aligned(act, 16) || !aligned(ids, 4))))
         return WD_ERR_ALIGN;
     wd_launch c;
-    if ((rc = resolve(cfg, B, K, E, false, &c))) return rc;
+    if ((rc = resolve(cfg, B, K, E, H, I, false, &c))) return rc;
     const int lpr = c.lanes_per_row;
     const int cpl = round_cpl_gate_up((H / 16 + lpr - 1) / lpr);
     if (cpl < 0) return WD_ERR_UNSUPPORTED;
@@ -267,7 +287,7 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         (B > 0 && (!aligned(act, 16) || !aligned(ids, 4) || !aligned(tw, 4) || !aligned(out, 2))))
         return WD_ERR_ALIGN;
     wd_launch c;
-    if ((rc = resolve(cfg, B, K, E, true, &c))) return rc;
+    if ((rc = resolve(cfg, B, K, E, H, I, true, &c))) return rc;
     if (c.form == 3) {
         // every slot's id held in registers (8 per lane), per-wave accumulators for 64 tokens,
         // expert ids packed in 10 bits
@@ -277,7 +297,8 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         const bool sc8 = (I / 32) % 4 == 0 && aligned(s_d, 4);
         // 8 waves: groups of 8 slots, accumulators for 64 tokens; 16 waves (register and LDS
         // budget of four waves per SIMD): groups of 4 slots, accumulators for 32 tokens
-        if (c.waves_per_block == 16 && B > 32) return WD_ERR_UNSUPPORTED;
+        const int tpr = (B + c.token_split - 1) / c.token_split;   // tokens per workgroup
+        if (c.waves_per_block == 16 && tpr > 32) return WD_ERR_UNSUPPORTED;
         void (*fn)(LayerArgs) =
             c.waves_per_block == 16 ? (sc8 ? wd::down_mfma_kernel<16, 4, true> : wd::down_mfma_kernel<16, 4, false>)
                                     : (sc8 ? wd::down_mfma_kernel<8, 8, true> : wd::down_mfma_kernel<8, 8, false>);
@@ -287,13 +308,15 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         a.act_in = act; a.ids = ids; a.tw = tw; a.w = w_d; a.s = s_d; a.out = out;
         a.B = B; a.K = K; a.E = E; a.H = H; a.I = I;
         a.nrowblk = H / 16;
-        a.nwaves = a.nrowblk * c.waves_per_block;
+        a.tsplit = c.token_split;
+        const int blocks = a.nrowblk * c.token_split;
+        a.nwaves = blocks * c.waves_per_block;
         const hipStream_t st = (hipStream_t)stream;
         if (c.start_event || c.stop_event)
-            hipExtLaunchKernelGGL(fn, dim3(a.nrowblk), dim3(64 * c.waves_per_block), 0, st,
+            hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, st,
                                   (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a);
         else
-            hipLaunchKernelGGL(fn, dim3(a.nrowblk), dim3(64 * c.waves_per_block), 0, st, a);
+            hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, st, a);
         return launched();
     }
     const int nc = K * (I / 16);

@@ -30,6 +30,7 @@ struct LayerArgs {
     int order;               // 1: row-block major, 2: token/slot major
     int remap;               // 1: XCD-contiguous workgroup numbering
     uint32_t nci_magic;      // down: floor(2^22 / (I/16)) + 1; (c * magic) >> 22 == c / (I/16) for all chunks c
+    int tsplit;              // down, matrix-core form: workgroups per 16-output block, each for its own tokens
 };
 
 // Logical wave index of the calling wave (wave-uniform, kept in an SGPR).
@@ -606,8 +607,15 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // loads, whose waits do not count the vector loads in flight.  The task state
 // is wave-uniform (scalar registers), and every refill issues the same loads
 // in one straight block, so each wait names exactly the set it needs.
-// Limits: B <= 64 (32 with 16 waves) and B * K <= 512 (the wave keeps every
-// slot's id in registers, 8 per lane), E <= 1024.
+// With tsplit = S > 1 the batch's tokens are cut into S ranges of
+// ceil(B / S) and each 16-output block gets S workgroups, one per range
+// (workgroup g: range g / (H / 16), block g % (H / 16)); each output is still
+// owned by one workgroup.  An expert used by tokens of several ranges is read
+// once per range, from the L2 after the first: with H / 16 a multiple of 8 the
+// S workgroups of a block sit on the same XCD.  This fills the CUs that H / 16
+// workgroups leave idle.
+// Limits: B <= 64, B * K <= 512 (the wave keeps every slot's id in registers,
+// 8 per lane), ceil(B / S) <= 64 (32 with 16 waves), E <= 1024.
 // ---------------------------------------------------------------------------
 constexpr int kDnMfmaMaxB = 64;
 constexpr int kDnMfmaMaxSlots = 512;
@@ -638,8 +646,13 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __shared__ uint32_t lexp[W][kMaxExp];              // per wave: e | first entry << 10 | count << 20
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
-    const int hb = (int)blockIdx.x;
-    const int BK = a.B * a.K, H = a.H, I = a.I, E = a.E;
+    const int hb = (int)blockIdx.x % a.nrowblk;
+    const int tpr = (a.B + a.tsplit - 1) / a.tsplit;   // tokens per range
+    const int tb0 = (int)blockIdx.x / a.nrowblk * tpr; // this workgroup's tokens: [tb0, tb1)
+    const int tb1 = min(a.B, tb0 + tpr);
+    if (tb0 >= tb1) return;                            // workgroup-uniform: a range past the batch
+    const int H = a.H, I = a.I, E = a.E;
+    const int sl0 = tb0 * a.K, sl1 = tb1 * a.K;        // its slots
     const int r16 = lane & 15, q = lane >> 4;
     const int wrow = lane >> 4, wslot = lane & 15;
     u32x4(*wt)[16] = tile[wv];
@@ -650,19 +663,20 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     const int nsb = (s_hi + kMfmaSteps - 1) / kMfmaSteps;   // batches per expert
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    int idv[kDnIdRegs];                                // id of slot 64 u + lane
+    int idv[kDnIdRegs];                                // id of slot 64 u + lane (-1: not this workgroup's)
 #pragma unroll
     for (int u = 0; u < kDnIdRegs; ++u) {
         const int sl = 64 * u + lane;
-        idv[u] = sl < BK ? a.ids[sl] : -1;
+        idv[u] = sl >= sl0 && sl < sl1 ? a.ids[sl] : -1;
     }
-    for (int t = lane; t < a.B * 4; t += 64) accs[wv][t >> 2][t & 3] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = lane; t < (tb1 - tb0) * 4; t += 64) accs[wv][t >> 2][t & 3] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
     uint64_t bad_tok = 0;
 #pragma unroll
     for (int u = 0; u < kDnIdRegs; ++u) {
-        uint64_t m = __builtin_amdgcn_ballot_w64(64 * u + lane < BK && (unsigned)idv[u] >= (unsigned)E);
+        const int sl = 64 * u + lane;
+        uint64_t m = __builtin_amdgcn_ballot_w64(sl >= sl0 && sl < sl1 && (unsigned)idv[u] >= (unsigned)E);
         while (m) {
             const int sl = 64 * u + (int)__builtin_ctzll(m);
             m &= m - 1;
@@ -857,7 +871,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
             const int tok = live ? slot / a.K : -1;
             const int tprev = __shfl(tok, (lane & 48) | ((r16 + 15) & 15));
             const bool dup = live && r16 > 0 && tprev == tok;     // same token as the previous column
-            f32x4 *dst = &accs[wv][live ? tok : 0][q];
+            f32x4 *dst = &accs[wv][live ? tok - tb0 : 0][q];
             auto fold = [&]() {
                 f32x4 v = *dst;
 #pragma unroll
@@ -885,11 +899,11 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     }
 
     __syncthreads();
-    for (int t = (int)threadIdx.x; t < a.B * 16; t += 64 * W) {
-        const int b = t >> 4, r = t & 15;
+    for (int t = (int)threadIdx.x; t < (tb1 - tb0) * 16; t += 64 * W) {
+        const int bl = t >> 4, r = t & 15, b = tb0 + bl;
         float y = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w) y += accs[w][b][r >> 2][r & 3];
+        for (int w = 0; w < W; ++w) y += accs[w][bl][r >> 2][r & 3];
         if ((bad_tok >> b) & 1) y = __builtin_nanf("");
         a.out[(size_t)b * H + (size_t)hb * 16 + r] = to_bf16(y);
     }

@@ -198,7 +198,7 @@ def test_matrix_core_form_limits():
     assert dnx(form=3) == -5
     assert dnx(B=64, form=3) == -5
     assert dnx(B=32, form=3, waves_per_block=16) == -5
-    assert dnx(B=33, form=3, waves_per_block=16) == -7
+    assert dnx(B=33, form=3, waves_per_block=16, token_split=1) == -7
     assert dnx(B=65, form=3) == -7
     assert dnx(B=40, K=16, form=3) == -7           # 640 slots
     assert dnx(E=1025, K=8, form=3) == -7
@@ -208,5 +208,15 @@ def test_matrix_core_form_limits():
     assert dnx(form=3, lanes_per_row=32) == -7
     assert dnx(form=3, weight_loads=2) == -7
     assert dnx(form=2) == -7
+    # token ranges per 16-output block: 1, 2 or 4, matrix-core down only; the 16-wave limit
+    # applies to the tokens of one range
+    assert dnx(B=64, form=3, waves_per_block=16, token_split=2) == -5
+    assert dnx(B=64, form=3, waves_per_block=16, token_split=4) == -5
+    assert dnx(B=33, form=3, waves_per_block=16, token_split=2) == -5
+    assert dnx(B=33, form=3, waves_per_block=16) == -5     # default: two ranges at H / 16 = 128 blocks
+    assert dnx(B=64, form=3, token_split=3) == -7
+    assert dnx(B=64, form=3, token_split=8) == -7
+    assert dnx(B=8, form=1, token_split=2) == -7
+    assert gux(form=3, token_split=2) == -7 and gux(token_split=2) == -7
     # the default picks it only where it applies; a tuned field keeps the token form
     assert dnx(B=64, E=2048) == -5 and dnx(B=64, K=16) == -5 and dnx(B=64, waves_per_block=2) == -5

@@ -88,7 +88,8 @@ FINGERPRINT_CFGS = {
     "lanes16": (dict(form=1, lanes_per_row=16, rows_per_wave=2), dict(math=1, rows_per_wave=4)),
     "matrix-cores": (dict(form=3), None),
     "matrix-cores-both": (dict(form=3), dict(form=3)),
-    "matrix-core-down-16w": (None, dict(form=3, waves_per_block=16)),
+    "matrix-core-down-16w": (None, dict(form=3, waves_per_block=16, token_split=1)),
+    "matrix-core-down-2-ranges": (None, dict(form=3, waves_per_block=16, token_split=2)),
 }
 
 
@@ -307,7 +308,7 @@ def test_down_matrix_core_form(B, W):
     if B > 2:
         t.ids[2, 1] = t.ids[2, 2] = t.ids[2, 0]
     dt = DevTokens(t)
-    cfg = dict(form=3, waves_per_block=W)
+    cfg = dict(form=3, waves_per_block=W, token_split=1)
     act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu)
     torch.cuda.synchronize()
     ob = _down(act, dt.ids, dt.w, dl, cfg)
@@ -323,6 +324,37 @@ def test_down_matrix_core_form(B, W):
     rev = _down(act.flip(1).contiguous(), dt.ids.flip(1).contiguous(), dt.w.flip(1).contiguous(), dl, cfg)
     plain = np.array([len(set(r)) == spec.K for r in t.ids])
     assert np.array_equal(rev[plain], ob[plain])
+    # the batch cut into token ranges, one workgroup per range and block: a token's sums
+    # do not depend on the other tokens, so the output is the same bit for bit
+    for S in (2, 4):
+        log(f"[mfma down] B={B} W={W} token_split={S}")
+        assert np.array_equal(_down(act, dt.ids, dt.w, dl, dict(cfg, token_split=S)), ob)
+
+
+@pytest.mark.parametrize("B,S", [(64, 2), (50, 4), (33, 2)])
+def test_down_matrix_core_token_split_16_waves(B, S):
+    """16 waves hold at most 32 tokens per workgroup; with token ranges the
+    batch may be larger.  Held to the oracle's down projection of the same
+    intermediate; each range's rows equal, bit for bit, a run on that range's
+    tokens alone."""
+    from moe_decode_gate_amd import binding as wd
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=98)
+    L = gen.make_layer(spec, threads=16)
+    dl = DevLayer(L)
+    t = gen.make_tokens(spec, B, routing="zipf")
+    dt = DevTokens(t)
+    act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu)
+    torch.cuda.synchronize()
+    y64 = oracle.down(bits_of(act), t.ids, t.w, L.wd, L.sd, nthreads=16)
+    ob = _down(act, dt.ids, dt.w, dl, dict(form=3, waves_per_block=16, token_split=S))
+    assert_output_parity(ob, y64, f"down matrix cores B={B} W=16 S={S}", unit_scale=False)
+    # each range's tokens alone give their rows bit for bit
+    tpr = -(-B // S)
+    for r0 in range(0, B, tpr):
+        sl = slice(r0, min(B, r0 + tpr))
+        part = _down(act[sl].contiguous(), dt.ids[sl].contiguous(), dt.w[sl].contiguous(), dl,
+                     dict(form=3, waves_per_block=16))
+        assert np.array_equal(part, ob[sl])
 
 
 def test_down_matrix_core_form_bad_ids():
@@ -337,8 +369,8 @@ def test_down_matrix_core_form_bad_ids():
     ids = t.ids.copy()
     ids[3, 2] = 16
     ids[7, 0] = -5
-    for W in (8, 16):
-        cfg = dict(form=3, waves_per_block=W)
+    for W, S in ((8, 1), (16, 1), (8, 2), (16, 4)):
+        cfg = dict(form=3, waves_per_block=W, token_split=S)
         ok = _down(act, dt.ids, dt.w, dl, cfg)
         bad = _down(act, torch.from_numpy(ids).cuda(), dt.w, dl, cfg)
         yb = (bad.astype(np.uint32) << 16).view(np.float32)
