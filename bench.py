@@ -23,6 +23,8 @@ steps never find their expert rows in the 256 MB last-level cache.
   cpu_baseline     the CPU oracle on this host's cores on a bounded sample
   stack48          a 48-layer decode step (chained layers, per-layer routing
                    from the router kernel) at B in {1, 2, 4, 8, 16, 32, 64}
+  large            the 128-expert / top-8 / H 4096 / I 1536 layer with Zipf(1.2)
+                   expert popularity at B in {1, 8, 32}
 """
 from __future__ import annotations
 
@@ -74,7 +76,7 @@ def load_traffic(name: str):
 class Workload:
     """R device copies of one layer plus per-step routing and activations."""
 
-    def __init__(self, torch, wd, gen, L, B, steps, copies, seed):
+    def __init__(self, torch, wd, gen, L, B, steps, copies, seed, routing="softmax"):
         spec = L.spec
         self.spec, self.B = spec, B
         dev = "cuda"
@@ -84,7 +86,8 @@ class Workload:
         self.steps = steps
         xs, ids, ws = [], [], []
         for s in range(steps):
-            t = gen.make_tokens(gen.LayerSpec(E=spec.E, K=spec.K, H=spec.H, I=spec.I, seed=seed), B, step=s)
+            t = gen.make_tokens(gen.LayerSpec(E=spec.E, K=spec.K, H=spec.H, I=spec.I, seed=seed), B,
+                                routing=routing, step=s)
             xs.append(t.x); ids.append(t.ids); ws.append(t.w)
         self.host_x, self.host_ids, self.host_w = np.stack(xs), np.stack(ids), np.stack(ws)
         self.x = torch.from_numpy(self.host_x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -160,6 +163,31 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int):
         kernels_GBps=(gu_bytes + dn_bytes) / ((gu_ms.mean() + dn_ms.mean()) * 1e-3) / 1e9,
     )
     return res
+
+
+def measure_large(torch, wd, gen, oracle, read_peak, batches=(1, 8, 32), steps=40, warmup=10):
+    """The larger layer (128 experts, top-8, H 4096, I 1536) with Zipf(1.2)
+    expert popularity at B in {1, 8, 32}: step time from one HIP graph and
+    per-kernel durations, as for the headline workload, with two distinct
+    weight copies (5 GB, 2.5x the last-level cache: a step never finds the
+    previous step's rows there), plus sampled parity against the oracle."""
+    cfg = gen.CONFIGS["large"]
+    spec = cfg["spec"]
+    t0 = time.time()
+    L = gen.make_layer(spec, threads=16)
+    eprint(f"[bench] large layer generated in {time.time() - t0:.1f} s")
+    out = []
+    for B in batches:
+        w = Workload(torch, wd, gen, L, B, max(steps, warmup), 2, seed=spec.seed, routing=cfg["routing"])
+        r = measure(torch, wd, w, steps, warmup)
+        cos, err, ymax = sampled_parity(oracle, L, w, [0, steps - 1])
+        r.update(parity_cos_min=cos, parity_max_abs_err=err, parity_max_abs_y=ymax,
+                 frac_of_measured_read_peak=r["layer_GBps_graph"] / read_peak)
+        eprint(f"[bench] large B={B}: {json.dumps(r)}")
+        out.append(r)
+        del w
+        torch.cuda.empty_cache()
+    return dict(workload="E=128 top-8 H=4096 I=1536, Zipf(1.2) routing", weight_copies=2, per_B=out)
 
 
 def one_shot_read(torch, wd, nbytes, copies=16, reps=16):
@@ -372,8 +400,10 @@ def hbm_read_peak(torch, wd, nbytes=4 << 30, reps=5):
 
 
 def sampled_parity(oracle, L, work: Workload, steps_to_check):
-    """Cosine and max |err| of GPU outputs against the oracle on a few steps."""
-    cos_min, err_max = 1.0, 0.0
+    """Cosine and max |err| of GPU outputs against the oracle on a few steps,
+    and the largest |output| of the oracle there (the scale of that error:
+    the BF16 output's half-ulp is 2^-9 of its binade)."""
+    cos_min, err_max, ymax = 1.0, 0.0, 0.0
     for s in steps_to_check:
         y64, _ = oracle.moe_decode(work.host_x[s], work.host_ids[s], work.host_w[s],
                                    L.wgu, L.sgu, L.wd, L.sd)
@@ -381,7 +411,8 @@ def sampled_parity(oracle, L, work: Workload, steps_to_check):
         cos = float(got.ravel() @ y64.ravel() / (np.linalg.norm(got) * np.linalg.norm(y64)))
         cos_min = min(cos_min, cos)
         err_max = max(err_max, float(np.abs(got - y64).max()))
-    return cos_min, err_max
+        ymax = max(ymax, float(np.abs(y64).max()))
+    return cos_min, err_max, ymax
 
 
 def accuracy(oracle, L, work: Workload, steps_to_check):
@@ -438,6 +469,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-b32", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-large", action="store_true", help="skip the H 4096 / I 1536 layer")
     ap.add_argument("--no-compare", action="store_true", help="skip the expert-centric comparison")
     ap.add_argument("--only-compare", action="store_true",
                     help="run only the expert-centric comparison and print its JSON object (for profiling)")
@@ -480,8 +512,8 @@ def main():
     r1 = measure(torch, wd, w1, steps, warmup)
     eprint(f"[bench] B=1: {json.dumps(r1)}")
     import oracle
-    cos1, err1 = sampled_parity(oracle, L, w1, [0, steps // 2, steps - 1])
-    r1.update(parity_cos_min=cos1, parity_max_abs_err=err1,
+    cos1, err1, ymax1 = sampled_parity(oracle, L, w1, [0, steps // 2, steps - 1])
+    r1.update(parity_cos_min=cos1, parity_max_abs_err=err1, parity_max_abs_y=ymax1,
               gate_up_over_one_shot_read=r1["gate_up_us"] / floor_us,
               down_over_one_shot_read=r1["down_us"] / floor_dn_us)
     del w1
@@ -491,8 +523,8 @@ def main():
     if not args.no_b32:
         w32 = Workload(torch, wd, gen, L, 32, max(steps, warmup), args.copies or 4, seed=gen.CONFIGS["qwen3_b32"]["spec"].seed)
         r32 = measure(torch, wd, w32, steps, warmup)
-        cos32, err32 = sampled_parity(oracle, L, w32, [0, steps - 1])
-        r32.update(parity_cos_min=cos32, parity_max_abs_err=err32,
+        cos32, err32, ymax32 = sampled_parity(oracle, L, w32, [0, steps - 1])
+        r32.update(parity_cos_min=cos32, parity_max_abs_err=err32, parity_max_abs_y=ymax32,
                    frac_of_measured_read_peak=r32["layer_GBps_graph"] / peak,
                    accuracy=accuracy(oracle, L, w32, [0, steps - 1]))
         eprint(f"[bench] B=32: {json.dumps(r32)}")
@@ -500,6 +532,8 @@ def main():
         torch.cuda.empty_cache()
 
     stack = None if args.no_stack else measure_stack(torch, wd, gen, L, peak)
+
+    large = None if args.no_large else measure_large(torch, wd, gen, oracle, peak)
 
     compare = None if args.no_compare else measure_comparison(torch, wd, gen, L, compare_batches)
 
@@ -531,6 +565,7 @@ def main():
         "b1": r1,
         "b32": r32,
         "stack48": stack,
+        "large": large,
         "vs_expert_centric": compare,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
