@@ -73,6 +73,14 @@ def load_traffic(name: str):
     return None
 
 
+def expert_bytes(spec):
+    """Algorithmic bytes one routed expert costs each kernel: its MXFP8 codes
+    plus one E8M0 byte per 32 codes (gate/up: 2I rows of H; down: H rows of I)."""
+    gate_up = 2 * spec.I * spec.H + 2 * spec.I * (spec.H // 32)
+    down = spec.H * spec.I + spec.H * (spec.I // 32)
+    return gate_up, down
+
+
 class Workload:
     """R device copies of one layer plus per-step routing and activations."""
 
@@ -146,8 +154,7 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int):
     dn_ms = np.array([evs[s][2].elapsed_time(evs[s][3]) for s in range(steps)])
 
     u = work.unique[:steps].astype(np.float64)
-    per_expert_gu = 2 * spec.I * spec.H + 2 * spec.I * (spec.H // 32)
-    per_expert_dn = spec.H * spec.I + spec.H * (spec.I // 32)
+    per_expert_gu, per_expert_dn = expert_bytes(spec)
     gu_bytes = float(np.mean(u * per_expert_gu))
     dn_bytes = float(np.mean(u * per_expert_dn))
     B = work.B
@@ -499,8 +506,7 @@ def main():
 
     peak, peak_cfg, copy_bw = hbm_read_peak(torch, wd)
     eprint(f"[bench] contiguous-read peak {peak:.0f} GB/s (unroll, blocks = {peak_cfg}); copy {copy_bw:.0f} GB/s")
-    gu_b1_bytes = 8 * (2 * spec.I * spec.H + 2 * spec.I * (spec.H // 32))      # gate/up bytes of 8 experts
-    dn_b1_bytes = 8 * (spec.H * spec.I + spec.H * (spec.I // 32))              # down bytes of 8 experts
+    gu_b1_bytes, dn_b1_bytes = (8 * n for n in expert_bytes(spec))   # each kernel's bytes of 8 experts
     floor_us, floor_cfg = one_shot_read(torch, wd, gu_b1_bytes)
     floor_dn_us, floor_dn_cfg = one_shot_read(torch, wd, dn_b1_bytes)
     eprint(f"[bench] one-shot read of {gu_b1_bytes} B: {floor_us:.2f} us (unroll, blocks = {floor_cfg}); "
