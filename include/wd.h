@@ -124,8 +124,8 @@ enum wd_status {
  *                    rows_per_wave, lanes_per_row, math, weight_loads,
  *                    waves_per_block is set and B >= 32 (B >= 8 when
  *                    K * I > 6144), else 1; with form 3 the default is
- *                    16 waves when a token range holds at most 32 tokens,
- *                    else 8.
+ *                    16 waves when a token range holds at most 32 tokens
+ *                    (16 with a single range), else 8.
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
  *                    streamed once and not kept in the caches)
  *   token_split      down, form 3 only: 1, 2 or 4 workgroups per block of 16

@@ -91,10 +91,13 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
         c.rows_per_wave = !batch ? (down && wide ? 2 : 1) : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
     if (down && c.form == 3) {
         // two token ranges when one workgroup per 16 outputs would leave CUs idle; 16 waves
-        // (the most issue slots per CU) whenever a range fits their 32-token accumulators
+        // (the most issue slots per CU) whenever a range fits their 32-token accumulators, but
+        // with one range only up to 16 tokens: 16 waves take slots in groups of 4, 8 waves in
+        // groups of 8, and an expert's rows are streamed once per group (4096 / 1536 layer,
+        // Zipf routing, B = 32: 101 us with 8 waves against 113 with 16)
         if (c.token_split == 0) c.token_split = (H / 16 < 256 && B >= 2) ? 2 : 1;
         if (c.waves_per_block == 0 && c.token_split > 0)
-            c.waves_per_block = (B + c.token_split - 1) / c.token_split <= 32 ? 16 : 8;
+            c.waves_per_block = (B + c.token_split - 1) / c.token_split <= (c.token_split > 1 ? 32 : 16) ? 16 : 8;
     }
     if (c.waves_per_block == 0)
         c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch ? 4 : 1);

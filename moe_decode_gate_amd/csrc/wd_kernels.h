@@ -603,8 +603,9 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // register sets (two with 16 waves) that many tasks ahead of the compute; a
 // task's compute first copies its set into the wave's LDS tiles (codes
 // XOR-swizzled by row, act rows padded to start 4 banks apart), refills the
-// set, then reads its operands from LDS.  Router weights come through scalar
-// loads, whose waits do not count the vector loads in flight.  The task state
+// set, then reads its operands from LDS.  The workgroup's router weights are
+// copied to LDS once at the start (a load per slot group, scalar or vector,
+// would put a cache round trip in front of every group).  The task state
 // is wave-uniform (scalar registers), and every refill issues the same loads
 // in one straight block, so each wait names exactly the set it needs.
 // With tsplit = S > 1 the batch's tokens are cut into S ranges of
@@ -644,6 +645,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __shared__ f32x4 accs[W][kMaxB][4];                // per wave: [token][rows 4 q .. 4 q + 3]
     __shared__ int16_t lslot[W][kDnMfmaMaxSlots];      // per wave: slots of its experts, expert by expert
     __shared__ uint32_t lexp[W][kMaxExp];              // per wave: e | first entry << 10 | count << 20
+    __shared__ float lw[kDnMfmaMaxSlots];              // router weights of the workgroup's slots, by slot - sl0
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
     const int hb = (int)blockIdx.x % a.nrowblk;
@@ -670,6 +672,8 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         idv[u] = sl >= sl0 && sl < sl1 ? a.ids[sl] : -1;
     }
     for (int t = lane; t < (tb1 - tb0) * 4; t += 64) accs[wv][t >> 2][t & 3] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) lw[t] = a.tw[sl0 + t];
+    __syncthreads();                                   // lw complete before any fold reads it
 
     // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
     uint64_t bad_tok = 0;
@@ -780,7 +784,6 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     };
 
     // ---- compute side ----
-    const __attribute__((address_space(4))) float *twc = (const __attribute__((address_space(4))) float *)a.tw;
     int slot = 0;
     bool live = false;
     float wk = 0.f;
@@ -795,15 +798,10 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         if (real && cp.sb == 0) {
             const int gn = min(G, cp.cnt - cp.grp * G);
             live = r16 < gn;
-            // every lane reads a slot of the group (lanes past its end: the first), so the
-            // read and the scalar loads below need no branch and go out together
+            // every lane reads a slot of the group (lanes past its end: the first) and its
+            // router weight, both from LDS
             slot = (int)lslot[wv][cp.start + cp.grp * G + (live ? r16 : 0)];
-            float t[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) t[g] = twc[__builtin_amdgcn_readlane(slot, g)];
-            wk = t[0];
-#pragma unroll
-            for (int g = 1; g < G; ++g) wk = r16 == g ? t[g] : wk;
+            wk = lw[slot - sl0];
             c = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         // the task's data into the wave's LDS tiles (the wave's reads of the previous task are
