@@ -171,9 +171,10 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
  * "Down Kernel"): one wave per (token b, output dim h).  The wave walks the K
  * routed experts' rows Wd[e_k, h, :], folds topk_w[b,k] into one FP32
  * accumulator, reduces across its 64 lanes with DPP row operations and one
- * lane read (no LDS) and writes out[b,h] = BF16(acc).  From B = 56 the
- * default is the expert form on the matrix cores (wd_launch.form 3), which
- * reads each Wd row block once for all the tokens routed to its expert. */
+ * lane read (no LDS) and writes out[b,h] = BF16(acc).  From B = 32 (B = 8
+ * when K * I > 6144) the default is the expert form on the matrix cores
+ * (wd_launch.form 3), which reads each Wd row block once per token range for
+ * all the tokens of the range routed to its expert. */
 int wd_down(const uint16_t *act, const int32_t *topk_ids, const float *topk_w,
             const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
             int B, int K, int E, int H, int I, void *stream);
