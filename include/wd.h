@@ -110,30 +110,28 @@ enum wd_status {
  *                    else 1.
  *                    down: 1 = one wave per (token, block of output dims);
  *                    3 = one workgroup of 8 or 16 waves (waves_per_block)
- *                    per block of 16 output dims serving every token: each
- *                    wave takes every 8th (16th) routed expert, forms the
- *                    16 x slots tile on the BF16 matrix cores (weights
- *                    converted exactly, act as stored, FP32 accumulation),
- *                    folds each slot's router weight into its token's FP32
- *                    accumulator, and the workgroup adds its waves'
- *                    accumulators in wave order (rows_per_wave 1,
+ *                    per block of 16 output dims serving every token (of
+ *                    its token range, see token_split): the routed experts
+ *                    are dealt to the waves in turn, each wave forms the
+ *                    16 x slots tile of its experts on the BF16 matrix cores
+ *                    (weights converted exactly, act as stored, FP32
+ *                    accumulation) and keeps each slot's 16 values in LDS;
+ *                    each output then folds its token's router weights in,
+ *                    one FMA per slot in expert order (rows_per_wave 1,
  *                    lanes_per_row 64, math 2, weight_loads 1; B <= 64;
- *                    at most 32 tokens per workgroup with 16 waves, see
- *                    token_split; B * K <= 512; E <= 1024).  Default: 3
+ *                    B * K <= 512; E <= 1024).  Default: 3
  *                    when B <= 64, B * K <= 512, E <= 1024, none of
  *                    rows_per_wave, lanes_per_row, math, weight_loads,
  *                    waves_per_block is set and B >= 32 (B >= 8 when
  *                    K * I > 6144), else 1; with form 3 the default is
- *                    16 waves when a token range holds at most 32 tokens
- *                    (16 with a single range), else 8.
+ *                    16 waves with several token ranges, else 8.
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
  *                    streamed once and not kept in the caches)
  *   token_split      down, form 3 only: 1, 2 or 4 workgroups per block of 16
  *                    output dims, each serving its own contiguous range of
  *                    ceil(B / token_split) tokens (an expert shared by
  *                    several ranges is read once per range; the output does
- *                    not depend on it bit for bit); ceil(B / token_split)
- *                    must be <= 64 (32 with 16 waves).  0 = default: 2 when
+ *                    not depend on it bit for bit).  0 = default: 2 when
  *                    H / 16 < 256 (fewer blocks than the 256 CUs), else 1.
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end

@@ -90,14 +90,13 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.rows_per_wave == 0)
         c.rows_per_wave = !batch ? (down && wide ? 2 : 1) : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
     if (down && c.form == 3) {
-        // two token ranges when one workgroup per 16 outputs would leave CUs idle; 16 waves
-        // (the most issue slots per CU) whenever a range fits their 32-token accumulators, but
-        // with one range only up to 16 tokens: 16 waves take slots in groups of 4, 8 waves in
-        // groups of 8, and an expert's rows are streamed once per group (4096 / 1536 layer,
-        // Zipf routing, B = 32: 101 us with 8 waves against 113 with 16)
+        // two token ranges when one workgroup per 16 outputs would leave CUs idle, with 16
+        // waves (Qwen-3 layer, B = 32: 44 us against 56 with 8); one range with 8 waves, which
+        // take slots in groups of 8 where 16 waves take them in groups of 4, each group
+        // streaming the expert's rows once (4096 / 1536 layer, Zipf routing: B = 8 43 against
+        // 45 us, B = 32 98 against 118)
         if (c.token_split == 0) c.token_split = (H / 16 < 256 && B >= 2) ? 2 : 1;
-        if (c.waves_per_block == 0 && c.token_split > 0)
-            c.waves_per_block = (B + c.token_split - 1) / c.token_split <= (c.token_split > 1 ? 32 : 16) ? 16 : 8;
+        if (c.waves_per_block == 0) c.waves_per_block = c.token_split > 1 ? 16 : 8;
     }
     if (c.waves_per_block == 0)
         c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch ? 4 : 1);
@@ -298,10 +297,7 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
             return WD_ERR_UNSUPPORTED;
         // E8M0 rows start on 4-byte boundaries: each batch's 8 bytes in one load
         const bool sc8 = (I / 32) % 4 == 0 && aligned(s_d, 4);
-        // 8 waves: groups of 8 slots, accumulators for 64 tokens; 16 waves (register and LDS
-        // budget of four waves per SIMD): groups of 4 slots, accumulators for 32 tokens
-        const int tpr = (B + c.token_split - 1) / c.token_split;   // tokens per workgroup
-        if (c.waves_per_block == 16 && tpr > 32) return WD_ERR_UNSUPPORTED;
+        // 8 waves: groups of 8 slots; 16 waves (register budget of four waves per SIMD): 4
         void (*fn)(LayerArgs) =
             c.waves_per_block == 16 ? (sc8 ? wd::down_mfma_kernel<16, 4, true> : wd::down_mfma_kernel<16, 4, false>)
                                     : (sc8 ? wd::down_mfma_kernel<8, 8, true> : wd::down_mfma_kernel<8, 8, false>);

@@ -583,17 +583,21 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // Down, expert form on the matrix cores: one workgroup of W waves per block of
 // 16 output dims h, serving every token of the batch.
 //
-// Wave w takes the experts e = w, w + W, w + 2W, ... that at least one slot is
-// routed to.  For each it forms, G slots at a time (slot order), the tile
+// The experts that at least one slot is routed to are dealt to the waves in
+// turn (the n-th routed expert, in expert order, to wave n mod W), so every
+// wave gets the same number of experts to within one.  For each of its experts
+// a wave forms, G slots at a time (slot order), the tile
 // P[h][c] = sum_i Wd[e][h][i] * act[slot c][i] with v_mfma_f32_16x16x32_bf16
 // (weight codes converted exactly to BF16, act as stored, FP32 accumulation;
-// A = the 16 weight rows, B = the slots' act rows), and folds the router
-// weight in, acc[token][h] = fma(w_slot, P[h][c], acc[token][h]), into FP32
-// accumulators in LDS that belong to the wave (the token form's routing-weight
-// fold, with the expert's dot products done once for all its slots).  At the
-// end the workgroup adds its waves' accumulators in wave order and writes
-// out[b][h] = BF16(sum).  Each output is owned by one workgroup: no atomic, no
-// buffer besides the output.  Every Wd byte is read once per call.
+// A = the 16 weight rows, B = the slots' act rows) and keeps each slot's 16
+// values in LDS: the expert's dot products are done once for all its slots.
+// At the end each output folds its token's router weights in, one FMA per
+// slot in expert order (equal experts in slot order),
+// y = fma(w_slot, P[h][slot], y), the token form's routing-weight fold, and
+// writes out[b][h] = BF16(y).  A token's result depends on its own slots only
+// (not on the other tokens, the wave that served an expert, or its top-k
+// order).  Each output is owned by one workgroup: no atomic, no buffer besides
+// the output.  Every Wd byte is read once per call.
 //
 // At the start each wave lists its routed experts and their slots (slot
 // order) in LDS.  Its work is then a sequence of tasks (expert, group of up to
@@ -616,7 +620,7 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // S workgroups of a block sit on the same XCD.  This fills the CUs that H / 16
 // workgroups leave idle.
 // Limits: B <= 64, B * K <= 512 (the wave keeps every slot's id in registers,
-// 8 per lane), ceil(B / S) <= 64 (32 with 16 waves), E <= 1024.
+// 8 per lane, and each slot's 16 products in LDS), E <= 1024.
 // ---------------------------------------------------------------------------
 constexpr int kDnMfmaMaxB = 64;
 constexpr int kDnMfmaMaxSlots = 512;
@@ -639,13 +643,14 @@ template <int W, int G, bool SC8>
 __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     constexpr int kXRow = 33;                          // u32x4 per act row in LDS: 256 bf16 + 16 bytes of padding
     constexpr int kMaxExp = (kDnMfmaMaxE + W - 1) / W; // experts one wave can be given
-    constexpr int kMaxB = W >= 16 ? 32 : kDnMfmaMaxB;  // tokens the per-wave accumulators hold (LDS)
     __shared__ u32x4 tile[W][16][16];                  // per wave: 16 rows x 256 bytes of codes, swizzled
     __shared__ u32x4 xtile[W][G][kXRow];               // per wave: the group's act for the batch
-    __shared__ f32x4 accs[W][kMaxB][4];                // per wave: [token][rows 4 q .. 4 q + 3]
+    __shared__ f32x4 pv[kDnMfmaMaxSlots][4];           // per slot - sl0: P[0..15] of its expert's rows
     __shared__ int16_t lslot[W][kDnMfmaMaxSlots];      // per wave: slots of its experts, expert by expert
     __shared__ uint32_t lexp[W][kMaxExp];              // per wave: e | first entry << 10 | count << 20
     __shared__ float lw[kDnMfmaMaxSlots];              // router weights of the workgroup's slots, by slot - sl0
+    __shared__ int16_t lord[kDnMfmaMaxSlots];          // per token of the range: its slots in fold order
+    __shared__ uint8_t lused[kDnMfmaMaxE];             // experts some slot of the range is routed to
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
     const int hb = (int)blockIdx.x % a.nrowblk;
@@ -671,9 +676,27 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         const int sl = 64 * u + lane;
         idv[u] = sl >= sl0 && sl < sl1 ? a.ids[sl] : -1;
     }
-    for (int t = lane; t < (tb1 - tb0) * 4; t += 64) accs[wv][t >> 2][t & 3] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) lw[t] = a.tw[sl0 + t];
-    __syncthreads();                                   // lw complete before any fold reads it
+    for (int t = (int)threadIdx.x; t < E; t += 64 * W) lused[t] = 0;
+    const int K = a.K;
+    for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) {
+        lw[t] = a.tw[sl0 + t];
+        // fold order of the slot within its token: by expert, equal experts by slot (ids
+        // outside [0, E) last; such tokens are NaN anyway)
+        const int tl = t / K, k = t - tl * K;
+        const int32_t *tid = a.ids + sl0 + tl * K;
+        const unsigned ek = (unsigned)tid[k] < (unsigned)E ? (unsigned)tid[k] : (unsigned)E;
+        int rank = 0;
+        for (int k2 = 0; k2 < K; ++k2) {
+            const unsigned e2 = (unsigned)tid[k2] < (unsigned)E ? (unsigned)tid[k2] : (unsigned)E;
+            rank += e2 < ek || (e2 == ek && k2 < k);
+        }
+        lord[tl * K + rank] = (int16_t)k;
+    }
+    __syncthreads();                                   // lused cleared before it is marked
+#pragma unroll
+    for (int u = 0; u < kDnIdRegs; ++u)
+        if ((unsigned)idv[u] < (unsigned)E) lused[idv[u]] = 1;
+    __syncthreads();                                   // lused, lw, lord complete
 
     // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
     uint64_t bad_tok = 0;
@@ -688,26 +711,32 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         }
     }
 
-    // the wave's experts and their slots, in expert then slot order
+    // the wave's experts (routed experts n = wv, wv + W, ... in expert order) and their
+    // slots, in expert then slot order
     int nx = 0;
     {
-        int ns = 0;
-        for (int e = wv; e < E; e += W) {
-            bool any = false;
+        int ns = 0, seen = 0;
+        for (int base = 0; base < E; base += 64) {
+            const bool used = base + lane < E && lused[base + lane] != 0;
+            const uint64_t um = __builtin_amdgcn_ballot_w64(used);
+            const int n = seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
+            uint64_t mine = __builtin_amdgcn_ballot_w64(used && n % W == wv);
+            seen += __builtin_popcountll(um);
+            while (mine) {
+                const int e = base + (int)__builtin_ctzll(mine);
+                mine &= mine - 1;
+                const int first = ns;
 #pragma unroll
-            for (int u = 0; u < kDnIdRegs; ++u) any |= idv[u] == e;
-            if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
-            const int first = ns;
-#pragma unroll
-            for (int u = 0; u < kDnIdRegs; ++u) {
-                const bool m = idv[u] == e;
-                const uint64_t bm = __builtin_amdgcn_ballot_w64(m);
-                const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-                if (m) lslot[wv][ns + rank] = (int16_t)(64 * u + lane);
-                ns += __builtin_popcountll(bm);
+                for (int u = 0; u < kDnIdRegs; ++u) {
+                    const bool m = idv[u] == e;
+                    const uint64_t bm = __builtin_amdgcn_ballot_w64(m);
+                    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+                    if (m) lslot[wv][ns + rank] = (int16_t)(64 * u + lane);
+                    ns += __builtin_popcountll(bm);
+                }
+                if (lane == 0) lexp[wv][nx] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)(ns - first) << 20;
+                ++nx;
             }
-            if (lane == 0) lexp[wv][nx] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)(ns - first) << 20;
-            ++nx;
         }
     }
 
@@ -786,7 +815,6 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // ---- compute side ----
     int slot = 0;
     bool live = false;
-    float wk = 0.f;
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
     const int xr = r16 < G ? r16 : 0;
     // One task: its data into the wave's LDS tiles, the set refilled with the task three
@@ -798,10 +826,8 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         if (real && cp.sb == 0) {
             const int gn = min(G, cp.cnt - cp.grp * G);
             live = r16 < gn;
-            // every lane reads a slot of the group (lanes past its end: the first) and its
-            // router weight, both from LDS
+            // every lane reads a slot of the group (lanes past its end: the first)
             slot = (int)lslot[wv][cp.start + cp.grp * G + (live ? r16 : 0)];
-            wk = lw[slot - sl0];
             c = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         // the task's data into the wave's LDS tiles (the wave's reads of the previous task are
@@ -864,25 +890,8 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
                 c = mfma_bf16(w1, xb, c);
             }
         }
-        if (cp.sb == nsb - 1) {
-            // lane (column r16, quad q) holds P[4 q + j][r16]: fold into the slot's token
-            const int tok = live ? slot / a.K : -1;
-            const int tprev = __shfl(tok, (lane & 48) | ((r16 + 15) & 15));
-            const bool dup = live && r16 > 0 && tprev == tok;     // same token as the previous column
-            f32x4 *dst = &accs[wv][live ? tok - tb0 : 0][q];
-            auto fold = [&]() {
-                f32x4 v = *dst;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(wk, c[j], v[j]);
-                *dst = v;
-            };
-            if (__builtin_amdgcn_ballot_w64(dup) == 0) {
-                if (live) fold();
-            } else {                                   // a token routed to the expert twice: columns in order
-                for (int col = 0; col < G; ++col)
-                    if (r16 == col && live) fold();
-            }
-        }
+        // lane (column r16, quad q) holds P[4 q + j][r16]: the slot's rows 4 q .. 4 q + 3
+        if (cp.sb == nsb - 1 && live) pv[slot - sl0][q] = c;
         advance(cp);
     };
 
@@ -900,8 +909,10 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     for (int t = (int)threadIdx.x; t < (tb1 - tb0) * 16; t += 64 * W) {
         const int bl = t >> 4, r = t & 15, b = tb0 + bl;
         float y = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) y += accs[w][bl][r >> 2][r & 3];
+        for (int i = 0; i < K; ++i) {                  // the token's slots in fold order
+            const int sl = bl * K + lord[bl * K + i];
+            y = __builtin_fmaf(lw[sl], pv[sl][r >> 2][r & 3], y);
+        }
         if ((bad_tok >> b) & 1) y = __builtin_nanf("");
         a.out[(size_t)b * H + (size_t)hb * 16 + r] = to_bf16(y);
     }

@@ -190,15 +190,16 @@ def test_matrix_core_form_limits():
     assert gux(form=3, weight_loads=2) == -7
     assert gux(form=4) == -7
 
-    # down on the matrix cores: 8 or 16 waves per workgroup, B <= 64 (32 with 16 waves),
-    # B * K <= 512, E <= 1024; accepted configurations get as far as the device check (-5 here)
+    # down on the matrix cores: 8 or 16 waves per workgroup, B <= 64, B * K <= 512, E <= 1024;
+    # accepted configurations get as far as the device check (-5 here)
     def dnx(B=1, K=8, E=128, **kw):
         return lib.wd_down_ex(A, A, A, A, A, A, B, K, E, 2048, 768, C.byref(wd.Launch(**kw)), None)
 
     assert dnx(form=3) == -5
     assert dnx(B=64, form=3) == -5
     assert dnx(B=32, form=3, waves_per_block=16) == -5
-    assert dnx(B=33, form=3, waves_per_block=16, token_split=1) == -7
+    assert dnx(B=33, form=3, waves_per_block=16, token_split=1) == -5
+    assert dnx(B=64, form=3, waves_per_block=16, token_split=1) == -5
     assert dnx(B=65, form=3) == -7
     assert dnx(B=40, K=16, form=3) == -7           # 640 slots
     assert dnx(E=1025, K=8, form=3) == -7
@@ -208,8 +209,7 @@ def test_matrix_core_form_limits():
     assert dnx(form=3, lanes_per_row=32) == -7
     assert dnx(form=3, weight_loads=2) == -7
     assert dnx(form=2) == -7
-    # token ranges per 16-output block: 1, 2 or 4, matrix-core down only; the 16-wave limit
-    # applies to the tokens of one range
+    # token ranges per 16-output block: 1, 2 or 4, matrix-core down only
     assert dnx(B=64, form=3, waves_per_block=16, token_split=2) == -5
     assert dnx(B=64, form=3, waves_per_block=16, token_split=4) == -5
     assert dnx(B=33, form=3, waves_per_block=16, token_split=2) == -5

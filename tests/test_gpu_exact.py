@@ -289,16 +289,17 @@ def _down(act, ids, w, dl, cfg):
     return bits_of(out)
 
 
-@pytest.mark.parametrize("B,W", [(3, 8), (32, 16), (40, 8), (64, 8)])
+@pytest.mark.parametrize("B,W", [(3, 8), (32, 16), (40, 8), (64, 8), (64, 16)])
 def test_down_matrix_core_form(B, W):
     """Down on the matrix cores sums in another order than the token form (the
-    matrix core's FP32 accumulation; experts folded wave by wave), so it is held
-    to the oracle's down projection of the same intermediate.  Zipf routing over
-    16 experts puts more slots on popular experts than one slot group holds, and
-    two tokens repeat an expert (one of them three times).  Reruns are
-    bit-identical; permuting the tokens permutes the output rows exactly (each
-    result column of the matrix instruction depends only on its own slot), and
-    so does reversing the top-k order of tokens without a repeated expert."""
+    matrix core's FP32 accumulation; each token's slots folded in expert
+    order), so it is held to the oracle's down projection of the same
+    intermediate.  Zipf routing over 16 experts puts more slots on popular
+    experts than one slot group holds, and two tokens repeat an expert (one of
+    them three times).  Reruns are bit-identical; permuting the tokens permutes
+    the output rows exactly (each result column of the matrix instruction
+    depends only on its own slot), and so does reversing the top-k order of
+    tokens without a repeated expert."""
     from moe_decode_gate_amd import binding as wd
     spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=96)
     L = gen.make_layer(spec, threads=16)
@@ -333,10 +334,9 @@ def test_down_matrix_core_form(B, W):
 
 @pytest.mark.parametrize("B,S", [(64, 2), (50, 4), (33, 2)])
 def test_down_matrix_core_token_split_16_waves(B, S):
-    """16 waves hold at most 32 tokens per workgroup; with token ranges the
-    batch may be larger.  Held to the oracle's down projection of the same
-    intermediate; each range's rows equal, bit for bit, a run on that range's
-    tokens alone."""
+    """16 waves with token ranges, held to the oracle's down projection of the
+    same intermediate; each range's rows equal, bit for bit, a run on that
+    range's tokens alone."""
     from moe_decode_gate_amd import binding as wd
     spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=98)
     L = gen.make_layer(spec, threads=16)
