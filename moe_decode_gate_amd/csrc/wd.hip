@@ -262,7 +262,8 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     if (I % rows_per_wave) return WD_ERR_UNSUPPORTED;
     const bool tail = (H / 16) % (lpr * cpl) != 0;
     // E8M0 rows start on 4-byte boundaries: each batch's 8 bytes per row in one load
-    const bool sc8 = (H / 32) % 4 == 0 && aligned(s_gu, 4);
+    // rows of a multiple of 8 E8M0 bytes: every batch's 8 bytes lie inside its row, one load
+    const bool sc8 = (H / 32) % 8 == 0 && aligned(s_gu, 4);
     KernelFn fn = c.form == 3   ? (sc8 ? wd::gate_up_mfma_kernel<true> : wd::gate_up_mfma_kernel<false>)
                   : c.form == 2 ? gate_up_expert_fn(cpl, c.rows_per_wave, tail)
                                 : gate_up_fn(cpl, c.rows_per_wave, lpr, tail, c.math, c.weight_loads == 2);
@@ -295,8 +296,8 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         // expert ids packed in 10 bits
         if (B > wd::kDnMfmaMaxB || (long long)B * K > wd::kDnMfmaMaxSlots || E > wd::kDnMfmaMaxE)
             return WD_ERR_UNSUPPORTED;
-        // E8M0 rows start on 4-byte boundaries: each batch's 8 bytes in one load
-        const bool sc8 = (I / 32) % 4 == 0 && aligned(s_d, 4);
+        // rows of a multiple of 8 E8M0 bytes: every batch's 8 bytes lie inside its row, one load
+        const bool sc8 = (I / 32) % 8 == 0 && aligned(s_d, 4);
         // 8 waves: groups of 8 slots; 16 waves (register budget of four waves per SIMD): 4
         void (*fn)(LayerArgs) =
             c.waves_per_block == 16 ? (sc8 ? wd::down_mfma_kernel<16, 4, true> : wd::down_mfma_kernel<16, 4, false>)

@@ -348,8 +348,9 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     // in the compute step zero what they brought) and every batch issues the same loads,
     // so no branch separates them and each wait counts exactly the loads it needs.
     // The E8M0 bytes of a batch (blocks 2 s0 .. 2 s0 + 7 of the lane's row) come in
-    // one 8-byte load when rows start on 4-byte boundaries (SC8: H a multiple of 128
-    // and the scale array 4-byte aligned), else byte by byte.
+    // one 8-byte load when every batch's window lies inside its row (SC8: H a multiple
+    // of 256, so a row holds a multiple of 8 bytes, and the scale array 4-byte aligned),
+    // else byte by byte (a last batch of fewer than 4 steps ends past the row).
     // Codes come coalesced: instruction j reads rows 4 (j % 4) + l / 16 of the gate
     // (j < 4) or up (j >= 4) block, 16 bytes per lane, the 16 lanes of a row covering its
     // 256 bytes of the batch in slot order p = l % 16 holding segment p ^ row (the swizzle
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
             bt.v[j] = ld16(base + (k < H ? k : 0));       // past H: clamped, zeroed when read
         }
         if constexpr (SC8) {
-            const int o = 2 * s0 + 8 <= (int)nbr ? 2 * s0 : 0;   // a batch past the row end uses none of them
+            const int o = 2 * s0 + 8 <= (int)nbr ? 2 * s0 : 0;   // always 2 s0 for H % 256 == 0
             bt.sg = *reinterpret_cast<const uint64_t *>(sg + o);
             bt.su = *reinterpret_cast<const uint64_t *>(su + o);
         } else {
@@ -798,7 +799,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
             st.v[j] = ld16(pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0));   // past I: the row's start, zeroed when read
         }
         const uint8_t *ps = a.s + ((size_t)e * H + (size_t)hb * 16) * (size_t)nbr + soff;
-        if constexpr (SC8) {       // rows of E8M0 bytes start on 4-byte boundaries: one 8-byte load
+        if constexpr (SC8) {       // rows of a multiple of 8 E8M0 bytes (I % 256 == 0): one 8-byte load
             st.sc = *reinterpret_cast<const uint64_t *>(ps + (2 * s0 + 8 <= nbr ? 2 * s0 : 0));
         } else {
             st.sc = 0;

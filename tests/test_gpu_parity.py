@@ -57,6 +57,9 @@ CASES = {
     "b64": (gen.LayerSpec(E=16, K=4, H=256, I=96, seed=505), 64, "softmax", False),
     # H/32 = 9 scale bytes per row: rows start off 4-byte boundaries (byte-wise scale loads)
     "h288": (gen.LayerSpec(E=6, K=2, H=288, I=64, seed=506), 3, "softmax", False),
+    # 12 and 28 scale bytes per row: the matrix-core kernels' last batch of 4 steps is partial and
+    # its 8-byte scale window would end past the row (a wrong window once gave cosine 0.994)
+    "scale_rows_4mod8": (gen.LayerSpec(E=12, K=5, H=384, I=896, seed=507), 40, "softmax", False),
 }
 
 
