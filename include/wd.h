@@ -92,7 +92,9 @@ enum wd_status {
  *                    accumulator.  Both are FP32 accumulation of exact products.
  *   lanes_per_row    gate/up only: 16, 32 or 64 lanes share one row's dot
  *                    products, so a wave works on 64 / lanes_per_row rows at
- *                    once (down: 64)
+ *                    once (down: 64); each lane holds at most 8 chunks of 16
+ *                    elements, so 16 lanes take H <= 2048 and 32 lanes
+ *                    H <= 4096 (the default uses 64 above that)
  *   form             gate/up only: 1 = one wave per (token, slot, row block);
  *                    2 = one wave per (expert, row block) serving every slot
  *                    routed to that expert, each weight row read and

@@ -109,8 +109,10 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
                            (down ? c.rows_per_wave == 1 : (c.lanes_per_row == 0 || c.lanes_per_row == 64));
         c.weight_loads = (!batch && nt_ok) ? 2 : 1;
     }
+    // 32 lanes per row hold at most 8 chunks each (H <= 4096); longer rows take 64
     if (c.lanes_per_row == 0)
-        c.lanes_per_row = (!down && batch && c.form == 1 && c.math == wd::kMathDot2 && c.weight_loads != 2) ? 32 : 64;
+        c.lanes_per_row =
+            (!down && batch && c.form == 1 && c.math == wd::kMathDot2 && c.weight_loads != 2 && H <= 4096) ? 32 : 64;
     if (c.rows_per_wave != 1 && c.rows_per_wave != 2 && c.rows_per_wave != 4 && c.rows_per_wave != 8)
         return WD_ERR_UNSUPPORTED;
     // down on the matrix cores: one workgroup of 8 or 16 waves per block of 16 outputs
@@ -261,7 +263,6 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     const int rows_per_wave = c.form == 3 ? 16 : (64 / lpr) * c.rows_per_wave;
     if (I % rows_per_wave) return WD_ERR_UNSUPPORTED;
     const bool tail = (H / 16) % (lpr * cpl) != 0;
-    // E8M0 rows start on 4-byte boundaries: each batch's 8 bytes per row in one load
     // rows of a multiple of 8 E8M0 bytes: every batch's 8 bytes lie inside its row, one load
     const bool sc8 = (H / 32) % 8 == 0 && aligned(s_gu, 4);
     KernelFn fn = c.form == 3   ? (sc8 ? wd::gate_up_mfma_kernel<true> : wd::gate_up_mfma_kernel<false>)

@@ -4,11 +4,17 @@ device call."""
 import ctypes as C
 
 import pytest
+import torch
 
 from moe_decode_gate_amd import binding as wd
 
 A = 0x10000          # a 16-byte-aligned stand-in address; never dereferenced here
 lib = wd.raw
+
+# Calls that pass every host check return WD_ERR_DEVICE (-5) here, where there is
+# no GPU; on a machine with one they would launch on the stand-in addresses.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-side argument checks with stand-in addresses need a machine without a GPU")
 
 
 def test_every_declared_symbol_is_exported():
@@ -92,6 +98,27 @@ def test_lanes_per_row_limits():
     # grouped rows apply to the gate/up kernel only, and need the row's chunks to fit the lanes
     assert lib.wd_down_ex(A, A, A, A, A, A, 1, 8, 128, 2048, 768, C.byref(wd.Launch(lanes_per_row=16)), None) == -7
     assert lib.wd_gate_up_ex(A, A, A, A, A, 1, 8, 128, 8192, 768, C.byref(wd.Launch(lanes_per_row=16)), None) == -7
+
+
+def test_defaults_cover_every_supported_shape():
+    """With no launch configuration, every size the library accepts gets a
+    compiled kernel variant: the call passes all host checks (and reaches the
+    device check, -5 here) instead of returning WD_ERR_UNSUPPORTED."""
+    n = 0
+    for H in (32, 96, 288, 2048, 4096, 4128, 6304, 8192):
+        for I in (32, 96, 768, 896, 1536, 4096, 8192):
+            for K in (1, 2, 3, 8, 16):
+                if K * I > 16384:
+                    continue
+                for E in (1, 16, 128, 1024, 2000):
+                    if K > E:
+                        continue
+                    for B in (1, 2, 3, 4, 5, 7, 8, 16, 23, 24, 31, 32, 48, 56, 64, 65, 200):
+                        rg = lib.wd_gate_up_ex(A, A, A, A, A, B, K, E, H, I, None, None)
+                        rd = lib.wd_down_ex(A, A, A, A, A, A, B, K, E, H, I, None, None)
+                        assert (rg, rd) == (-5, -5), (B, K, E, H, I, rg, rd)
+                        n += 1
+    assert n > 1000
 
 
 def test_helpers_reject_bad_arguments():

@@ -84,3 +84,71 @@ def test_random_shape_parity(case):
             got = wd.down(act, dt.ids, dt.w, dl.wd, sd_k, cfg=dict(form=3, waves_per_block=8, token_split=S))
             torch.cuda.synchronize()
             assert np.array_equal(bits_of(got), bits_of(base)), (n, S)
+
+
+GU_CFGS = [None, dict(form=1, math=1), dict(form=1, math=2, lanes_per_row=64, rows_per_wave=1),
+           dict(form=1, math=2, lanes_per_row=32, rows_per_wave=4), dict(form=1, math=2, lanes_per_row=16, rows_per_wave=2),
+           dict(form=1, math=2, weight_loads=2), dict(form=2), dict(form=3)]
+DN_CFGS = [None, dict(math=1, rows_per_wave=1), dict(math=2, rows_per_wave=2), dict(math=1, rows_per_wave=4),
+           dict(math=2, rows_per_wave=8), dict(math=1, rows_per_wave=8), dict(math=2, rows_per_wave=1, weight_loads=2),
+           dict(form=3, waves_per_block=16, token_split=2), dict(form=3, waves_per_block=8, token_split=1)]
+
+
+def _cases_wide(n=12, seed=20261203):
+    """Wider ranges: up to 1024 experts, top-16, H up to 8192, I up to 4096, and
+    tokens that name one expert twice."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.choice([1, 3, 17, 64, 200, 513, 1024]))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        H = 32 * int(rng.integers(1, 257))
+        I = 32 * int(rng.integers(1, 129))
+        B = int(rng.integers(1, 65))
+        if K * I > 16384 or B * K * H * I > 2 ** 28 or E * 3 * H * I > 3 * 2 ** 29:
+            continue
+        dup = K >= 2 and rng.random() < 0.5
+        gu = GU_CFGS[int(rng.integers(0, len(GU_CFGS)))]
+        dn = DN_CFGS[int(rng.integers(0, len(DN_CFGS)))]
+        out.append((len(out), E, K, H, I, B, dup, gu, dn, int(rng.integers(1, 2 ** 31))))
+    return out
+
+
+WIDE = _cases_wide()
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[f"w{c[0]}" for c in WIDE])
+def test_random_wide_parity(case):
+    """Every launch family on the wider shapes; a drawn configuration that the
+    library does not build for the shape (status WD_ERR_UNSUPPORTED, checked on
+    the host) runs under the defaults instead."""
+    from moe_decode_gate_amd import binding as wd
+    n, E, K, H, I, B, dup, cfg_gu, cfg_dn, seed = case
+    log(f"[case] w{n}: E={E} K={K} H={H} I={I} B={B} dup={dup} gate/up={cfg_gu} down={cfg_dn}")
+    spec = gen.LayerSpec(E=E, K=K, H=H, I=I, seed=seed)
+    t = gen.make_tokens(spec, B, routing="softmax")
+    if dup:
+        t.ids[::2, 1] = t.ids[::2, 0]                   # every other token names its first expert twice
+    L = gen.make_layer(spec, experts=t.ids.ravel(), threads=16)
+    dl, dt = DevLayer(L), DevTokens(t)
+    y64, act_o = oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd, nthreads=16)
+    k = unit_shift(y64)
+    sd_k = shifted(dl.sd, k)
+
+    def run(cfg, fn, what):
+        try:
+            return fn(cfg)
+        except wd.WDError as err:
+            if err.status != -7:
+                raise
+            log(f"[case] w{n}: {what} {cfg} not built for this shape; defaults instead")
+            return fn(None)
+
+    act = run(cfg_gu, lambda c: wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu, cfg=c), "gate/up")
+    out = run(cfg_dn, lambda c: wd.down(act, dt.ids, dt.w, dl.wd, sd_k, cfg=c), "down")
+    torch.cuda.synchronize()
+    frac, ulps, within = act_flip_stats(bits_of(act), act_o)
+    log(f"[act] w{n}: flip fraction {frac:.2e}, max {ulps:.2f} ulp, within bound: {within}")
+    assert frac <= 2e-3 and within, (frac, ulps, within)
+    y_of_gpu_act = oracle.down(bits_of(act), t.ids, t.w, L.wd, L.sd, nthreads=16)
+    assert_output_parity(bits_of(out), y_of_gpu_act * 2.0 ** k, f"w{n} layer vs oracle(act_gpu)")
