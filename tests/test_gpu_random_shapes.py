@@ -94,7 +94,7 @@ DN_CFGS = [None, dict(math=1, rows_per_wave=1), dict(math=2, rows_per_wave=2), d
            dict(form=3, waves_per_block=16, token_split=2), dict(form=3, waves_per_block=8, token_split=1)]
 
 
-def _cases_wide(n=12, seed=20261203):
+def _cases_wide(n=12, seed=20261203, bmax=64):
     """Wider ranges: up to 1024 experts, top-16, H up to 8192, I up to 4096, and
     tokens that name one expert twice."""
     rng = np.random.default_rng(seed)
@@ -104,7 +104,7 @@ def _cases_wide(n=12, seed=20261203):
         K = int(rng.integers(1, min(E, 16) + 1))
         H = 32 * int(rng.integers(1, 257))
         I = 32 * int(rng.integers(1, 129))
-        B = int(rng.integers(1, 65))
+        B = int(rng.integers(1, bmax + 1))
         if K * I > 16384 or B * K * H * I > 2 ** 28 or E * 3 * H * I > 3 * 2 ** 29:
             continue
         dup = K >= 2 and rng.random() < 0.5
@@ -115,6 +115,8 @@ def _cases_wide(n=12, seed=20261203):
 
 
 WIDE = _cases_wide()
+# batches past the matrix-core down's 64 tokens (token form only)
+WIDE += [(len(WIDE) + c[0],) + c[1:] for c in _cases_wide(n=6, seed=20261204, bmax=300) if c[5] > 64]
 
 
 @pytest.mark.parametrize("case", WIDE, ids=[f"w{c[0]}" for c in WIDE])
