@@ -404,3 +404,31 @@ def test_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits_of(out), eager), i
+
+
+def _random_cases(n=8, seed=20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.integers(1, 301))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        H = 32 * int(rng.integers(1, 129))
+        I = 32 * int(rng.integers(1, 65))
+        B = int(rng.integers(1, 65))
+        if B * K * H * I > 2 ** 27:
+            continue
+        routing = "zipf" if rng.random() < 0.4 else "softmax"
+        out.append((f"r{len(out)}", gen.LayerSpec(E=E, K=K, H=H, I=I, seed=int(rng.integers(1, 2 ** 31))), B, routing))
+    return out
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("name,spec,B,routing", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shapes(name, spec, B, routing):
+    """Seeded random layer shapes, batch sizes and routing laws: every stage
+    and the end-to-end output held to the oracle as above."""
+    t = gen.make_tokens(spec, B, routing=routing)
+    L = gen.make_layer(spec, experts=t.ids.ravel(), threads=16)
+    full_check(name, spec, t, L)
