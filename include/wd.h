@@ -124,7 +124,7 @@ enum wd_status {
  *                    B * K <= 512; E <= 1024).  Default: 3
  *                    when B <= 64, B * K <= 512, E <= 1024, none of
  *                    rows_per_wave, lanes_per_row, math, weight_loads,
- *                    waves_per_block is set and B >= 32 (B >= 8 when
+ *                    waves_per_block is set and B >= 24 (B >= 8 when
  *                    K * I > 6144), else 1; with form 3 the default is
  *                    16 waves with several token ranges, else 8.
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
@@ -171,7 +171,7 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
  * "Down Kernel"): one wave per (token b, output dim h).  The wave walks the K
  * routed experts' rows Wd[e_k, h, :], folds topk_w[b,k] into one FP32
  * accumulator, reduces across its 64 lanes with DPP row operations and one
- * lane read (no LDS) and writes out[b,h] = BF16(acc).  From B = 32 (B = 8
+ * lane read (no LDS) and writes out[b,h] = BF16(acc).  From B = 24 (B = 8
  * when K * I > 6144) the default is the expert form on the matrix cores
  * (wd_launch.form 3), which reads each Wd row block once per token range for
  * all the tokens of the range routed to its expert. */

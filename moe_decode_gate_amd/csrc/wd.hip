@@ -62,17 +62,17 @@ int check_dims(int B, int K, int E, int H, int I) {
 //          75 against 136 us at B = 64);
 //   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
 //   down, B 3..5: 4 rows per wave, FP32 math; B 6..55: 8 rows per wave;
-//   down, B 32..64 (B * K <= 512): the expert form on the matrix cores, one
+//   down, B 24..64 (B * K <= 512): the expert form on the matrix cores, one
 //          16-wave workgroup per 16 outputs and token range, the batch cut in
-//          two ranges when H / 16 workgroups would leave CUs idle (47 against
-//          49 us at B = 32, 51 against 60 at B = 40, 60 against 84 at B = 64;
-//          at B = 24 the token form wins, 39 against 42 us).
+//          two ranges when H / 16 workgroups would leave CUs idle (equal at
+//          B = 24, 42 against 46 us at B = 28, 44 against 49 at B = 32, 58
+//          against 83 at B = 64; at B = 16 the token form wins, 32 against 32.3).
 // The token-form down keeps K * I / 1024 act chunks per lane in registers; past
 // 6 (K * I > 6144) its FP32-math variants need more than 200 VGPRs (one or two
-// waves per SIMD), so there it takes the BF16-pair math, two rows per wave at
+// waves per SIMD), so there it takes the BF16-pair math, 2 B rows per wave at
 // B <= 2 (the 128-expert / top-8 / H 4096 / I 1536 layer: 10.0 against 12.4 us
-// at B = 1) and, from B = 8, the matrix-core form (46 against 49 us at B = 8,
-// where the FP32 math took 225 us).
+// at B = 1, 16.1 against 17.5 at B = 2) and, from B = 8, the matrix-core form
+// (43 against 49 us at B = 8, where the FP32 math took 225 us).
 int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, wd_launch *out) {
     wd_launch c = in ? *in : wd_launch{};
     const bool batch = down ? B >= 3 : B >= 5;
@@ -81,14 +81,14 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     // is read once per expert however many tokens share it
     const bool untuned = c.rows_per_wave == 0 && c.lanes_per_row == 0 && c.math == 0 && c.weight_loads == 0;
     if (c.form == 0) {
-        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 32) && B <= wd::kDnMfmaMaxB &&
+        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 24) && B <= wd::kDnMfmaMaxB &&
                                      (long long)B * K <= wd::kDnMfmaMaxSlots && E <= wd::kDnMfmaMaxE
                                : untuned && B >= 24;
         c.form = mfma ? 3 : 1;
     }
     if (c.form == 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
     if (c.rows_per_wave == 0)
-        c.rows_per_wave = !batch ? (down && wide ? 2 : 1) : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
+        c.rows_per_wave = !batch ? (down && wide ? 2 * B : 1) : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
     if (down && c.form == 3) {
         // two token ranges when one workgroup per 16 outputs would leave CUs idle, with 16
         // waves (Qwen-3 layer, B = 32: 44 us against 56 with 8); one range with 8 waves, which
