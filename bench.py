@@ -483,8 +483,8 @@ def main():
     ap.add_argument("--compare-batches", default="1,2,4,8,16,32,64", help="batch sizes of the comparison")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs the layer "
-              "on a single MI355X and has no multi-GPU path)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on a single "
+              "MI355X; there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -47,7 +47,7 @@
  * its slot's intermediate row is written as NaN and every output of its token
  * becomes NaN.
  *
- * Size limits of this build: H and I multiples of 32, H <= 8192,
+ * Size limits of this library: H and I multiples of 32, H <= 8192,
  * K * I <= 16384, B * K * I < 2^31.  B = 0 is accepted and launches nothing
  * (activation/output/routing pointers may then be NULL).
  */
@@ -69,7 +69,7 @@ enum wd_status {
     WD_ERR_WORKSPACE = -4,   /* workspace smaller than wd_workspace_bytes() */
     WD_ERR_DEVICE = -5,      /* no HIP device, or the current device is not gfx950 */
     WD_ERR_LAUNCH = -6,      /* the kernel launch was rejected by the HIP runtime */
-    WD_ERR_UNSUPPORTED = -7  /* sizes beyond this build's limits, or a bad launch configuration */
+    WD_ERR_UNSUPPORTED = -7  /* sizes beyond the library's limits, or a bad launch configuration */
 };
 
 /* Launch configuration (tuning and timing).  Any integer field left 0 takes
