@@ -532,7 +532,10 @@ def main():
         cos32, err32, ymax32 = sampled_parity(oracle, L, w32, [0, steps - 1])
         r32.update(parity_cos_min=cos32, parity_max_abs_err=err32, parity_max_abs_y=ymax32,
                    frac_of_measured_read_peak=r32["layer_GBps_graph"] / peak,
-                   accuracy=accuracy(oracle, L, w32, [0, steps - 1]))
+                   accuracy=accuracy(oracle, L, w32, [0, steps - 1]),
+                   roofline={"bound": "hbm", "achieved": r32["gate_up_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                             "frac": r32["gate_up_GBps"] / PEAK_HBM_GBPS, "kernel": "gate_up",
+                             "traffic": load_traffic("gate_up_qwen3_b32")})
         eprint(f"[bench] B=32: {json.dumps(r32)}")
         del w32
         torch.cuda.empty_cache()
