@@ -451,20 +451,29 @@ def accuracy(oracle, L, work: Workload, steps_to_check):
                 reference="FP64 layer, exact MXFP8 weights, unrounded intermediate and output")
 
 
-def cpu_baseline(oracle, L, gen, B, seconds=12.0):
+def cpu_baseline(oracle, L, gen, B, seconds=12.0, single_seconds=4.0):
     """The oracle as it stands, on every host core, over fresh seeded batches
-    of the same workload until about `seconds` of CPU work have run."""
+    of the same workload until about `seconds` of CPU work have run; and the
+    same on one thread for about `single_seconds`."""
     spec = L.spec
-    n_tok, t_used, s = 0, 0.0, 0
-    while t_used < seconds:
-        t = gen.make_tokens(spec, B, step=10_000 + s)
-        t0 = time.perf_counter()
-        oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
-        t_used += time.perf_counter() - t0
-        n_tok += B
-        s += 1
+
+    def run(nthreads, budget, first_step):
+        n_tok, t_used, s = 0, 0.0, 0
+        while t_used < budget:
+            t = gen.make_tokens(spec, B, step=first_step + s)
+            t0 = time.perf_counter()
+            oracle.moe_decode(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd, nthreads=nthreads)
+            t_used += time.perf_counter() - t0
+            n_tok += B
+            s += 1
+        return n_tok, t_used, s
+
+    n_tok, t_used, s = run(0, seconds, 10_000)
+    n1, t1, _ = run(1, single_seconds, 20_000)
     return dict(value=n_tok / t_used, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
-                sample=f"{n_tok} tokens in {s} batches of B={B} on the same layer, {t_used:.1f} s")
+                sample=f"{n_tok} tokens in {s} batches of B={B} on the same layer, {t_used:.1f} s",
+                single_thread=dict(value=n1 / t1, unit="tokens/s", cores=1,
+                                   sample=f"{n1} tokens in batches of B={B}, {t1:.1f} s"))
 
 
 def main():
