@@ -468,9 +468,10 @@ def cpu_baseline(oracle, L, gen, B, seconds=12.0, single_seconds=4.0):
             s += 1
         return n_tok, t_used, s
 
-    n_tok, t_used, s = run(0, seconds, 10_000)
+    cores = oracle.max_threads()            # the oracle's thread count persists per call: set it each time
     n1, t1, _ = run(1, single_seconds, 20_000)
-    return dict(value=n_tok / t_used, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
+    n_tok, t_used, s = run(cores, seconds, 10_000)
+    return dict(value=n_tok / t_used, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{n_tok} tokens in {s} batches of B={B} on the same layer, {t_used:.1f} s",
                 single_thread=dict(value=n1 / t1, unit="tokens/s", cores=1,
                                    sample=f"{n1} tokens in batches of B={B}, {t1:.1f} s"))
