@@ -154,3 +154,37 @@ def test_random_wide_parity(case):
     assert frac <= 2e-3 and within, (frac, ulps, within)
     y_of_gpu_act = oracle.down(bits_of(act), t.ids, t.w, L.wd, L.sd, nthreads=16)
     assert_output_parity(bits_of(out), y_of_gpu_act * 2.0 ** k, f"w{n} layer vs oracle(act_gpu)")
+
+
+@pytest.mark.parametrize("case", CASES[:8], ids=[f"c{c[0]}" for c in CASES[:8]])
+def test_random_fused_entry_and_graph(case):
+    """wd_moe_decode (both kernels, library defaults, one workspace) gives the
+    two separate calls' output bit for bit, eagerly and replayed three times
+    from a HIP graph with eager work in between."""
+    from moe_decode_gate_amd import binding as wd
+    n, E, K, H, I, B, routing, _, _, seed = case
+    log(f"[case] fused c{n}: E={E} K={K} H={H} I={I} B={B} routing={routing}")
+    spec = gen.LayerSpec(E=E, K=K, H=H, I=I, seed=seed)
+    t = gen.make_tokens(spec, B, routing=routing)
+    L = gen.make_layer(spec, experts=t.ids.ravel(), threads=16)
+    dl, dt = DevLayer(L), DevTokens(t)
+    _, ref = run_layer(dl, dt)
+    ref = bits_of(ref)
+    ws = torch.empty(max(wd.workspace_bytes(B, K, I), 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    wd.moe_decode(dt.x, dt.ids, dt.w, dl.wgu, dl.sgu, dl.wd, dl.sd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), ref)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            wd.moe_decode(dt.x, dt.ids, dt.w, dl.wgu, dl.sgu, dl.wd, dl.sd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out), ref)
