@@ -652,6 +652,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __shared__ float lw[kDnMfmaMaxSlots];              // router weights of the workgroup's slots, by slot - sl0
     __shared__ int16_t lord[kDnMfmaMaxSlots];          // per token of the range: its slots in fold order
     __shared__ uint8_t lused[kDnMfmaMaxE];             // experts some slot of the range is routed to
+    __shared__ uint8_t loth[kDnMfmaMaxE];              // experts some slot of another range is routed to
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
     const int hb = (int)blockIdx.x % a.nrowblk;
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         const int sl = 64 * u + lane;
         idv[u] = sl >= sl0 && sl < sl1 ? a.ids[sl] : -1;
     }
-    for (int t = (int)threadIdx.x; t < E; t += 64 * W) lused[t] = 0;
+    for (int t = (int)threadIdx.x; t < E; t += 64 * W) lused[t] = loth[t] = 0;
     const int K = a.K;
     for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) {
         lw[t] = a.tw[sl0 + t];
@@ -697,7 +698,14 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
 #pragma unroll
     for (int u = 0; u < kDnIdRegs; ++u)
         if ((unsigned)idv[u] < (unsigned)E) lused[idv[u]] = 1;
-    __syncthreads();                                   // lused, lw, lord complete
+    if (a.tsplit > 1) {
+        const int BK = a.B * K;
+        for (int t = (int)threadIdx.x; t < BK; t += 64 * W) {
+            const int id = t >= sl0 && t < sl1 ? -1 : a.ids[t];
+            if ((unsigned)id < (unsigned)E) loth[id] = 1;
+        }
+    }
+    __syncthreads();                                   // lused, loth, lw, lord complete
 
     // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
     uint64_t bad_tok = 0;
@@ -712,13 +720,19 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         }
     }
 
-    // the wave's experts (routed experts n = wv, wv + W, ... in expert order) and their
-    // slots, in expert then slot order
+    // the wave's experts (routed experts n = wv, wv + W, ... in turn) and their slots, in
+    // expert then slot order.  Experts that other token ranges use as well come first, in
+    // expert order, then the rest: the workgroups of the other ranges of this output block
+    // stream the shared rows at about the same time, so the later reads find them in the
+    // L2.  (The order of experts changes no result: each slot's products are kept and
+    // folded per token in expert order at the end.)
     int nx = 0;
     {
         int ns = 0, seen = 0;
+        for (int pass = 0; pass < 2; ++pass)
         for (int base = 0; base < E; base += 64) {
-            const bool used = base + lane < E && lused[base + lane] != 0;
+            const bool used = base + lane < E && lused[base + lane] != 0 &&
+                              (loth[base + lane] != 0) == (pass == 0);
             const uint64_t um = __builtin_amdgcn_ballot_w64(used);
             const int n = seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
             uint64_t mine = __builtin_amdgcn_ballot_w64(used && n % W == wv);
