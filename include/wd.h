@@ -69,8 +69,14 @@ enum wd_status {
     WD_ERR_WORKSPACE = -4,   /* workspace smaller than wd_workspace_bytes() */
     WD_ERR_DEVICE = -5,      /* no HIP device, or the current device is not gfx950 */
     WD_ERR_LAUNCH = -6,      /* the kernel launch was rejected by the HIP runtime */
-    WD_ERR_UNSUPPORTED = -7  /* sizes beyond the library's limits, or a bad launch configuration */
+    WD_ERR_UNSUPPORTED = -7, /* sizes beyond the library's limits, or a bad launch configuration */
+    WD_ERR_SCRATCH = -8      /* wd_moe_decode_noalloc: act[B,K,I] larger than WD_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Size of the device-resident scratch array that wd_moe_decode_noalloc uses
+ * for act[B,K,I] (B * K * I * 2 bytes must fit): 4 MiB, e.g. 341 tokens of
+ * the 128-expert / top-8 / I 768 layer, 128 tokens at K * I = 16384. */
+#define WD_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Launch configuration (tuning and timing).  Any integer field left 0 takes
  * the library default for the call's sizes.
@@ -189,6 +195,25 @@ int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_
                   const uint8_t *w_d, const uint8_t *s_d,
                   void *workspace, size_t workspace_bytes, uint16_t *out,
                   int B, int K, int E, int H, int I, void *stream);
+
+/* Whole layer without any allocation, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same kernels, launch defaults and
+ * results (bit for bit) as wd_moe_decode; act[B,K,I] lives in a static device
+ * array of WD_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends (its address is looked up once per device, on the
+ * first call with that device current).  The caller passes inputs and `out`
+ * as for wd_moe_decode.  Calls no hipMalloc, hipFree or allocating library
+ * routine.  Returns WD_ERR_SCRATCH, launching nothing, when B * K * I * 2 >
+ * WD_NOALLOC_SCRATCH_BYTES.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams, or several host
+ * threads without ordering) race on it and must be serialised by the caller;
+ * calls in order on one stream are safe.  Nothing in the array needs to start
+ * at zero (gate/up writes every act element the down kernel reads). */
+int wd_moe_decode_noalloc(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                          const uint8_t *w_gu, const uint8_t *s_gu,
+                          const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
+                          int B, int K, int E, int H, int I, void *stream);
 
 /* Router (top-k gating ahead of the layer; the pages name it as routing each
  * token to 8 of 128 experts: the Chinese summary's 传统路径的困境 section, p2

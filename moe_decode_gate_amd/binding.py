@@ -27,7 +27,8 @@ _lib = C.CDLL(LIB_PATH)
 
 WD_OK = 0
 STATUS = {0: "WD_OK", -1: "WD_ERR_NULL", -2: "WD_ERR_DIMS", -3: "WD_ERR_ALIGN", -4: "WD_ERR_WORKSPACE",
-          -5: "WD_ERR_DEVICE", -6: "WD_ERR_LAUNCH", -7: "WD_ERR_UNSUPPORTED"}
+          -5: "WD_ERR_DEVICE", -6: "WD_ERR_LAUNCH", -7: "WD_ERR_UNSUPPORTED", -8: "WD_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 4 << 20      # WD_NOALLOC_SCRATCH_BYTES in include/wd.h
 
 
 class WDError(RuntimeError):
@@ -65,6 +66,7 @@ _sig = {
     "wd_down": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "wd_down_ex": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, C.POINTER(Launch), _P]),
     "wd_moe_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _I, _I, _I, _I, _I, _P]),
+    "wd_moe_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "wd_workspace_bytes": (_S, [_I, _I, _I]),
     "wd_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "wd_status_string": (C.c_char_p, [_I]),
@@ -215,6 +217,25 @@ def moe_decode(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, out=None, workspace=No
                             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
                             B, K, E, H, I, _stream(stream))
     _check(rc, "wd_moe_decode")
+    return out
+
+
+def moe_decode_noalloc(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, out=None, stream=None):
+    """The whole layer through wd_moe_decode_noalloc: the intermediate lives in
+    the library's per-GPU scratch array (no workspace).  Calls overlapping in
+    time on one GPU race on that array."""
+    E, H, I = _dims(w_gu)
+    B, K = topk_ids.shape
+    _dev(x, "x", _BF16, (B, H)); _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,), (B, K))
+    _dev(w_gu, "w_gu", _U8, (E, 2 * I, H)); _dev(s_gu, "s_gu", _U8, (E, 2 * I, H // 32))
+    _dev(w_d, "w_d", _U8, (E, H, I)); _dev(s_d, "s_d", _U8, (E, H, I // 32))
+    if out is None:
+        out = torch.empty((B, H), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", _BF16, (B, H))
+    rc = _lib.wd_moe_decode_noalloc(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_gu), _ptr(s_gu), _ptr(w_d),
+                                    _ptr(s_d), _ptr(out), B, K, E, H, I, _stream(stream))
+    _check(rc, "wd_moe_decode_noalloc")
     return out
 
 

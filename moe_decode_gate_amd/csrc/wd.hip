@@ -398,6 +398,63 @@ int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_
     return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, true);
 }
 
+}  // extern "C"
+
+// ---- the entry point that allocates nothing ---------------------------------
+//
+// wd_moe_decode_noalloc keeps the intermediate act[B,K,I] in this file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy for the life of the process.  In host code the name
+// `scratch` is only a host-side stand-in: its device address is looked up with
+// hipGetSymbolAddress once per device (with that device current) and only that
+// address is handed to the kernels.
+static __device__ __align__(256) uint8_t scratch[WD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void *> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of the current device's scratch array (nullptr on failure).
+void *scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) { (void)hipGetLastError(); return nullptr; }
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // two threads racing here both store the same address
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wd_moe_decode_noalloc(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                          const uint8_t *w_gu, const uint8_t *s_gu, const uint8_t *w_d, const uint8_t *s_d,
+                          uint16_t *out, int B, int K, int E, int H, int I, void *stream) {
+    int rc = check_dims(B, K, E, H, I);
+    if (rc) return rc;
+    if (!w_gu || !s_gu || !w_d || !s_d) return WD_ERR_NULL;
+    if (B > 0 && (!x || !topk_ids || !topk_w || !out)) return WD_ERR_NULL;
+    if (wd_workspace_bytes(B, K, I) > (size_t)WD_NOALLOC_SCRATCH_BYTES) return WD_ERR_SCRATCH;
+    if (!aligned(w_gu, 16) || !aligned(w_d, 16) ||
+        (B > 0 && (!aligned(x, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(out, 2))))
+        return WD_ERR_ALIGN;
+    if (B == 0) return WD_OK;
+    if ((rc = check_device())) return rc;
+    uint16_t *act = static_cast<uint16_t *>(scratch_ptr());
+    if (!act) return WD_ERR_DEVICE;
+    // gate/up writes every act element the down kernel reads, so nothing is cleared
+    rc = gate_up_impl(x, topk_ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, true);
+    if (rc) return rc;
+    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, true);
+}
+
 const char *wd_status_string(int status) {
     switch (status) {
         case WD_OK: return "ok";
@@ -408,6 +465,8 @@ const char *wd_status_string(int status) {
         case WD_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
         case WD_ERR_LAUNCH: return "kernel launch failed";
         case WD_ERR_UNSUPPORTED: return "unsupported sizes or launch configuration (H <= 8192, K*I <= 16384)";
+        case WD_ERR_SCRATCH:
+            return "act[B,K,I] (B*K*I*2 bytes) exceeds the no-allocation scratch (WD_NOALLOC_SCRATCH_BYTES = 4 MiB)";
     }
     return "unknown status";
 }

@@ -25,7 +25,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert lib.wd_status_string(s)
     assert lib.wd_status_string(123) == b"unknown status"
 
@@ -247,3 +247,25 @@ def test_matrix_core_form_limits():
     assert gux(form=3, token_split=2) == -7 and gux(token_split=2) == -7
     # the default picks it only where it applies; a tuned field keeps the token form
     assert dnx(B=64, E=2048) == -5 and dnx(B=64, K=16) == -5 and dnx(B=64, waves_per_block=2) == -5
+
+
+def na(**kw):
+    d = dict(x=A, ids=A, tw=A, wgu=A, sgu=A, wd=A, sd=A, out=A, B=1, K=8, E=128, H=2048, I=768)
+    d.update(kw)
+    return lib.wd_moe_decode_noalloc(d["x"], d["ids"], d["tw"], d["wgu"], d["sgu"], d["wd"], d["sd"], d["out"],
+                                     d["B"], d["K"], d["E"], d["H"], d["I"], None)
+
+
+def test_noalloc_host_checks():
+    """The no-allocation entry point: the act[B,K,I] of the call must fit the
+    4 MiB scratch (341 tokens of the 128-expert / top-8 / I 768 layer); larger
+    calls return WD_ERR_SCRATCH before any device call."""
+    assert wd.NOALLOC_SCRATCH_BYTES == 4 << 20
+    assert na(B=341) == -5                              # fits: reaches the device check
+    assert na(B=342) == -8
+    assert na(B=128, K=8, I=2048) == -5 and na(B=129, K=8, I=2048) == -8
+    assert lib.wd_status_string(-8) and b"scratch" in lib.wd_status_string(-8)
+    assert na(B=0, x=None, ids=None, tw=None, out=None) == 0
+    assert na(out=None) == -1 and na(wd=None) == -1
+    assert na(x=A + 8) == -3 and na(out=A + 1) == -3
+    assert na(H=100) == -2 and na(K=32, I=1024) == -7
