@@ -13,11 +13,15 @@ Timing hygiene: the layer's weights are replicated into R distinct device
 copies and step s runs on copy s % R with its own routing, so consecutive
 steps never find their expert rows in the 256 MB last-level cache.
 
-  value            tokens/s over exactly --steps steps, replayed from one HIP
-                   graph, bracketed by synchronisation
+  value            tokens/s: B / the median per-step time over >= 100 replays
+                   (and >= 0.2 s) of one HIP graph of >= 200 layer steps (a
+                   multiple of --steps, cycling the --steps batches), each
+                   replay timed by HIP events
   roofline         the dominant kernel (gate/up): algorithmic bytes per launch
                    (unique routed experts x gate/up codes + E8M0 scales) divided
-                   by its mean duration from HIP events around each launch
+                   by its mean execution time from HIP events recorded by its
+                   own dispatch; under graph_node the same bytes over its time
+                   per node in a graph of that kernel alone
   hbm_read_peak    best-of-10 contiguous-read bandwidth of a 16-byte-load
                    kernel over a 4 GiB buffer, measured in the same run
   cpu_baseline     the CPU oracle on this host's cores on a bounded sample
@@ -41,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
+GRAPH_MIN_STEPS = 200          # layer steps per timed graph (at least)
 
 
 def eprint(*a):
@@ -106,52 +111,130 @@ class Workload:
         self.unique = np.array([np.unique(self.host_ids[s]).size for s in range(steps)])
         self.wd = wd
 
-    def step(self, s, which="both", cfg=None):
-        wgu, sgu, wdn, sdn = self.copies[s % len(self.copies)]
+    def step(self, j, which="both", cfg_gu=None, cfg_dn=None, batch=None):
+        """Layer step j on weight copy j % R with batch `batch` (default j)."""
+        s = j if batch is None else batch
+        wgu, sgu, wdn, sdn = self.copies[j % len(self.copies)]
         if which in ("both", "gate_up"):
-            self.wd.gate_up(self.x[s], self.ids[s], wgu, sgu, act=self.act[s], cfg=cfg)
+            self.wd.gate_up(self.x[s], self.ids[s], wgu, sgu, act=self.act[s], cfg=cfg_gu)
         if which in ("both", "down"):
-            self.wd.down(self.act[s], self.ids[s], self.w[s], wdn, sdn, out=self.out[s], cfg=cfg)
+            self.wd.down(self.act[s], self.ids[s], self.w[s], wdn, sdn, out=self.out[s], cfg=cfg_dn)
 
 
-def measure(torch, wd, work: Workload, steps: int, warmup: int):
-    spec = work.spec
-    # warmup (eager), also initialises the library's device check outside capture
-    for s in range(warmup):
-        work.step(s % work.steps)
-    torch.cuda.synchronize()
-
-    # --- timed region 1: exactly `steps` steps replayed from one HIP graph
+def capture(torch, fn):
+    """One HIP graph of everything fn() launches (on a side stream, as torch's
+    capture requires)."""
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g, stream=cap):
-            for s in range(steps):
-                work.step(s)
+            fn()
     torch.cuda.synchronize()
-    g.replay()                                  # one untimed replay (graph upload)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / steps
+    return g
 
-    # --- timed region 2: per-kernel durations from HIP events that the kernels'
-    # own dispatches record (hipExtLaunchKernelGGL) on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+def time_replays(torch, wd, g, warm=20, min_replays=100, min_seconds=0.2, max_replays=4000, chunk=50):
+    """Replays of one captured graph, each bracketed by HIP events on the stream
+    that launches it: `warm` untimed replays, then at least `min_replays` and at
+    least `min_seconds` of timed ones.  The replays are queued in chunks behind a
+    sleeping wave, so the host is ahead of the GPU and each event pair measures
+    the GPU's time for that replay (its nodes and the gaps between them).
+    Returns the per-replay durations in microseconds."""
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(); g.replay(); e1.record()
+    torch.cuda.synchronize()
+    est_s = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+    n = int(min(max_replays, max(min_replays, -(-min_seconds // est_s))))
+    us = []
+    sleep_units = 20000                 # ~70 ms before the first chunk; then twice the measured enqueue time
+    while len(us) < n:
+        m = min(chunk, n - len(us))
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(m + 1)]
+        wd.gpu_sleep(sleep_units)
+        t0 = time.perf_counter()
+        evs[0].record()
+        for i in range(m):
+            g.replay()
+            evs[i + 1].record()
+        host_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        us += [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(m)]
+        # one sleep unit is 8192 shader clocks, about 3.4 us
+        sleep_units = int(min(40000, 600 + 2 * host_s / 3.4e-6))
+    return np.array(us)
+
+
+def spread(per_step_us):
+    q = np.percentile(per_step_us, [0, 10, 50, 90, 100])
+    return dict(min=float(q[0]), p10=float(q[1]), median=float(q[2]), p90=float(q[3]), max=float(q[4]))
+
+
+def measure(torch, wd, work: Workload, steps: int, warmup: int, gu_cfg=None, dn_cfg=None):
+    """Step time and per-kernel durations of one workload.
+
+    Headline: G layer steps captured in one HIP graph (G = the smallest
+    multiple of `steps` that is at least 200; step j runs batch j % steps on
+    weight copy j % R), replayed at least 100 times (and for at least 0.2 s)
+    after 20 warm-up replays; each replay is timed by HIP events; the per-step
+    time is the median replay time divided by G.  Holding G at 200 or more
+    keeps the graph's own start-up (a few microseconds per replay) below 0.1%
+    of the replay, so the result does not depend on `steps`.
+
+    Per kernel, two figures: (1) the kernel's execution time, from HIP events
+    recorded by its own dispatch (hipExtLaunchKernelGGL) over at least 200
+    eager launches queued behind a sleeping wave (mean, after one untimed
+    pass); (2) its time per node in a graph of that kernel alone (G launches,
+    replayed as above), which adds the dispatch gap between consecutive
+    nodes, the regime the headline runs in.  The two graph figures add up to
+    the step time."""
+    spec = work.spec
+    # warmup (eager), also initialises the library's device check outside capture
+    for s in range(warmup):
+        work.step(s % work.steps, cfg_gu=gu_cfg, cfg_dn=dn_cfg)
+    torch.cuda.synchronize()
+
+    G = -(-GRAPH_MIN_STEPS // steps) * steps          # graph steps: a multiple of `steps`, >= 200
+
+    # --- timed region: the layer graph
+    g = capture(torch, lambda: [work.step(j, cfg_gu=gu_cfg, cfg_dn=dn_cfg, batch=j % steps) for j in range(G)])
+    rep_us = time_replays(torch, wd, g)
+    per_step = rep_us / G
+    us_per_step = float(np.median(per_step))
+    del g
+
+    # --- per-kernel time per node in single-kernel graphs (same replay timing)
+    node_us = {}
+    for which, cfg in (("gate_up", gu_cfg), ("down", dn_cfg)):
+        kw = {"cfg_gu" if which == "gate_up" else "cfg_dn": cfg}
+        g = capture(torch, lambda: [work.step(j, which, batch=j % steps, **kw) for j in range(G)])
+        node_us[which] = float(np.median(time_replays(torch, wd, g, min_replays=50))) / G
+        del g
+
+    # --- per-kernel execution time from HIP events that the kernels' own
+    # dispatches record (hipExtLaunchKernelGGL) on the launch stream: one
+    # untimed pass over the batches, then G timed launches of each kernel
+    for s in range(steps):
+        work.step(s, cfg_gu=gu_cfg, cfg_dn=dn_cfg)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(G)]
     for row in evs:
         for e in row:
             e.record()                          # materialise the hipEvent_t
     torch.cuda.synchronize()
-    wd.gpu_sleep(20000)                         # ~70 ms: lets the host queue the steps ahead
-    for s in range(steps):
-        work.step(s, "gate_up", wd.Launch(start_event=evs[s][0].cuda_event, stop_event=evs[s][1].cuda_event))
-        work.step(s, "down", wd.Launch(start_event=evs[s][2].cuda_event, stop_event=evs[s][3].cuda_event))
+    wd.gpu_sleep(20000)                         # ~70 ms: lets the host queue the launches ahead
+    for j in range(G):
+        work.step(j, "gate_up", batch=j % steps,
+                  cfg_gu=wd.Launch(start_event=evs[j][0].cuda_event, stop_event=evs[j][1].cuda_event,
+                                   **(gu_cfg or {})))
+        work.step(j, "down", batch=j % steps,
+                  cfg_dn=wd.Launch(start_event=evs[j][2].cuda_event, stop_event=evs[j][3].cuda_event,
+                                   **(dn_cfg or {})))
     torch.cuda.synchronize()
-    gu_ms = np.array([evs[s][0].elapsed_time(evs[s][1]) for s in range(steps)])
-    dn_ms = np.array([evs[s][2].elapsed_time(evs[s][3]) for s in range(steps)])
+    gu_ms = np.array([evs[j][0].elapsed_time(evs[j][1]) for j in range(G)])
+    dn_ms = np.array([evs[j][2].elapsed_time(evs[j][3]) for j in range(G)])
 
     u = work.unique[:steps].astype(np.float64)
     per_expert_gu, per_expert_dn = expert_bytes(spec)
@@ -159,25 +242,44 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int):
     dn_bytes = float(np.mean(u * per_expert_dn))
     B = work.B
     res = dict(
-        B=B, steps=steps, ms_per_step=ms_per_step, tokens_per_s=B / (ms_per_step * 1e-3),
+        B=B, steps=steps, graph_steps=G, replays=int(rep_us.size), us_per_step=us_per_step,
+        ms_per_step=us_per_step * 1e-3,
+        tokens_per_s=B / (us_per_step * 1e-6), step_us_spread=spread(per_step),
         unique_experts_mean=float(u.mean()),
         unique_weight_bytes_mean=gu_bytes + dn_bytes,
-        layer_GBps_graph=(gu_bytes + dn_bytes) / (ms_per_step * 1e-3) / 1e9,
+        layer_GBps_graph=(gu_bytes + dn_bytes) / (us_per_step * 1e-6) / 1e9,
         gate_up_us=float(gu_ms.mean() * 1e3), down_us=float(dn_ms.mean() * 1e3),
+        gate_up_graph_node_us=node_us["gate_up"], down_graph_node_us=node_us["down"],
         gate_up_bytes=gu_bytes, down_bytes=dn_bytes,
         gate_up_GBps=gu_bytes / (gu_ms.mean() * 1e-3) / 1e9,
         down_GBps=dn_bytes / (dn_ms.mean() * 1e-3) / 1e9,
+        gate_up_graph_node_GBps=gu_bytes / (node_us["gate_up"] * 1e-6) / 1e9,
+        down_graph_node_GBps=dn_bytes / (node_us["down"] * 1e-6) / 1e9,
         kernels_GBps=(gu_bytes + dn_bytes) / ((gu_ms.mean() + dn_ms.mean()) * 1e-3) / 1e9,
     )
     return res
 
 
+def roofline(r, kernel, traffic_name):
+    """The roofline object of one kernel: `achieved` from its execution time
+    (kernel-own events); the same bytes over its time per graph node (execution
+    plus the dispatch gap) under `graph_node`."""
+    a = r[f"{kernel}_GBps"]
+    gn = r[f"{kernel}_graph_node_GBps"]
+    return {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": a / PEAK_HBM_GBPS,
+            "traffic": load_traffic(traffic_name), "kernel": kernel,
+            "algorithmic_bytes_per_launch": r[f"{kernel}_bytes"], "duration_us": r[f"{kernel}_us"],
+            "graph_node": {"achieved": gn, "frac": gn / PEAK_HBM_GBPS, "duration_us": r[f"{kernel}_graph_node_us"]}}
+
+
 def measure_large(torch, wd, gen, oracle, read_peak, batches=(1, 8, 32), steps=40, warmup=10):
     """The larger layer (128 experts, top-8, H 4096, I 1536) with Zipf(1.2)
     expert popularity at B in {1, 8, 32}: step time from one HIP graph and
-    per-kernel durations, as for the headline workload, with two distinct
-    weight copies (5 GB, 2.5x the last-level cache: a step never finds the
-    previous step's rows there), plus sampled parity against the oracle."""
+    per-kernel durations, as for the headline workload, with four distinct
+    weight copies cycled (10 GB; consecutive steps never share a copy, and a
+    copy comes back only after three other steps' rows, at least 470 MB, have
+    passed through the 256 MB last-level cache), plus sampled parity against
+    the oracle."""
     cfg = gen.CONFIGS["large"]
     spec = cfg["spec"]
     t0 = time.time()
@@ -185,7 +287,7 @@ def measure_large(torch, wd, gen, oracle, read_peak, batches=(1, 8, 32), steps=4
     eprint(f"[bench] large layer generated in {time.time() - t0:.1f} s")
     out = []
     for B in batches:
-        w = Workload(torch, wd, gen, L, B, max(steps, warmup), 2, seed=spec.seed, routing=cfg["routing"])
+        w = Workload(torch, wd, gen, L, B, max(steps, warmup), 4, seed=spec.seed, routing=cfg["routing"])
         r = measure(torch, wd, w, steps, warmup)
         cos, err, ymax = sampled_parity(oracle, L, w, [0, steps - 1])
         r.update(parity_cos_min=cos, parity_max_abs_err=err, parity_max_abs_y=ymax,
@@ -194,7 +296,7 @@ def measure_large(torch, wd, gen, oracle, read_peak, batches=(1, 8, 32), steps=4
         out.append(r)
         del w
         torch.cuda.empty_cache()
-    return dict(workload="E=128 top-8 H=4096 I=1536, Zipf(1.2) routing", weight_copies=2, per_B=out)
+    return dict(workload="E=128 top-8 H=4096 I=1536, Zipf(1.2) routing", weight_copies=4, per_B=out)
 
 
 def one_shot_read(torch, wd, nbytes, copies=16, reps=16):
@@ -227,15 +329,28 @@ def one_shot_read(torch, wd, nbytes, copies=16, reps=16):
     return best, best_cfg
 
 
-def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64), layers=48, reps=10):
+def unit_shift(m: float) -> int:
+    """Integer k with m * 2^k in [0.5, 1) (0 for m = 0)."""
+    return 0 if m == 0.0 else -int(np.floor(np.log2(m))) - 1
+
+
+def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64), layers=48):
     """A decode step through `layers` MoE layers of the layer's shape: distinct
     device copies of the weights (about 30 GB for 48 layers), per-layer routing
     from the router kernel on per-layer seeded logits, each layer's output
     feeding the next layer's input, all layers captured in one HIP graph per
-    batch size and replayed `reps` times."""
+    batch size and replayed (>= 100 replays, each timed by HIP events).
+
+    Each layer's down-projection E8M0 bytes are shifted by the integer that
+    brings that layer's largest |output| into [0.5, 1) on this batch (an exact
+    power-of-two rescale, standing in for the normalisation a model applies
+    between layers), so every layer carries unit-scale activations; without it
+    the chained outputs shrink about quadratically per layer and reach zero
+    within a few layers."""
     spec = L.spec
     base = [torch.from_numpy(a).to("cuda") for a in (L.wgu, L.sgu, L.wd, L.sd)]
     copies = [base] + [[t.clone() for t in base] for _ in range(layers - 1)]
+    sd0 = base[3].clone()
     per_expert = gen.expert_bytes(spec)
     out = []
     for B in batches:
@@ -249,11 +364,28 @@ def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64)
         for i in ids:
             uniq += int(torch.unique(i).numel())
         x0 = torch.from_numpy(gen.make_tokens(spec, B).x.view(np.int16)).to("cuda").view(torch.bfloat16)
-        xa, xb = x0.clone(), torch.empty_like(x0)
+        xs = [x0.clone(), torch.empty_like(x0)]
         act = torch.empty((B, spec.K, spec.I), dtype=torch.bfloat16, device="cuda")
 
+        # per-layer unit-scale shifts for this batch (eager, before capture)
+        shifts = []
+        src, dst = xs
+        for l in range(layers):
+            c = copies[l]
+            c[3].copy_(sd0)
+            wd.gate_up(src, ids[l], c[0], c[1], act=act)
+            wd.down(act, ids[l], ws[l], c[2], c[3], out=dst)
+            k = unit_shift(float(dst.float().abs().max().item()))
+            if k:
+                c[3].copy_((sd0.to(torch.int16) + k).to(torch.uint8))
+                wd.down(act, ids[l], ws[l], c[2], c[3], out=dst)
+            shifts.append(k)
+            src, dst = dst, src
+        last_max = float(src.float().abs().max().item())
+        xs[0].copy_(x0)
+
         def step():
-            src, dst = xa, xb
+            src, dst = xs
             for l in range(layers):
                 c = copies[l]
                 wd.gate_up(src, ids[l], c[0], c[1], act=act)
@@ -262,38 +394,32 @@ def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64)
 
         step()                                   # eager once (warm-up, device checks)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                step()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        us = (time.perf_counter() - t0) * 1e6 / reps
+        g = capture(torch, step)
+        rep = time_replays(torch, wd, g, min_replays=50)
+        us = float(np.median(rep))
         gbps = uniq * per_expert / (us * 1e-6) / 1e9
-        out.append(dict(B=B, step_us=us, tokens_per_s=B / (us * 1e-6), unique_experts=uniq,
-                        GBps=gbps, frac_of_measured_read_peak=gbps / read_peak))
+        out.append(dict(B=B, step_us=us, step_us_spread=spread(rep), replays=int(rep.size),
+                        tokens_per_s=B / (us * 1e-6), unique_experts=uniq,
+                        GBps=gbps, frac_of_measured_read_peak=gbps / read_peak,
+                        down_scale_shifts=shifts, last_layer_max_abs_out=last_max))
         eprint(f"[bench] stack B={B}: {out[-1]}")
         del g
     del copies, base
     torch.cuda.empty_cache()
     best = max(out, key=lambda r: r["GBps"])
     return dict(layers=layers, per_B=out, peak_bandwidth_B=best["B"],
-                note="distinct weight copies per layer, per-layer routing, chained activations, one HIP graph")
+                note="distinct weight copies per layer, per-layer routing, chained activations kept at unit scale "
+                     "by per-layer E8M0 shifts of the down projection, one HIP graph")
 
 
-def measure_comparison(torch, wd, gen, L, batches=(1, 2, 4, 8, 16, 32, 64), steps=40, copies=16):
+def measure_comparison(torch, wd, gen, L, batches=(1, 2, 4, 8, 16, 32, 64), steps=20, copies=16):
     """Warp decode against the expert-centric path on the same inputs: for each
     batch size, `steps` layer steps (fresh routing and x per step, weight copies
     cycled so that consecutive steps do not hit the same cached weights)
-    captured in one HIP graph per path and replayed; plus the expert-centric
-    stages' own kernel durations from HIP events."""
+    captured in one HIP graph per path and replayed (median of >= 30 replays,
+    each timed by HIP events); plus the expert-centric stages' own kernel
+    durations from HIP events.  Above 64 tokens warp decode runs its defaults
+    there (gate/up on the matrix cores, down in the token form)."""
     spec = L.spec
     base = [torch.from_numpy(a).to("cuda") for a in (L.wgu, L.sgu, L.wd, L.sd)]
     cps = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
@@ -325,20 +451,9 @@ def measure_comparison(torch, wd, gen, L, batches=(1, 2, 4, 8, 16, 32, 64), step
             for s in range(steps):
                 fn(s)                                 # eager pass: warm-up and device checks
             torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(g, stream=cap):
-                    for s in range(steps):
-                        fn(s, stream=cap)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            g.replay()
-            torch.cuda.synchronize()
-            res[f"{name}_us_per_step"] = (time.perf_counter() - t0) * 1e6 / steps
+            g = capture(torch, lambda: [fn(s, stream=torch.cuda.current_stream()) for s in range(steps)])
+            rep = time_replays(torch, wd, g, min_replays=30, min_seconds=0.1)
+            res[f"{name}_us_per_step"] = float(np.median(rep)) / steps
             del g
         # stage kernel durations of the expert-centric path
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
@@ -369,6 +484,7 @@ def measure_comparison(torch, wd, gen, L, batches=(1, 2, 4, 8, 16, 32, 64), step
     faster = [r["B"] for r in out if r["speedup_warp_decode"] < 1.0]
     return dict(per_B=out, steps=steps, weight_copies=copies,
                 crossover_B=min(faster) if faster else None,
+                largest_B_measured=max(r["B"] for r in out),
                 note="both paths graph-replayed on the same inputs; speedup = expert-centric time / warp-decode "
                      "time; crossover_B = smallest measured B where the expert-centric path is faster")
 
@@ -451,6 +567,19 @@ def accuracy(oracle, L, work: Workload, steps_to_check):
                 reference="FP64 layer, exact MXFP8 weights, unrounded intermediate and output")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo) and its logical CPU count."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"{name} ({os.cpu_count()} logical CPUs visible)"
+
+
 def cpu_baseline(oracle, L, gen, B, seconds=12.0, single_seconds=4.0):
     """The oracle as it stands, on every host core, over fresh seeded batches
     of the same workload until about `seconds` of CPU work have run; and the
@@ -471,8 +600,10 @@ def cpu_baseline(oracle, L, gen, B, seconds=12.0, single_seconds=4.0):
     cores = oracle.max_threads()            # the oracle's thread count persists per call: set it each time
     n1, t1, _ = run(1, single_seconds, 20_000)
     n_tok, t_used, s = run(cores, seconds, 10_000)
+    from oracle import build as ob
     return dict(value=n_tok / t_used, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{n_tok} tokens in {s} batches of B={B} on the same layer, {t_used:.1f} s",
+                cpu_model=cpu_model(), compiler_flags=" ".join(ob.CFLAGS),
                 single_thread=dict(value=n1 / t1, unit="tokens/s", cores=1,
                                    sample=f"{n1} tokens in batches of B={B}, {t1:.1f} s"))
 
@@ -490,7 +621,8 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip the expert-centric comparison")
     ap.add_argument("--only-compare", action="store_true",
                     help="run only the expert-centric comparison and print its JSON object (for profiling)")
-    ap.add_argument("--compare-batches", default="1,2,4,8,16,32,64", help="batch sizes of the comparison")
+    ap.add_argument("--compare-batches", default="1,2,4,8,16,32,64,96,128,192,256,384,512",
+                    help="batch sizes of the comparison")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on a single "
@@ -531,7 +663,8 @@ def main():
     cos1, err1, ymax1 = sampled_parity(oracle, L, w1, [0, steps // 2, steps - 1])
     r1.update(parity_cos_min=cos1, parity_max_abs_err=err1, parity_max_abs_y=ymax1,
               gate_up_over_one_shot_read=r1["gate_up_us"] / floor_us,
-              down_over_one_shot_read=r1["down_us"] / floor_dn_us)
+              down_over_one_shot_read=r1["down_us"] / floor_dn_us,
+              roofline_down=roofline(r1, "down", "down_qwen3_b1"))
     del w1
     torch.cuda.empty_cache()
 
@@ -543,10 +676,19 @@ def main():
         r32.update(parity_cos_min=cos32, parity_max_abs_err=err32, parity_max_abs_y=ymax32,
                    frac_of_measured_read_peak=r32["layer_GBps_graph"] / peak,
                    accuracy=accuracy(oracle, L, w32, [0, steps - 1]),
-                   roofline={"bound": "hbm", "achieved": r32["gate_up_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                             "frac": r32["gate_up_GBps"] / PEAK_HBM_GBPS, "kernel": "gate_up",
-                             "traffic": load_traffic("gate_up_qwen3_b32")})
+                   roofline=roofline(r32, "gate_up", "gate_up_qwen3_b32"),
+                   roofline_down=roofline(r32, "down", "down_qwen3_b32"))
         eprint(f"[bench] B=32: {json.dumps(r32)}")
+        # the same workload with both kernels in their token forms (one wave per (token, slot,
+        # rows) for gate/up, one per (token, outputs) for down: no matrix cores, no LDS)
+        tf = measure(torch, wd, w32, steps, warmup, gu_cfg=dict(form=1), dn_cfg=dict(form=1))
+        cos_t, err_t, ymax_t = sampled_parity(oracle, L, w32, [0, steps - 1])
+        tf.update(parity_cos_min=cos_t, parity_max_abs_err=err_t, parity_max_abs_y=ymax_t,
+                  frac_of_measured_read_peak=tf["layer_GBps_graph"] / peak,
+                  roofline=roofline(tf, "gate_up", "gate_up_token_form_qwen3_b32"),
+                  launch={"gate_up": {"form": 1}, "down": {"form": 1}})
+        r32["token_form"] = tf
+        eprint(f"[bench] B=32 token form: {json.dumps(tf)}")
         del w32
         torch.cuda.empty_cache()
 
@@ -558,7 +700,6 @@ def main():
 
     cpu = None if args.no_cpu else cpu_baseline(oracle, L, gen, 1)
 
-    achieved = r1["gate_up_GBps"]
     line = {
         "metric": "MoE-layer decode tokens/s and achieved HBM TB/s (% of 8 TB/s) at B=1 and 32",
         "value": r1["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -567,9 +708,12 @@ def main():
         "data": "synthetic: seeded N(0,0.02) weights quantized to MXFP8, N(0,1) bf16 x, softmax top-8 routing",
         "config": {"workload": "Qwen-3-style MoE decode layer E=128 top-8 H=2048 I=768, B=1",
                    "global_batch": 1, "parallelism": "single GPU", "weight_copies": copies1},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "kernel": "gate_up",
-                     "traffic": load_traffic("gate_up_qwen3_b1")},
+        "roofline": roofline(r1, "gate_up", "gate_up_qwen3_b1"),
+        "timing": "value = B / median per-step time over >= 100 replays (and >= 0.2 s) of one HIP graph of "
+                  "`steps` layer steps, each replay timed by HIP events; roofline.achieved = the kernel's "
+                  "algorithmic bytes / its mean execution time from HIP events recorded by its own dispatch; "
+                  "roofline.graph_node = the same bytes / its time per node in a graph of that kernel alone "
+                  "(execution plus the dispatch gap between nodes)",
         "hbm_read_peak_GBps": peak,
         "one_shot_read": {"gate_up_bytes": gu_b1_bytes, "gate_up_us": floor_us,
                           "gate_up_GBps": gu_b1_bytes / (floor_us * 1e-6) / 1e9, "gate_up_unroll_blocks": floor_cfg,

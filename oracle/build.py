@@ -11,11 +11,14 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
+# -ffp-contract=off: every product and sum is rounded as written (no FMA
+# contraction), so results do not depend on the host CPU's instruction set.
+# No -march=native: the library is built once and may run on another host CPU.
+CFLAGS = ["-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-std=c11", "-Wall", "-Wextra"]
+
+
 def build(verbose: bool = False) -> str:
-    # -ffp-contract=off: every product and sum is rounded as written (no FMA
-    # contraction), so results do not depend on the host CPU's instruction set.
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-std=c11", "-Wall", "-Wextra", SRC, "-o", LIB + ".tmp", "-lm"]
+    cmd = ["gcc", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -43,6 +43,9 @@ MUTANTS = [
     ("e4m3 encode rounds ties up", "if (r > 0.5 || (r == 0.5 && fmod(m, 2.0) == 1.0)) m += 1.0;",
      "if (r >= 0.5) m += 1.0;", 2),
     ("mx shared exponent off by one", "sb = (ex - 1) - 8 + 127;", "sb = ex - 8 + 127;", 1),
+    ("mx scale from amax / 448 rounded up", "sb = (ex - 1) - 8 + 127;",
+     "sb = (int)ceil(log2(amax / 448.0)) + 127;", 1),
+    ("mx scale byte not clamped to 254", "if (sb > 254) sb = 254;", "", 1),
     ("conventional keeps x unrounded", "for (long h = 0; h < H; ++h) xq[h] = oracle_dequant(xc[h], xs[h / 32]);",
      "for (long h = 0; h < H; ++h) xq[h] = xv[h];", 1),
     ("conventional skips the per-expert BF16",

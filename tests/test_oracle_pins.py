@@ -385,6 +385,58 @@ def test_mxfp8_quantize_matches_generator(rng):
     assert np.array_equal(t[c1], t[c2])
 
 
+def test_mxfp8_quantize_scale_rule_from_the_format(rng):
+    """The MX shared scale, pinned by what the OCP MX definition fixes rather
+    than by a second copy of the formula: the scale is a power of two that
+    puts the block's largest magnitude in the top binade of the element
+    format, [2^8, 2^9) for E4M3 (whose largest normal is 1.75 * 2^8 = 448);
+    the block maximum's code is then in that binade or saturated at 448; the
+    scale byte moves one for one with a power-of-two rescale of the block; and
+    every element is within half an E4M3 spacing of its scaled value (or
+    saturated)."""
+    t = oracle.e4m3_table()
+    v = (rng.standard_normal((64, 256)) * 10.0 ** rng.integers(-6, 4, (64, 1))).astype(np.float64)
+    codes, sb = oracle.mxfp8_quantize(v)
+    blk = v.reshape(64, 8, 32)
+    amax = np.abs(blk).max(axis=-1)
+    scaled_max = amax * 2.0 ** (127 - sb.astype(np.float64))
+    assert ((scaled_max >= 256.0) & (scaled_max < 512.0)).all()
+    q = t[codes].reshape(64, 8, 32)
+    qmax = np.abs(q).max(axis=-1)
+    assert ((qmax >= 256.0) & (qmax <= 448.0)).all()
+    # elements: nearest E4M3 value of the scaled input, or saturated at +-448
+    sc = blk * 2.0 ** (127 - sb.astype(np.float64))[..., None]
+    finite = np.sort(np.unique(np.abs(t[np.isfinite(t)])))
+    idx = np.clip(np.searchsorted(finite, np.abs(sc)), 1, len(finite) - 1)
+    gap = finite[idx] - finite[idx - 1]
+    inside = np.abs(sc) <= 448.0
+    assert (np.abs(np.abs(q) - np.abs(sc))[inside] <= gap[inside] / 2 + 1e-300).all()
+    assert (np.abs(q)[~inside] == 448.0).all()
+    assert (np.sign(q) == np.sign(sc))[np.abs(q) > 0].all()
+    # a power-of-two rescale of the input moves every scale byte by the same amount
+    for k in (-5, 3, 17):
+        c2, s2 = oracle.mxfp8_quantize(np.ldexp(v, k))
+        assert np.array_equal(c2, codes) and np.array_equal(s2.astype(int), sb.astype(int) + k)
+    # worked values: a block whose largest magnitude is 1.0 has shared exponent -8 (byte 119) and
+    # its maximum encodes 256 = 2^8 (code 0x78); one whose largest is 0.875 * 2^-3 keeps exponent -12
+    one = np.zeros(32); one[5] = 1.0; one[6] = -0.25
+    c, s = oracle.mxfp8_quantize(one)
+    assert s[0] == 119 and c[5] == 0x78 and t[c[6]] == -64.0
+    b = np.zeros(32); b[0] = 0.875 * 2.0 ** -3                       # = 1.75 * 2^-4
+    c, s = oracle.mxfp8_quantize(b)
+    assert s[0] == 127 - 12 and t[c[0]] == 448.0
+    # a largest magnitude just below the next binade scales to 511.75 and saturates at 448
+    b[0] = 1.9990234375 * 2.0 ** -3
+    c, s = oracle.mxfp8_quantize(b)
+    assert s[0] == 127 - 11 and t[c[0]] == 448.0
+    # the scale byte is clamped to E8M0's finite range [0, 254] (255 encodes NaN): far above it the
+    # elements saturate, far below they underflow to zero
+    c, s = oracle.mxfp8_quantize(np.full(32, 2.0 ** 140))
+    assert s[0] == 254 and (t[c] == 448.0).all()
+    c, s = oracle.mxfp8_quantize(np.full(32, -(2.0 ** -140)))
+    assert s[0] == 0 and (t[c] == 0.0).all()
+
+
 def _dense_exact(x, ids, w, L):
     def deq(codes, scales):
         v = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
