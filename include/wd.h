@@ -85,13 +85,18 @@ enum wd_status {
  *                    rows)
  *   waves_per_block  1..4: waves per workgroup (down on the matrix cores:
  *                    8 or 16)
- *   order            1 = row-block major (the waves of all tokens and slots
- *                    for one block of rows are adjacent, so tokens that share
- *                    an expert re-read its rows while they are in cache);
- *                    2 = token/slot major (one slot's rows are adjacent)
+ *   order            token forms: 1 = row-block major (the waves of all tokens
+ *                    and slots for one block of rows are adjacent, so tokens
+ *                    that share an expert re-read its rows while they are in
+ *                    cache); 2 = token/slot major (one slot's rows are
+ *                    adjacent).  Gate/up expert forms (2, 3, 4): 1 = row-block
+ *                    major with a per-expert skew of the row block; 2 = expert
+ *                    major (the default, with xcd_remap 2); 3 = row-block
+ *                    major without the skew
  *   xcd_remap        1 = renumber workgroups so that each of the 8 XCDs gets
  *                    one contiguous range of the work order; 2 = keep the
- *                    hardware's round-robin numbering
+ *                    hardware's round-robin numbering (the default for
+ *                    gate/up below 5 tokens and for its expert forms)
  *   math             1 = MXFP8 pairs converted to FP32, FMA accumulation;
  *                    2 = MXFP8 pairs converted to BF16 (exact for normal
  *                    values), two products per v_dot2_f32_bf16 into the FP32
@@ -113,9 +118,15 @@ enum wd_status {
  *                    accumulation in the matrix core's summation order
  *                    (rows_per_wave 1, lanes_per_row 64, math 2,
  *                    weight_loads 1; waves_per_block and order apply as for
- *                    the other forms).  Default: 3 when B >= 24 and none of
- *                    rows_per_wave, lanes_per_row, math, weight_loads is set,
- *                    else 1.
+ *                    the other forms);
+ *                    4 = form 3's work and arithmetic (bit-identical
+ *                    results) with the codes loaded straight from memory
+ *                    into a two-batch LDS ring per wave and x one batch
+ *                    ahead in registers; needs H a multiple of 256, s_gu
+ *                    4-byte aligned, B * H * 2 <= 0x7FFF0000 and 2 or 4
+ *                    waves per workgroup (default 4).
+ *                    Default: 3 when B >= 24 and none of rows_per_wave,
+ *                    lanes_per_row, math, weight_loads is set, else 1.
  *                    down: 1 = one wave per (token, block of output dims);
  *                    3 = one workgroup of 8 or 16 waves (waves_per_block)
  *                    per block of 16 output dims serving every token (of
@@ -141,6 +152,9 @@ enum wd_status {
  *                    several ranges is read once per range; the output does
  *                    not depend on it bit for bit).  0 = default: 2 when
  *                    H / 16 < 256 (fewer blocks than the 256 CUs), else 1.
+ *   lds_bytes        extra LDS per workgroup requested at launch (0..65536),
+ *                    unused by the kernel: fewer workgroups then share a CU
+ *                    (an occupancy knob for tuning)
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end
  *                    time into them (hipExtLaunchKernelGGL), so the elapsed
@@ -158,14 +172,21 @@ typedef struct wd_launch {
     int form;
     int weight_loads;
     int token_split;
+    int lds_bytes;
 } wd_launch;
 
 /* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section
- * "How the two kernels work"; the Chinese summary's "Gate/Up Kernel"): one
- * 64-lane wave per (token b, slot k, intermediate row j).  The wave streams
- * gate row j and up row I+j of expert e = topk_ids[b,k], converting MXFP8 to
- * FP32 in registers, reads x[b] once for both dot products, reduces across its
- * lanes and writes act[b,k,j] = BF16(SiLU(g) * u). */
+ * "How the two kernels work"; the Chinese summary's "Gate/Up Kernel"):
+ * act[b,k,j] = BF16(SiLU(g) * u) with g, u the dot products of x[b] with gate
+ * row j and up row I+j of expert e = topk_ids[b,k], MXFP8 converted exactly
+ * as it is read, FP32 accumulation, x read once for both.  Below 24 tokens
+ * (the default token form) one 64-lane wave serves each (token, slot, block
+ * of rows) and reduces across its lanes: no LDS, no barrier.  From 24 tokens
+ * the default is the expert form on the matrix cores (wd_launch.form 3, or 4
+ * when H is a multiple of 256): one wave per (expert, 16 rows) reads each
+ * weight row once for all slots routed to that expert, stages its codes in
+ * its own LDS region and computes the same sums on v_mfma_f32_16x16x32_bf16
+ * in another order. */
 int wd_gate_up(const uint16_t *x, const int32_t *topk_ids,
                const uint8_t *w_gu, const uint8_t *s_gu, uint16_t *act,
                int B, int K, int E, int H, int I, void *stream);
@@ -174,13 +195,16 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
                   int B, int K, int E, int H, int I, const wd_launch *cfg, void *stream);
 
 /* Down kernel (moe_down_3d_batched; same sections; the Chinese summary's
- * "Down Kernel"): one wave per (token b, output dim h).  The wave walks the K
- * routed experts' rows Wd[e_k, h, :], folds topk_w[b,k] into one FP32
- * accumulator, reduces across its 64 lanes with DPP row operations and one
- * lane read (no LDS) and writes out[b,h] = BF16(acc).  From B = 24 (B = 8
- * when K * I > 6144) the default is the expert form on the matrix cores
- * (wd_launch.form 3), which reads each Wd row block once per token range for
- * all the tokens of the range routed to its expert. */
+ * "Down Kernel"): out[b,h] = BF16(sum_k topk_w[b,k] * Wd[e_k,h,:] . act[b,k,:])
+ * with the router weight folded into the FP32 accumulator.  In the token
+ * form (the default below 24 tokens) one wave per (token b, output dims)
+ * walks the K routed experts' rows, reduces across its 64 lanes with DPP row
+ * operations and one lane read (no LDS) and writes out[b,h].  From B = 24
+ * (B = 8 when K * I > 6144; up to 64 tokens and 512 slots) the default is
+ * the expert form on the matrix cores (wd_launch.form 3): one workgroup per
+ * 16 output dims and token range reads each Wd row block once per range for
+ * all the range's tokens routed to its expert, keeps each slot's products in
+ * LDS and folds the router weights in per token after a workgroup barrier. */
 int wd_down(const uint16_t *act, const int32_t *topk_ids, const float *topk_w,
             const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
             int B, int K, int E, int H, int I, void *stream);

@@ -46,7 +46,7 @@ class Launch(C.Structure):
                 ("order", C.c_int), ("xcd_remap", C.c_int),
                 ("start_event", C.c_void_p), ("stop_event", C.c_void_p), ("math", C.c_int),
                 ("lanes_per_row", C.c_int), ("form", C.c_int), ("weight_loads", C.c_int),
-                ("token_split", C.c_int)]
+                ("token_split", C.c_int), ("lds_bytes", C.c_int)]
 
 
 class ECLaunch(C.Structure):

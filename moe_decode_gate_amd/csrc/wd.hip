@@ -59,7 +59,10 @@ int check_dims(int B, int K, int E, int H, int I) {
 //          that share an expert row read it from the same L2 while resident;
 //   gate/up, B >= 24: the expert form on the matrix cores (one wave per
 //          expert row block; equal at B = 24, 70 against 85 us at B = 32 and
-//          75 against 136 us at B = 64);
+//          75 against 136 us at B = 64), register-staged (form 3; the form that
+//          streams its codes into LDS measured no faster: 70.9 against 71.7 us
+//          at B = 32, and slower on the 4096 / 1536 layer, 137 against 121 us
+//          at B = 8);
 //   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
 //   down, B 3..5: 4 rows per wave, FP32 math; B 6..55: 8 rows per wave;
 //   down, B 24..64 (B * K <= 512): the expert form on the matrix cores, one
@@ -73,7 +76,10 @@ int check_dims(int B, int K, int E, int H, int I) {
 // B <= 2 (the 128-expert / top-8 / H 4096 / I 1536 layer: 10.0 against 12.4 us
 // at B = 1, 16.1 against 17.5 at B = 2) and, from B = 8, the matrix-core form
 // (43 against 49 us at B = 8, where the FP32 math took 225 us).
-int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, wd_launch *out) {
+// form4_ok: the gate/up kernel that streams codes into LDS applies (rows of a multiple of 256
+// elements, 4-byte-aligned scale bytes, x within one 2 GB buffer resource).
+int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, wd_launch *out,
+            bool form4_ok = false) {
     wd_launch c = in ? *in : wd_launch{};
     const bool batch = down ? B >= 3 : B >= 5;
     const bool wide = (long long)K * I > 6144;      // down: more than 6 act chunks per lane
@@ -86,7 +92,7 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
                                : untuned && B >= 24;
         c.form = mfma ? 3 : 1;
     }
-    if (c.form == 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
+    if (c.form >= 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
     if (c.rows_per_wave == 0)
         c.rows_per_wave = !batch ? (down && wide ? 2 * B : 1) : down ? (B >= 6 ? 8 : 4) : c.form == 2 ? 2 : 4;
     if (down && c.form == 3) {
@@ -99,9 +105,16 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
         if (c.waves_per_block == 0) c.waves_per_block = c.token_split > 1 ? 16 : 8;
     }
     if (c.waves_per_block == 0)
-        c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch ? 4 : 1);
-    if (c.order == 0) c.order = 1;
-    if (c.xcd_remap == 0) c.xcd_remap = (!down && !batch) ? 2 : 1;
+        c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch || c.form == 4 ? 4 : 1);
+    // gate/up expert forms: expert-major order (consecutive waves stream consecutive row blocks
+    // of one expert) with the hardware's round-robin workgroup placement, which deals every
+    // expert's row blocks over all 8 XCDs, so the XCDs stay balanced whichever experts the batch
+    // routes to.  Measured at B = 32 / 64 (us): Qwen-3 layer 71.7 / 77.0 (XCD-contiguous: 71.5 /
+    // 76.3; row-block-major: 73.8 / 81.5); 4096 / 1536 layer with Zipf routing, B = 8 / 32:
+    // 121 / 218 (XCD-contiguous: 132 / 228; row-block-major: 117 / 214).
+    const bool expert_form = !down && c.form >= 2;
+    if (c.order == 0) c.order = expert_form ? 2 : 1;
+    if (c.xcd_remap == 0) c.xcd_remap = ((!down && !batch) || expert_form) ? 2 : 1;
     if (c.math == 0) c.math = (down && batch && !wide && c.form != 3) ? wd::kMathF32 : wd::kMathDot2;
     if (c.weight_loads == 0) {
         // non-temporal where no other wave re-reads the rows and the variant is compiled
@@ -121,23 +134,26 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     } else if (c.waves_per_block < 1 || c.waves_per_block > 4) {
         return WD_ERR_UNSUPPORTED;
     }
-    if (c.order != 1 && c.order != 2) return WD_ERR_UNSUPPORTED;
+    if (c.order != 1 && c.order != 2 && !(c.order == 3 && !down && c.form >= 2)) return WD_ERR_UNSUPPORTED;
     if (c.xcd_remap != 1 && c.xcd_remap != 2) return WD_ERR_UNSUPPORTED;
     if (c.math != wd::kMathF32 && c.math != wd::kMathDot2) return WD_ERR_UNSUPPORTED;
     if (c.lanes_per_row != 16 && c.lanes_per_row != 32 && c.lanes_per_row != 64) return WD_ERR_UNSUPPORTED;
-    if (c.form < 1 || c.form > 3) return WD_ERR_UNSUPPORTED;
+    if (c.form < 1 || c.form > 4) return WD_ERR_UNSUPPORTED;
+    if (c.form == 4 && (down || !form4_ok || (c.waves_per_block != 2 && c.waves_per_block != 4)))
+        return WD_ERR_UNSUPPORTED;
     if (c.weight_loads != 1 && c.weight_loads != 2) return WD_ERR_UNSUPPORTED;
     if (down && (c.lanes_per_row != 64 || c.form == 2)) return WD_ERR_UNSUPPORTED;
     if (c.form == 2 && (c.lanes_per_row != 64 || c.math != wd::kMathDot2 || c.weight_loads != 1))
         return WD_ERR_UNSUPPORTED;
     // matrix-core expert form: fixed 16-row blocks and lane layout, BF16 operands, cached loads
-    if (c.form == 3 && (c.rows_per_wave != 1 || c.lanes_per_row != 64 || c.math != wd::kMathDot2 ||
+    if (c.form >= 3 && (c.rows_per_wave != 1 || c.lanes_per_row != 64 || c.math != wd::kMathDot2 ||
                         c.weight_loads != 1))
         return WD_ERR_UNSUPPORTED;
     // token ranges per 16-output block: the matrix-core down only
     if (c.token_split == 0) c.token_split = 1;
     if (c.token_split != 1 && c.token_split != 2 && c.token_split != 4) return WD_ERR_UNSUPPORTED;
     if (c.token_split != 1 && !(down && c.form == 3)) return WD_ERR_UNSUPPORTED;
+    if (c.lds_bytes < 0 || c.lds_bytes > 65536) return WD_ERR_UNSUPPORTED;
     *out = c;
     return WD_OK;
 }
@@ -238,11 +254,14 @@ int round_cpl_down(int need) {
 
 int launch(KernelFn fn, LayerArgs a, const wd_launch &c, hipStream_t s) {
     const int blocks = (a.nwaves + c.waves_per_block - 1) / c.waves_per_block;
+    a.nblocks = blocks;
+    a.wpb = c.waves_per_block;
+    const unsigned lds = (unsigned)c.lds_bytes;
     if (c.start_event || c.stop_event)
-        hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, s,
+        hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, s,
                               (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a);
     else
-        hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, s, a);
+        hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, s, a);
     return launched();
 }
 
@@ -256,16 +275,19 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     if (!aligned(w_gu, 16) || (B > 0 && (!aligned(x, 16) || !aligned(act, 16) || !aligned(ids, 4))))
         return WD_ERR_ALIGN;
     wd_launch c;
-    if ((rc = resolve(cfg, B, K, E, H, I, false, &c))) return rc;
+    const bool form4_ok = H % 256 == 0 && aligned(s_gu, 4) && (long long)B * H * 2 <= 0x7FFF0000LL;
+    if ((rc = resolve(cfg, B, K, E, H, I, false, &c, form4_ok))) return rc;
     const int lpr = c.lanes_per_row;
     const int cpl = round_cpl_gate_up((H / 16 + lpr - 1) / lpr);
     if (cpl < 0) return WD_ERR_UNSUPPORTED;
-    const int rows_per_wave = c.form == 3 ? 16 : (64 / lpr) * c.rows_per_wave;
+    const int rows_per_wave = c.form >= 3 ? 16 : (64 / lpr) * c.rows_per_wave;
     if (I % rows_per_wave) return WD_ERR_UNSUPPORTED;
     const bool tail = (H / 16) % (lpr * cpl) != 0;
     // rows of a multiple of 8 E8M0 bytes: every batch's 8 bytes lie inside its row, one load
     const bool sc8 = (H / 32) % 8 == 0 && aligned(s_gu, 4);
-    KernelFn fn = c.form == 3   ? (sc8 ? wd::gate_up_mfma_kernel<true> : wd::gate_up_mfma_kernel<false>)
+    KernelFn fn = c.form == 4   ? (c.waves_per_block == 2 ? wd::gate_up_mfma_lds_kernel<2>
+                                                          : wd::gate_up_mfma_lds_kernel<4>)
+                  : c.form == 3 ? (sc8 ? wd::gate_up_mfma_kernel<true> : wd::gate_up_mfma_kernel<false>)
                   : c.form == 2 ? gate_up_expert_fn(cpl, c.rows_per_wave, tail)
                                 : gate_up_fn(cpl, c.rows_per_wave, lpr, tail, c.math, c.weight_loads == 2);
     if (!fn) return WD_ERR_UNSUPPORTED;
@@ -312,12 +334,15 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         a.tsplit = c.token_split;
         const int blocks = a.nrowblk * c.token_split;
         a.nwaves = blocks * c.waves_per_block;
+        a.nblocks = blocks;
+        a.wpb = c.waves_per_block;
         const hipStream_t st = (hipStream_t)stream;
+        const unsigned lds = (unsigned)c.lds_bytes;
         if (c.start_event || c.stop_event)
-            hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, st,
+            hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, st,
                                   (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a);
         else
-            hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), 0, st, a);
+            hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, st, a);
         return launched();
     }
     const int nc = K * (I / 16);

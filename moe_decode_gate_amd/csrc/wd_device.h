@@ -21,6 +21,55 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Buffer resource (V#) for raw buffer loads over `bytes` bytes from `base`:
+// stride 0, 32-bit data format (required by gfx9-family buffer loads).  A
+// load whose offset is at or past `bytes` returns zero and touches no memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS (gfx950): lane l's bytes
+// land at lds + 16 l; `voff` is the lane's byte offset, `soff` a wave-uniform
+// one.
+__device__ __forceinline__ void ld16_lds(rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)lds, 16, voff, soff, 0, 0);
+}
+
+// Waits on the wave's own counters (gfx9 s_waitcnt encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; a field at its maximum does not
+// wait).  Needed around buffer-to-LDS loads: the compiler models such a load
+// as writing 16 bytes at the pointer it is given, not the 16 bytes per lane
+// it writes, so it neither waits for the data before later LDS reads of the
+// other lanes' bytes nor for earlier reads before the load overwrites them.
+// Scheduling barriers on both sides keep the compiler from moving memory
+// instructions across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wave-uniform 32-bit load through the scalar data cache (s_load): the
+// pointer is read as constant memory, which the inputs of a launch are.
+__device__ __forceinline__ int32_t sload(const int32_t *p) {
+    return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+
+__device__ __forceinline__ u32x4 buf16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // 16-byte weight load; NT marks it non-temporal (streamed once, not kept in
 // the caches), which pays off when no other wave re-reads the row.
 template <bool NT>

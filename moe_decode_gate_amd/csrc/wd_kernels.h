@@ -3,12 +3,23 @@
 // Gate/up (the write-ups' moe_gate_up_3d_batched) and down
 // (moe_down_3d_batched): "Better MoE model inference with warp decode", Key
 // claims, section "How the two kernels work", and the Chinese summary's
-// 技术原理 section with its Gate/Up and Down kernel subsections.  Each 64-lane
+// 技术原理 section with its Gate/Up and Down kernel subsections.
+//
+// Token forms (the pages' design; the defaults below 24 tokens): each 64-lane
 // wave owns output values for its whole life, streams the MXFP8 weight rows
-// it needs straight from HBM into registers, converts them to FP32 as it
-// reads them, keeps a private FP32 accumulator and finishes with a cross-lane
-// butterfly; waves never exchange data, so there is no LDS traffic, no
-// barrier and no atomic.
+// it needs straight from HBM into registers, converts them as it reads them,
+// keeps a private FP32 accumulator and finishes with a cross-lane butterfly;
+// waves never exchange data, so there is no LDS traffic, no barrier and no
+// atomic.
+//
+// Expert forms on the matrix cores (the defaults from 24 tokens, where tokens
+// share experts; a departure from the pages' design): gate/up takes one wave
+// per (expert, 16 intermediate rows) and down one workgroup per (16 output
+// dims, token range); both stage weight tiles through LDS (their own wave's
+// region, or with the down kernel's workgroup barrier the per-slot products),
+// and compute the same FP32 sums of exact products on
+// v_mfma_f32_16x16x32_bf16 in another order.  Still no atomic and no buffer
+// besides the intermediate and the output.
 #pragma once
 
 #include "wd_device.h"
@@ -31,12 +42,46 @@ struct LayerArgs {
     int remap;               // 1: XCD-contiguous workgroup numbering
     uint32_t nci_magic;      // down: floor(2^22 / (I/16)) + 1; (c * magic) >> 22 == c / (I/16) for all chunks c
     int tsplit;              // down, matrix-core form: workgroups per 16-output block, each for its own tokens
+    int nblocks;             // workgroups in the grid
+    int wpb;                 // waves per workgroup
 };
 
+// Makes the compiler load the kernel arguments a wave needs first in one
+// batch at the start (an empty asm that takes them as scalar operands), so
+// that they arrive with one wait instead of several sequential ones spread
+// over the wave's opening instructions.
+__device__ __forceinline__ void args_early(const LayerArgs &a) {
+    asm volatile("" ::"s"(a.ids), "s"(a.w), "s"(a.s), "s"(a.B), "s"(a.K), "s"(a.H), "s"(a.I), "s"(a.nwaves),
+                 "s"(a.nrowblk), "s"(a.order), "s"(a.remap), "s"(a.nblocks), "s"(a.wpb));
+}
+
+// (expert e, row block jb) of unit u of the expert forms of gate/up.
+//   order 1: row-block major with a skew, u = i * E + e, jb = (i + e) % nrowblk:
+//            with XCD-contiguous numbering every XCD gets the same share of
+//            every expert's rows, whichever experts the batch routes to, and
+//            the waves resident together read different row offsets of their
+//            experts (expert regions are a power-of-two multiple apart, and
+//            equal offsets would load the same memory channels);
+//   order 2: expert major, u = e * nrowblk + jb;
+//   order 3: row-block major without the skew, u = jb * E + e.
+__device__ __forceinline__ void expert_unit(const LayerArgs &a, int u, int &e, int &jb) {
+    if (a.order == 2) {
+        e = u / a.nrowblk; jb = u - e * a.nrowblk;
+    } else {
+        const int i = u / a.E;
+        e = u - i * a.E;
+        jb = a.order == 1 ? (i + e) % a.nrowblk : i;
+    }
+}
+
 // Logical wave index of the calling wave (wave-uniform, kept in an SGPR).
+// The grid and workgroup sizes come from the kernel's own arguments, loaded
+// with the rest of them, rather than from the dispatch's hidden arguments,
+// which would put two more dependent scalar loads ahead of a wave's first
+// weight load.
 __device__ __forceinline__ int logical_wave(const LayerArgs &a) {
-    const int g = a.remap == 1 ? xcd_logical((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
-    return __builtin_amdgcn_readfirstlane(g * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6));
+    const int g = a.remap == 1 ? xcd_logical((int)blockIdx.x, a.nblocks) : (int)blockIdx.x;
+    return __builtin_amdgcn_readfirstlane(g * a.wpb + (int)(threadIdx.x >> 6));
 }
 
 // ---------------------------------------------------------------------------
@@ -62,6 +107,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
     constexpr int G = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int grp = lane / LPR, tl = lane % LPR;
+    args_early(a);
     const int t = logical_wave(a);
     if (t >= a.nwaves) return;                       // wave-uniform exit
 
@@ -73,7 +119,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
     }
     const int H = a.H, I = a.I;
     const int NC = H >> 4;                           // chunks per row
-    int e = a.ids[b * a.K + k];
+    int e = sload(a.ids + b * a.K + k);              // (b, k) is wave-uniform
     const bool bad = (unsigned)e >= (unsigned)a.E;   // never read out of bounds for a bad id
     if (bad) e = 0;
 
@@ -162,15 +208,16 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
 // v_dot2_f32_bf16), so every act value is bit-identical to that form's.
 // Waves whose expert no token uses exit after the ballot.  Slots with an id
 // outside [0, E) get NaN rows from the waves of expert 0.
-// Wave t handles expert t / nrowblk, row block t % nrowblk: consecutive waves
-// stream consecutive rows of one expert.
+// Wave t handles (expert t % E, row block t / E) in row-block-major order
+// (order 1), else (expert t / nrowblk, row block t % nrowblk).
 // ---------------------------------------------------------------------------
 template <int CPL, int R, bool TAIL>
 __global__ __launch_bounds__(256) void gate_up_expert_kernel(LayerArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = logical_wave(a);
     if (t >= a.nwaves) return;
-    const int e = t / a.nrowblk, jb = t % a.nrowblk;
+    int e, jb;
+    expert_unit(a, t, e, jb);
     const int BK = a.B * a.K, H = a.H, I = a.I, NC = H >> 4;
 
     // which slots use this expert (and, for expert 0, which ids are invalid)
@@ -332,7 +379,8 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     const int lane = threadIdx.x & 63;
     const int unit = logical_wave(a);
     if (unit >= a.nwaves) return;
-    const int e = unit / a.nrowblk, jb = unit % a.nrowblk;
+    int e, jb;
+    expert_unit(a, unit, e, jb);
     const int BK = a.B * a.K, H = a.H, I = a.I;
     const int r16 = lane & 15, q = lane >> 4;
     u32x4(*wt)[16][16] = tile[threadIdx.x >> 6];
@@ -510,6 +558,256 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Gate/up, expert form on the matrix cores, weight codes streamed straight
+// into LDS (form 4; rows of a multiple of 256 elements).  The work and the
+// arithmetic are those of gate_up_mfma_kernel above -- one wave per (expert
+// e, block of 16 intermediate rows), the 16 x T gate and up tiles of each
+// group of T <= 16 slots on v_mfma_f32_16x16x32_bf16, weights converted
+// exactly to BF16, x as stored, FP32 accumulation in the same order -- so
+// the intermediate is bit-identical to that kernel's.  What differs is how
+// the bytes arrive:
+//   * the codes of a batch (2 steps of 64 elements: 16 gate and 16 up rows x
+//     128 bytes) go from memory to the wave's LDS ring by buffer-to-LDS loads
+//     (no register staging and no LDS stores), two batches ahead: a ring of
+//     two slots, the load of batch n + 2 issued into the slot of batch n as
+//     soon as n's operands are read from it;
+//   * x and the rows' E8M0 bytes come by buffer loads one batch ahead, into
+//     one of two register sets; the columns past the group's slots get an
+//     offset past the end of x, so their loads return zero without touching
+//     memory;
+//   * every address offset is loop-invariant except a wave-uniform batch
+//     offset, so a batch costs its loads, 4 LDS reads, 32 conversions and 8
+//     matrix instructions.
+// Each 16-byte segment s of row r sits in slot s ^ ((r >> 1) & 7) of the
+// row's 8 LDS slots, so the operand reads (16 rows, one segment each) hit
+// distinct banks.  When a group holds 16 slots (another may follow), its
+// last batches load the rows' first two batches into the ring for the next
+// group of the same expert; otherwise nothing is loaded past the rows' end.
+// Waves drain their loads before exiting.
+// ---------------------------------------------------------------------------
+template <int WPB>
+__global__ __launch_bounds__(64 * WPB) void gate_up_mfma_lds_kernel(LayerArgs a) {
+    constexpr int kSeg = 8;                                // 16-byte segments per row per batch
+    __shared__ u32x4 ring0[WPB][2][16][kSeg];              // slot 0: [wave][gate, up][row][slot]
+    __shared__ u32x4 ring1[WPB][2][16][kSeg];              // slot 1
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int unit = logical_wave(a);
+    if (unit >= a.nwaves) return;                          // wave-uniform, before any load
+    int e, jb;
+    expert_unit(a, unit, e, jb);
+    const int BK = a.B * a.K, H = a.H, I = a.I;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int nb = H >> 7;                                 // batches per row (even: H % 256 == 0)
+    const uint32_t nbr = (uint32_t)(H >> 5);
+
+    // the tile's gate rows start at row0, its up rows at row0 + I (one resource covers both)
+    const size_t row0 = (size_t)e * 2 * I + (size_t)jb * 16;
+    const rsrc_t rw = make_rsrc(a.w + row0 * (size_t)H, (uint32_t)((I + 16) * H));
+    const rsrc_t rs = make_rsrc(a.s + row0 * nbr, (uint32_t)(I + 16) * nbr);
+    const rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.B * H * 2));   // at most 0x7FFF0000 (host check)
+
+    // buffer-to-LDS loads of one batch: instruction j covers rows 8 (j & 1) + l / 8 of the gate
+    // (j < 2) or up (j >= 2) tile, lane l bringing segment (l % 8) ^ ((row >> 1) & 7)
+    uint32_t doff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * (j & 1) + (lane >> 3);
+        const int sg = (lane & 7) ^ ((r >> 1) & 7);
+        doff[j] = (uint32_t)(((j >> 1) * I + r) * H + 16 * sg);
+    }
+    auto issue = [&](u32x4 (*slot)[2][16][kSeg], int n) {
+        const uint32_t so = (uint32_t)(128 * n);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ld16_lds(rw, &slot[wv][j >> 1][8 * (j & 1)][0], doff[j], so);
+    };
+    // the first two batches do not depend on the routing
+    issue(ring0, 0);
+    issue(ring1, 1 % nb);
+
+    if (e == 0) {              // NaN rows for slots whose id is outside [0, E)
+        for (int base = 0; base < BK; base += 64) {
+            const int sl = base + lane;
+            const int id = sl < BK ? a.ids[sl] : 0;
+            uint64_t m = __builtin_amdgcn_ballot_w64(sl < BK && (unsigned)id >= (unsigned)a.E);
+            while (m) {
+                const int s0 = base + (int)__builtin_ctzll(m);
+                m &= m - 1;
+                if (lane < 16) a.out[(size_t)s0 * I + (size_t)jb * 16 + lane] = 0x7FC0;
+            }
+        }
+    }
+
+    // Slots routed to e, found 512 at a time: eight independent id loads, then ballots.
+    uint64_t mk[8];
+    int chunk = 0, next_chunk = 0;
+    auto refill = [&]() {
+        int idv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = next_chunk + 64 * u + lane;
+            idv[u] = sl < BK ? a.ids[sl] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mk[u] = __builtin_amdgcn_ballot_w64(idv[u] == e);
+        chunk = next_chunk;
+        next_chunk += 512;
+    };
+    refill();
+
+    // per-lane offsets of the rows' E8M0 bytes (4 per batch) and, per group, of x
+    const uint32_t sg_off = (uint32_t)r16 * nbr, su_off = (uint32_t)(I + r16) * nbr;
+    struct XSet {
+        u32x4 x[4];            // step i: x[2 i] = elements 64 i + 16 q .. + 7, x[2 i + 1] = + 8 .. + 15
+        uint32_t sg, su;       // the lane's gate and up row's 4 E8M0 bytes of the batch
+    };
+    uint32_t xoff = 0;
+    auto load_x = [&](XSet &st, int n) {
+        const uint32_t so = (uint32_t)(256 * n);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            st.x[2 * i] = buf16(rx, xoff + 128 * i, so);
+            st.x[2 * i + 1] = buf16(rx, xoff + 128 * i + 16, so);
+        }
+        st.sg = buf4(rs, sg_off, (uint32_t)(4 * n));
+        st.su = buf4(rs, su_off, (uint32_t)(4 * n));
+    };
+    f32x4 cg, cu;
+    // one batch: the weight operands of its two steps from the ring slot (segment 4 i + q of
+    // row r16), then 8 matrix instructions
+    auto read_ops = [&](u32x4 (*slot)[2][16][kSeg], u32x4 (&wg)[2], u32x4 (&wu)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int sl = (4 * i + q) ^ ((r16 >> 1) & 7);
+            wg[i] = slot[wv][0][r16][sl];
+            wu[i] = slot[wv][1][r16][sl];
+        }
+    };
+    auto mma = [&](const XSet &st, const u32x4 (&wg)[2], const u32x4 (&wu)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int sh = 8 * (2 * i + (q >> 1));         // byte of block 4 n + 2 i + q / 2
+            const float fg = e8m0_operand((st.sg >> sh) & 0xFFu), fu = e8m0_operand((st.su >> sh) & 0xFFu);
+            uint32_t gw[8], uw[8];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                mx_word_bf16(wg[i][d], fg, gw[2 * d], gw[2 * d + 1]);
+                mx_word_bf16(wu[i][d], fu, uw[2 * d], uw[2 * d + 1]);
+            }
+            const u32x4 g0 = {gw[0], gw[1], gw[2], gw[3]}, g1 = {gw[4], gw[5], gw[6], gw[7]};
+            const u32x4 u0 = {uw[0], uw[1], uw[2], uw[3]}, u1 = {uw[4], uw[5], uw[6], uw[7]};
+            cg = mfma_bf16(g0, st.x[2 * i], cg);
+            cg = mfma_bf16(g1, st.x[2 * i + 1], cg);
+            cu = mfma_bf16(u0, st.x[2 * i], cu);
+            cu = mfma_bf16(u1, st.x[2 * i + 1], cu);
+        }
+    };
+
+    XSet sa, sb;
+    for (;;) {
+        // the next up-to-16 slots routed to e, in slot order, one per lane 0..15
+        int my_slot = 0, cnt = 0;
+        for (;;) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                while (mk[u] != 0 && cnt < 16) {
+                    const int s0 = chunk + 64 * u + (int)__builtin_ctzll(mk[u]);
+                    mk[u] &= mk[u] - 1;
+                    if (lane == cnt) my_slot = s0;
+                    ++cnt;
+                }
+            }
+            if (cnt == 16 || next_chunk >= BK) break;
+            refill();
+        }
+        if (cnt == 0) break;
+        const int slot = __shfl(my_slot, r16);
+        const bool live = r16 < cnt;
+        // columns past the group's slots: an offset past the end of x, so their loads return zero
+        xoff = live ? (uint32_t)((slot / a.K) * H * 2 + 32 * q) : 0x7FFF0000u;
+
+        cg = f32x4{0.f, 0.f, 0.f, 0.f};
+        cu = cg;
+        load_x(sa, 0);
+        // nothing in flight when the loop starts: its waits then need only the steady-state counts
+        wait_vmcnt<0>();
+        // Vector-memory instructions are issued in the order x(n + 1) (6), codes(n + 2) (4),
+        // x(n + 2) (6), codes(n + 3) (4) per pair of batches (the waits below are scheduling
+        // barriers and keep that order).  So when batch n's codes are read, at least x(n),
+        // codes(n + 1) and x(n + 1) -- 16 instructions -- were issued after them, and
+        // vmcnt(16) waits for codes(n) and nothing younger (at a group's first batches more
+        // was issued since, which only makes the wait exact sooner); batch n's compute then
+        // waits for x(n) alone, with codes(n + 1) and (n + 2) still in flight.  Each slot is
+        // refilled only after its reads have returned (lgkmcnt(0)).
+        const bool more = cnt == 16;                       // another group of this expert may follow
+        int n = 0;
+        for (; n + 2 < nb; n += 2) {
+            u32x4 wg[2], wu[2];
+            load_x(sb, n + 1);
+            wait_vmcnt<16>();
+            read_ops(ring0, wg, wu);
+            wait_lgkmcnt0();
+            issue(ring0, n + 2);
+            mma(sa, wg, wu);
+            __builtin_amdgcn_sched_barrier(0);
+            load_x(sa, n + 2);
+            wait_vmcnt<16>();
+            read_ops(ring1, wg, wu);
+            wait_lgkmcnt0();
+            issue(ring1, n + 3);
+            mma(sb, wg, wu);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        {   // the last two batches (nb is even)
+            u32x4 wg[2], wu[2];
+            load_x(sb, n + 1);
+            wait_vmcnt<16>();
+            read_ops(ring0, wg, wu);
+            if (more) {
+                // the ring takes the rows' first two batches for the next group
+                wait_lgkmcnt0();
+                issue(ring0, 0);
+                mma(sa, wg, wu);
+                __builtin_amdgcn_sched_barrier(0);
+                load_x(sa, 0);                             // (reloaded with the next group's tokens)
+                wait_vmcnt<16>();
+                read_ops(ring1, wg, wu);
+                wait_lgkmcnt0();
+                issue(ring1, 1);
+                mma(sb, wg, wu);
+            } else {
+                // nothing more to load: after codes(n + 1) only x(n + 1) (6) was issued
+                mma(sa, wg, wu);
+                wait_vmcnt<6>();
+                read_ops(ring1, wg, wu);
+                mma(sb, wg, wu);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (live) {
+            uint32_t packed[2];
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+                uint32_t h2 = 0;
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const float gv = cg[r + d], uv = cu[r + d];
+                    const float en = expf(-__builtin_fabsf(gv));
+                    const float sig = gv >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
+                    h2 |= (uint32_t)to_bf16(gv * sig * uv) << (16 * d);
+                }
+                packed[r >> 1] = h2;
+            }
+            *reinterpret_cast<uint2 *>(a.out + (size_t)slot * I + (size_t)jb * 16 + 4 * q) =
+                make_uint2(packed[0], packed[1]);
+        }
+        if (cnt < 16) break;
+    }
+    // the ring's last loads (never read) land before the wave's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ---------------------------------------------------------------------------
 // Down: one wave per (token b, block of R output dims).
 //
 // The K routed rows Wd[e_k, h, 0:I] of one output dim are cut into 16-element
@@ -523,6 +821,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
 template <int CPL, int R, bool TAIL, int MATH, bool NT>
 __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
     const int lane = threadIdx.x & 63;
+    args_early(a);
     const int t = logical_wave(a);
     if (t >= a.nwaves) return;
 

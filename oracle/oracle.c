@@ -202,9 +202,9 @@ int oracle_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
 
  * The warp-decode write-ups claim their output is 1.4x closer to a full
  * FP32 reference than the conventional path's, because the conventional
- * path rounds BF16 activations to MXFP8 and back (p2 Key claims, section
+ * path rounds BF16 activations to MXFP8 and back (the English summary, Key claims,
  * "Improved accuracy"; the Chinese summary, section 性能与精度 2), and writes
- * per-expert outputs to a BF16 buffer that a combine step sums (p2, section
+ * per-expert outputs to a BF16 buffer that a combine step sums (the English summary,
  * "Buffer elimination").  These functions give the reference and the
  * conventional path's numerics in FP64. */
 
@@ -347,8 +347,8 @@ int oracle_moe_decode_conventional(const uint16_t *x, const int32_t *ids, const 
 /* ---- router ------------------------------------------------------------
 
  * Top-k gating ahead of the layer (the pages name it only as routing each
- * token to a few of many experts, "128 选 8": the Chinese summary, section
- * 传统路径的困境; p2 Method).  Plain definition: the K largest logits of a
+ * token to 8 of 128 experts: the Chinese summary, section 传统路径的困境;
+ * the English summary, Method).  Plain definition: the K largest logits of a
  * token (larger first; equal logits: the lower expert index first), and
  * weights = softmax over the full row renormalised to the chosen K, which is
  * the softmax of the chosen logits: w_k = exp(l_k - l_max) / sum_j exp(l_j - l_max).

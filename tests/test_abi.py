@@ -215,7 +215,8 @@ def test_matrix_core_form_limits():
     assert gux(form=3, lanes_per_row=32) == -7
     assert gux(form=3, math=1) == -7
     assert gux(form=3, weight_loads=2) == -7
-    assert gux(form=4) == -7
+    assert gux(form=5) == -7
+    assert gux(form=4, rows_per_wave=2) == -7 and gux(form=4, math=1) == -7
 
     # down on the matrix cores: 8 or 16 waves per workgroup, B <= 64, B * K <= 512, E <= 1024;
     # accepted configurations get as far as the device check (-5 here)
@@ -269,3 +270,15 @@ def test_noalloc_host_checks():
     assert na(out=None) == -1 and na(wd=None) == -1
     assert na(x=A + 8) == -3 and na(out=A + 1) == -3
     assert na(H=100) == -2 and na(K=32, I=1024) == -7
+
+
+def test_lds_gate_up_form_limits():
+    """Form 4 (matrix-core gate/up streaming its codes into LDS) needs rows of
+    a multiple of 256 elements, 4-byte-aligned scale bytes, x within 2 GB and
+    2 or 4 waves per workgroup; it is gate/up only."""
+    def g(H=2048, B=32, s=A, **kw):
+        return lib.wd_gate_up_ex(A, A, A, s, A, B, 8, 128, H, 768, C.byref(wd.Launch(form=4, **kw)), None)
+    assert g() == -5 and g(B=1) == -5 and g(waves_per_block=2) == -5
+    assert g(H=96) == -7 and g(H=288) == -7 and g(s=A + 2) == -7 and g(waves_per_block=3) == -7
+    assert g(H=8192, B=131072) == -7                     # x of 2 GB: past the buffer resource's range
+    assert lib.wd_down_ex(A, A, A, A, A, A, 32, 8, 128, 2048, 768, C.byref(wd.Launch(form=4)), None) == -7
