@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
 GRAPH_MIN_STEPS = 200          # layer steps per timed graph (at least)
+MIN_REPLAYS = 100              # timed replays per graph (at least)
 
 
 def eprint(*a):
@@ -108,8 +109,13 @@ class Workload:
         self.w = torch.from_numpy(self.host_w).to(dev)
         self.act = torch.empty((steps, B, spec.K, spec.I), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((steps, B, spec.H), dtype=torch.bfloat16, device=dev)
+        # the down kernel's expert-split scratch (zeroed once; every call leaves it zero); the
+        # library's default launch configuration decides whether it is used
+        self.dscr = wd.down_scratch(B, spec.H)
+        self.dn_default = {"down_scratch": self.dscr}
         self.unique = np.array([np.unique(self.host_ids[s]).size for s in range(steps)])
         self.wd = wd
+        self.gen = gen
 
     def step(self, j, which="both", cfg_gu=None, cfg_dn=None, batch=None):
         """Layer step j on weight copy j % R with batch `batch` (default j)."""
@@ -118,7 +124,8 @@ class Workload:
         if which in ("both", "gate_up"):
             self.wd.gate_up(self.x[s], self.ids[s], wgu, sgu, act=self.act[s], cfg=cfg_gu)
         if which in ("both", "down"):
-            self.wd.down(self.act[s], self.ids[s], self.w[s], wdn, sdn, out=self.out[s], cfg=cfg_dn)
+            self.wd.down(self.act[s], self.ids[s], self.w[s], wdn, sdn, out=self.out[s],
+                         cfg=self.dn_default if cfg_dn is None else cfg_dn)
 
 
 def capture(torch, fn):
@@ -134,13 +141,18 @@ def capture(torch, fn):
     return g
 
 
-def time_replays(torch, wd, g, warm=20, min_replays=100, min_seconds=0.2, max_replays=4000, chunk=50):
+def time_replays(torch, wd, g, warm=20, min_replays=None, min_seconds=0.2, max_replays=4000, chunk=50):
     """Replays of one captured graph, each bracketed by HIP events on the stream
     that launches it: `warm` untimed replays, then at least `min_replays` and at
     least `min_seconds` of timed ones.  The replays are queued in chunks behind a
     sleeping wave, so the host is ahead of the GPU and each event pair measures
     the GPU's time for that replay (its nodes and the gaps between them).
     Returns the per-replay durations in microseconds."""
+    if min_replays is None:
+        min_replays = MIN_REPLAYS
+    min_replays = min(min_replays, MIN_REPLAYS)
+    if MIN_REPLAYS < 100:                    # a profiling run: no time floor, no long warm-up
+        min_seconds, warm = 0.0, min(warm, 2)
     for _ in range(warm):
         g.replay()
     torch.cuda.synchronize()
@@ -227,11 +239,10 @@ def measure(torch, wd, work: Workload, steps: int, warmup: int, gu_cfg=None, dn_
     wd.gpu_sleep(20000)                         # ~70 ms: lets the host queue the launches ahead
     for j in range(G):
         work.step(j, "gate_up", batch=j % steps,
-                  cfg_gu=wd.Launch(start_event=evs[j][0].cuda_event, stop_event=evs[j][1].cuda_event,
-                                   **(gu_cfg or {})))
+                  cfg_gu=dict(start_event=evs[j][0].cuda_event, stop_event=evs[j][1].cuda_event, **(gu_cfg or {})))
         work.step(j, "down", batch=j % steps,
-                  cfg_dn=wd.Launch(start_event=evs[j][2].cuda_event, stop_event=evs[j][3].cuda_event,
-                                   **(dn_cfg or {})))
+                  cfg_dn=dict(start_event=evs[j][2].cuda_event, stop_event=evs[j][3].cuda_event,
+                              **(work.dn_default if dn_cfg is None else dn_cfg)))
     torch.cuda.synchronize()
     gu_ms = np.array([evs[j][0].elapsed_time(evs[j][1]) for j in range(G)])
     dn_ms = np.array([evs[j][2].elapsed_time(evs[j][3]) for j in range(G)])
@@ -366,6 +377,7 @@ def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64)
         x0 = torch.from_numpy(gen.make_tokens(spec, B).x.view(np.int16)).to("cuda").view(torch.bfloat16)
         xs = [x0.clone(), torch.empty_like(x0)]
         act = torch.empty((B, spec.K, spec.I), dtype=torch.bfloat16, device="cuda")
+        dcfg = {"down_scratch": wd.down_scratch(B, spec.H)}
 
         # per-layer unit-scale shifts for this batch (eager, before capture)
         shifts = []
@@ -374,11 +386,11 @@ def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64)
             c = copies[l]
             c[3].copy_(sd0)
             wd.gate_up(src, ids[l], c[0], c[1], act=act)
-            wd.down(act, ids[l], ws[l], c[2], c[3], out=dst)
+            wd.down(act, ids[l], ws[l], c[2], c[3], out=dst, cfg=dcfg)
             k = unit_shift(float(dst.float().abs().max().item()))
             if k:
                 c[3].copy_((sd0.to(torch.int16) + k).to(torch.uint8))
-                wd.down(act, ids[l], ws[l], c[2], c[3], out=dst)
+                wd.down(act, ids[l], ws[l], c[2], c[3], out=dst, cfg=dcfg)
             shifts.append(k)
             src, dst = dst, src
         last_max = float(src.float().abs().max().item())
@@ -389,7 +401,7 @@ def measure_stack(torch, wd, gen, L, read_peak, batches=(1, 2, 4, 8, 16, 32, 64)
             for l in range(layers):
                 c = copies[l]
                 wd.gate_up(src, ids[l], c[0], c[1], act=act)
-                wd.down(act, ids[l], ws[l], c[2], c[3], out=dst)
+                wd.down(act, ids[l], ws[l], c[2], c[3], out=dst, cfg=dcfg)
                 src, dst = dst, src
 
         step()                                   # eager once (warm-up, device checks)
@@ -436,10 +448,12 @@ def measure_comparison(torch, wd, gen, L, batches=(1, 2, 4, 8, 16, 32, 64), step
         y_ec = torch.empty_like(y_wd)
         wsp = torch.empty(wd.ec_workspace_bytes(B, spec.K, spec.E, spec.H, spec.I), dtype=torch.uint8, device="cuda")
 
+        dcfg = {"down_scratch": wd.down_scratch(B, spec.H)}
+
         def run_wd(s, stream=None):
             c = cps[s % copies]
             wd.gate_up(xs[s], ids[s], c[0], c[1], act=act, stream=stream)
-            wd.down(act, ids[s], ws[s], c[2], c[3], out=y_wd[s], stream=stream)
+            wd.down(act, ids[s], ws[s], c[2], c[3], out=y_wd[s], cfg=dcfg, stream=stream)
 
         def run_ec(s, stream=None, cfg=None):
             c = cps[s % copies]
@@ -561,10 +575,37 @@ def accuracy(oracle, L, work: Workload, steps_to_check):
         ref_sq += float((gt ** 2).sum())
         m_wd += float(np.abs(got - gt).mean()); m_cv += float(np.abs(cv - gt).mean())
     rel_wd, rel_cv, rel_ec = (e_wd / ref_sq) ** 0.5, (e_cv / ref_sq) ** 0.5, (e_ec / ref_sq) ** 0.5
+    # against the layer with the weights as drawn, before MXFP8 quantization (the
+    # checked steps' tokens in one batch: every token's result is its own)
+    xs = np.concatenate([work.host_x[s] for s in steps_to_check])
+    ids = np.concatenate([work.host_ids[s] for s in steps_to_check])
+    wts = np.concatenate([work.host_w[s] for s in steps_to_check])
+    drawn = {}
+
+    def weights(e, part):
+        if e not in drawn:
+            drawn.clear()
+            drawn[e] = work.gen.expert_weights_fp32(spec, e)
+        return drawn[e][part]
+
+    full = oracle.moe_decode_dense_weights(xs, ids, wts, lambda e: weights(e, 0), lambda e: weights(e, 1))
+    outs = {"warp_decode_gpu": np.concatenate([work.out[s].float().cpu().numpy() for s in steps_to_check]),
+            "conventional": np.concatenate([oracle.moe_decode_conventional(
+                work.host_x[s], work.host_ids[s], work.host_w[s], L.wgu, L.sgu, L.wd, L.sd)
+                for s in steps_to_check]),
+            "mxfp8_exact": np.concatenate([oracle.moe_decode_exact(
+                work.host_x[s], work.host_ids[s], work.host_w[s], L.wgu, L.sgu, L.wd, L.sd)
+                for s in steps_to_check])}
+    fsq = float((full ** 2).sum())
+    vs_full = {k: (float(((v.astype(np.float64) - full) ** 2).sum()) / fsq) ** 0.5 for k, v in outs.items()}
     return dict(rel_l2_warp_decode_gpu=rel_wd, rel_l2_conventional=rel_cv, rel_l2_ratio=rel_cv / rel_wd,
                 rel_l2_expert_centric_gpu=rel_ec, rel_l2_ratio_gpu_paths=rel_ec / rel_wd,
                 mean_abs_ratio=m_cv / m_wd, steps=len(steps_to_check),
-                reference="FP64 layer, exact MXFP8 weights, unrounded intermediate and output")
+                reference="FP64 layer, exact MXFP8 weights, unrounded intermediate and output",
+                vs_unquantized_weights=dict(
+                    {f"rel_l2_{k}": v for k, v in vs_full.items()},
+                    rel_l2_ratio=vs_full["conventional"] / vs_full["warp_decode_gpu"],
+                    reference="FP64 layer with the FP32 weights as drawn before MXFP8 quantization"))
 
 
 def cpu_model() -> str:
@@ -621,9 +662,15 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip the expert-centric comparison")
     ap.add_argument("--only-compare", action="store_true",
                     help="run only the expert-centric comparison and print its JSON object (for profiling)")
+    ap.add_argument("--replays", type=int, default=100,
+                    help="minimum timed replays of each graph (fewer only for profiling runs)")
+    ap.add_argument("--graph-min-steps", type=int, default=200,
+                    help="layer steps per timed graph, at least (fewer only for profiling runs)")
     ap.add_argument("--compare-batches", default="1,2,4,8,16,32,64,96,128,192,256,384,512",
                     help="batch sizes of the comparison")
     args = ap.parse_args()
+    global GRAPH_MIN_STEPS, MIN_REPLAYS
+    GRAPH_MIN_STEPS, MIN_REPLAYS = args.graph_min_steps, args.replays
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs on a single "
               "MI355X; there is no multi-GPU path)", file=sys.stderr)

@@ -125,8 +125,9 @@ enum wd_status {
  *                    ahead in registers; needs H a multiple of 256, s_gu
  *                    4-byte aligned, B * H * 2 <= 0x7FFF0000 and 2 or 4
  *                    waves per workgroup (default 4).
- *                    Default: 3 when B >= 24 and none of rows_per_wave,
- *                    lanes_per_row, math, weight_loads is set, else 1.
+ *                    Default: 3 when B >= 24 (B >= 16 when H >= 4096) and
+ *                    none of rows_per_wave, lanes_per_row, math,
+ *                    weight_loads is set, else 1.
  *                    down: 1 = one wave per (token, block of output dims);
  *                    3 = one workgroup of 8 or 16 waves (waves_per_block)
  *                    per block of 16 output dims serving every token (of
@@ -155,6 +156,22 @@ enum wd_status {
  *   lds_bytes        extra LDS per workgroup requested at launch (0..65536),
  *                    unused by the kernel: fewer workgroups then share a CU
  *                    (an occupancy knob for tuning)
+ *   expert_split     down, form 3 only: 2 = two workgroups per block of 16
+ *                    output dims, one for the experts with even ids and one
+ *                    for odd, all tokens each; each workgroup keeps its
+ *                    class's partial sums in FP32, and the second of the two
+ *                    to finish adds them (class 0 + class 1) and writes the
+ *                    output, so every Wd row is read once.  Needs
+ *                    down_scratch (not combined with token_split > 1).
+ *                    1 = off.  0 = default: 2 when down_scratch is given and
+ *                    the token ranges would otherwise be used (H / 16 < 256,
+ *                    B >= 2), else 1.
+ *   down_scratch,    down: device memory for the expert split, at least
+ *   down_scratch_bytes  wd_down_scratch_bytes(B, H) bytes, 256-byte aligned:
+ *                    one counter per block of 16 outputs, then the partial
+ *                    sums.  Its first H / 16 * 4 bytes must be zero before
+ *                    the first call; every call leaves them zero.  Calls that
+ *                    overlap in time must not share it.
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end
  *                    time into them (hipExtLaunchKernelGGL), so the elapsed
@@ -173,6 +190,9 @@ typedef struct wd_launch {
     int weight_loads;
     int token_split;
     int lds_bytes;
+    int expert_split;
+    void *down_scratch;
+    size_t down_scratch_bytes;
 } wd_launch;
 
 /* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section
@@ -180,10 +200,11 @@ typedef struct wd_launch {
  * act[b,k,j] = BF16(SiLU(g) * u) with g, u the dot products of x[b] with gate
  * row j and up row I+j of expert e = topk_ids[b,k], MXFP8 converted exactly
  * as it is read, FP32 accumulation, x read once for both.  Below 24 tokens
- * (the default token form) one 64-lane wave serves each (token, slot, block
- * of rows) and reduces across its lanes: no LDS, no barrier.  From 24 tokens
- * the default is the expert form on the matrix cores (wd_launch.form 3, or 4
- * when H is a multiple of 256): one wave per (expert, 16 rows) reads each
+ * (16 when H >= 4096; the default token form) one 64-lane wave serves each
+ * (token, slot, block of rows) and reduces across its lanes: no LDS, no
+ * barrier.  From there on the default is the expert form on the matrix cores
+ * (wd_launch.form 3; form 4 is an equivalent variant): one wave per
+ * (expert, 16 rows) reads each
  * weight row once for all slots routed to that expert, stages its codes in
  * its own LDS region and computes the same sums on v_mfma_f32_16x16x32_bf16
  * in another order. */
@@ -213,7 +234,12 @@ int wd_down_ex(const uint16_t *act, const int32_t *topk_ids, const float *topk_w
                int B, int K, int E, int H, int I, const wd_launch *cfg, void *stream);
 
 /* Whole layer: wd_gate_up into `workspace` (used as act[B,K,I]), then wd_down,
- * both on `stream`.  workspace_bytes must be >= wd_workspace_bytes(B, K, I). */
+ * both on `stream`.  workspace_bytes must be >= wd_workspace_bytes(B, K, I).
+ * With workspace_bytes >= wd_layer_workspace_bytes(B, K, H, I) (and the
+ * workspace 256-byte aligned) the rest of the workspace serves the down
+ * kernel's expert split (see wd_launch.expert_split); its counters are
+ * cleared by this call's gate/up kernel, so the workspace needs no
+ * preparation. */
 int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                   const uint8_t *w_gu, const uint8_t *s_gu,
                   const uint8_t *w_d, const uint8_t *s_d,
@@ -250,6 +276,15 @@ int wd_route(const float *logits, int B, int E, int K, int32_t *topk_ids, float 
 
 /* Bytes of the intermediate act[B,K,I] (BF16); 0 for invalid sizes. */
 size_t wd_workspace_bytes(int B, int K, int I);
+
+/* Bytes of the down kernel's expert-split scratch (wd_launch.down_scratch):
+ * H / 16 counters padded to 256 bytes, then 2 * B * H FP32 partial sums;
+ * 0 for invalid sizes. */
+size_t wd_down_scratch_bytes(int B, int H);
+
+/* Workspace of wd_moe_decode that also holds the expert-split scratch:
+ * act[B,K,I] rounded up to 256 bytes plus wd_down_scratch_bytes(B, H). */
+size_t wd_layer_workspace_bytes(int B, int K, int H, int I);
 
 /* Static string naming a status code (never NULL). */
 const char *wd_status_string(int status);

@@ -46,7 +46,8 @@ class Launch(C.Structure):
                 ("order", C.c_int), ("xcd_remap", C.c_int),
                 ("start_event", C.c_void_p), ("stop_event", C.c_void_p), ("math", C.c_int),
                 ("lanes_per_row", C.c_int), ("form", C.c_int), ("weight_loads", C.c_int),
-                ("token_split", C.c_int), ("lds_bytes", C.c_int)]
+                ("token_split", C.c_int), ("lds_bytes", C.c_int), ("expert_split", C.c_int),
+                ("down_scratch", C.c_void_p), ("down_scratch_bytes", C.c_size_t)]
 
 
 class ECLaunch(C.Structure):
@@ -68,6 +69,8 @@ _sig = {
     "wd_moe_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _I, _I, _I, _I, _I, _P]),
     "wd_moe_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "wd_workspace_bytes": (_S, [_I, _I, _I]),
+    "wd_down_scratch_bytes": (_S, [_I, _I]),
+    "wd_layer_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "wd_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "wd_status_string": (C.c_char_p, [_I]),
     "wd_dequant_probe": (_I, [_P, _P]),
@@ -139,6 +142,12 @@ def _cfg(cfg):
         return None
     if isinstance(cfg, Launch):
         return C.byref(cfg)
+    cfg = dict(cfg)
+    scr = cfg.pop("down_scratch", None)
+    if isinstance(scr, torch.Tensor):     # a device tensor: its pointer and size
+        cfg["down_scratch"], cfg["down_scratch_bytes"] = scr.data_ptr(), scr.numel() * scr.element_size()
+    elif scr is not None:
+        cfg["down_scratch"] = scr
     return C.byref(Launch(**cfg))
 
 
@@ -198,6 +207,21 @@ def workspace_bytes(B: int, K: int, I: int) -> int:
     return _lib.wd_workspace_bytes(B, K, I)
 
 
+def down_scratch_bytes(B: int, H: int) -> int:
+    return _lib.wd_down_scratch_bytes(B, H)
+
+
+def layer_workspace_bytes(B: int, K: int, H: int, I: int) -> int:
+    return _lib.wd_layer_workspace_bytes(B, K, H, I)
+
+
+def down_scratch(B: int, H: int, device="cuda") -> torch.Tensor:
+    """Zeroed scratch for the down kernel's expert split (wd_launch.down_scratch);
+    every call leaves its counters zero again, so it can be reused by calls in
+    stream order."""
+    return torch.zeros(max(down_scratch_bytes(B, H), 256), dtype=torch.uint8, device=device)
+
+
 def moe_decode(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, out=None, workspace=None, stream=None):
     """The whole layer (gate/up then down) on one stream; returns out[B,H] bf16."""
     E, H, I = _dims(w_gu)
@@ -209,7 +233,7 @@ def moe_decode(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, out=None, workspace=No
     if out is None:
         out = torch.empty((B, H), dtype=torch.bfloat16, device=x.device)
     _dev(out, "out", _BF16, (B, H))
-    need = workspace_bytes(B, K, I)
+    need = layer_workspace_bytes(B, K, H, I)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _dev(workspace, "workspace", (torch.uint8, torch.bfloat16))

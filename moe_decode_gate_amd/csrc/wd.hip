@@ -57,9 +57,11 @@ int check_dims(int B, int K, int E, int H, int I) {
 //   gate/up, B 5..23: 32 lanes per row, 4 rows per lane group (8 per wave),
 //          row-block-major order with XCD-contiguous numbering, so the tokens
 //          that share an expert row read it from the same L2 while resident;
-//   gate/up, B >= 24: the expert form on the matrix cores (one wave per
-//          expert row block; equal at B = 24, 70 against 85 us at B = 32 and
-//          75 against 136 us at B = 64), register-staged (form 3; the form that
+//   gate/up, B >= 24 (B >= 16 when H >= 4096): the expert form on the matrix
+//          cores (one wave per expert row block; equal at B = 24, 70 against
+//          85 us at B = 32 and 75 against 136 us at B = 64; on the 4096 / 1536
+//          layer 158 against 181 us at B = 16, 120 against 99 at B = 8),
+//          register-staged (form 3; the form that
 //          streams its codes into LDS measured no faster: 70.9 against 71.7 us
 //          at B = 32, and slower on the 4096 / 1536 layer, 137 against 121 us
 //          at B = 8);
@@ -78,8 +80,9 @@ int check_dims(int B, int K, int E, int H, int I) {
 // (43 against 49 us at B = 8, where the FP32 math took 225 us).
 // form4_ok: the gate/up kernel that streams codes into LDS applies (rows of a multiple of 256
 // elements, 4-byte-aligned scale bytes, x within one 2 GB buffer resource).
+// have_scratch: the down kernel was given scratch for its expert split.
 int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, wd_launch *out,
-            bool form4_ok = false) {
+            bool form4_ok = false, bool have_scratch = false) {
     wd_launch c = in ? *in : wd_launch{};
     const bool batch = down ? B >= 3 : B >= 5;
     const bool wide = (long long)K * I > 6144;      // down: more than 6 act chunks per lane
@@ -89,7 +92,7 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.form == 0) {
         const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 24) && B <= wd::kDnMfmaMaxB &&
                                      (long long)B * K <= wd::kDnMfmaMaxSlots && E <= wd::kDnMfmaMaxE
-                               : untuned && B >= 24;
+                               : untuned && (B >= 24 || (H >= 4096 && B >= 16));
         c.form = mfma ? 3 : 1;
     }
     if (c.form >= 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
@@ -101,7 +104,14 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
         // take slots in groups of 8 where 16 waves take them in groups of 4, each group
         // streaming the expert's rows once (4096 / 1536 layer, Zipf routing: B = 8 43 against
         // 45 us, B = 32 98 against 118)
-        if (c.token_split == 0) c.token_split = (H / 16 < 256 && B >= 2) ? 2 : 1;
+        // With scratch for the partial sums, the two workgroups of a block split the experts
+        // instead (even / odd ids, all tokens each): every Wd row is read once, and each
+        // workgroup streams about half the routed experts where a token range streams the
+        // union of its tokens' experts, about two thirds of them at B = 32.
+        const bool few_blocks = H / 16 < 256 && B >= 2;
+        if (c.expert_split == 0)
+            c.expert_split = (have_scratch && few_blocks && (c.token_split == 0 || c.token_split == 1)) ? 2 : 1;
+        if (c.token_split == 0) c.token_split = (few_blocks && c.expert_split == 1) ? 2 : 1;
         if (c.waves_per_block == 0) c.waves_per_block = c.token_split > 1 ? 16 : 8;
     }
     if (c.waves_per_block == 0)
@@ -154,6 +164,10 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.token_split != 1 && c.token_split != 2 && c.token_split != 4) return WD_ERR_UNSUPPORTED;
     if (c.token_split != 1 && !(down && c.form == 3)) return WD_ERR_UNSUPPORTED;
     if (c.lds_bytes < 0 || c.lds_bytes > 65536) return WD_ERR_UNSUPPORTED;
+    // the expert split: the matrix-core down only, with scratch, not combined with token ranges
+    if (c.expert_split == 0) c.expert_split = 1;
+    if (c.expert_split != 1 && c.expert_split != 2) return WD_ERR_UNSUPPORTED;
+    if (c.expert_split == 2 && !(down && c.form == 3 && have_scratch && c.token_split == 1)) return WD_ERR_UNSUPPORTED;
     *out = c;
     return WD_OK;
 }
@@ -267,7 +281,7 @@ int launch(KernelFn fn, LayerArgs a, const wd_launch &c, hipStream_t s) {
 
 int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, const uint8_t *s_gu,
                  uint16_t *act, int B, int K, int E, int H, int I, const wd_launch *cfg,
-                 void *stream, bool checked_device) {
+                 void *stream, bool checked_device, int *zero_ptr = nullptr, int zero_n = 0) {
     int rc = check_dims(B, K, E, H, I);
     if (rc) return rc;
     if (!w_gu || !s_gu) return WD_ERR_NULL;
@@ -299,12 +313,46 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     a.nrowblk = I / rows_per_wave;
     a.nwaves = (c.form == 1 ? B * K : E) * a.nrowblk;
     a.order = c.order; a.remap = c.xcd_remap;
+    a.zero_ptr = zero_ptr; a.zero_n = zero_ptr ? zero_n : 0;
     return launch(fn, a, c, (hipStream_t)stream);
+}
+
+// Bytes of the down kernel's expert-split scratch: one counter per 16-output
+// block (padded to 256 bytes), then the partial outputs [2][H/16][B][16] FP32.
+size_t down_counter_bytes(int H) { return ((size_t)(H / 16) * 4 + 255) / 256 * 256; }
+size_t down_scratch_bytes(int B, int H) { return down_counter_bytes(H) + (size_t)2 * B * H * 4; }
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const uint8_t *w_d,
+              const uint8_t *s_d, uint16_t *out, int B, int K, int E, int H, int I,
+              const wd_launch *cfg, void *stream, bool checked_device,
+              void *scratch_in, size_t scratch_bytes_in);
+
+// Both kernels of one layer step on `stream`, act[B,K,I] at the start of `ws`; when `ws` also
+// holds the down kernel's expert-split scratch after it, the gate/up kernel clears that
+// scratch's counters first (the down kernel leaves them zero again).  Arguments already checked.
+int layer(const uint16_t *x, const int32_t *ids, const float *tw, const uint8_t *w_gu, const uint8_t *s_gu,
+          const uint8_t *w_d, const uint8_t *s_d, void *ws, size_t ws_bytes, uint16_t *out,
+          int B, int K, int E, int H, int I, void *stream) {
+    uint16_t *act = static_cast<uint16_t *>(ws);
+    const size_t act_bytes = round256((size_t)B * K * I * 2u);
+    uint8_t *scr = nullptr;
+    size_t scr_bytes = 0;
+    int *counters = nullptr;
+    if (ws_bytes >= act_bytes + down_scratch_bytes(B, H) && aligned(ws, 256)) {
+        scr = static_cast<uint8_t *>(ws) + act_bytes;
+        scr_bytes = ws_bytes - act_bytes;
+        counters = reinterpret_cast<int *>(scr);
+    }
+    int rc = gate_up_impl(x, ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, true, counters, H / 16);
+    if (rc) return rc;
+    return down_impl(act, ids, tw, w_d, s_d, out, B, K, E, H, I, nullptr, stream, true, scr, scr_bytes);
 }
 
 int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const uint8_t *w_d,
               const uint8_t *s_d, uint16_t *out, int B, int K, int E, int H, int I,
-              const wd_launch *cfg, void *stream, bool checked_device) {
+              const wd_launch *cfg, void *stream, bool checked_device,
+              void *scratch_in, size_t scratch_bytes_in) {
     int rc = check_dims(B, K, E, H, I);
     if (rc) return rc;
     if (!w_d || !s_d) return WD_ERR_NULL;
@@ -312,8 +360,13 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
     if (!aligned(w_d, 16) ||
         (B > 0 && (!aligned(act, 16) || !aligned(ids, 4) || !aligned(tw, 4) || !aligned(out, 2))))
         return WD_ERR_ALIGN;
+    // scratch for the expert split: the caller's (wd_launch.down_scratch) or the layer workspace's
+    void *scr = scratch_in;
+    size_t scr_bytes = scratch_bytes_in;
+    if (cfg && cfg->down_scratch) { scr = cfg->down_scratch; scr_bytes = cfg->down_scratch_bytes; }
+    const bool have_scratch = scr && aligned(scr, 256) && B > 0 && scr_bytes >= down_scratch_bytes(B, H);
     wd_launch c;
-    if ((rc = resolve(cfg, B, K, E, H, I, true, &c))) return rc;
+    if ((rc = resolve(cfg, B, K, E, H, I, true, &c, false, have_scratch))) return rc;
     if (c.form == 3) {
         // every slot's id held in registers (8 per lane), per-wave accumulators for 64 tokens,
         // expert ids packed in 10 bits
@@ -332,7 +385,12 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         a.B = B; a.K = K; a.E = E; a.H = H; a.I = I;
         a.nrowblk = H / 16;
         a.tsplit = c.token_split;
-        const int blocks = a.nrowblk * c.token_split;
+        a.esplit = c.expert_split;
+        if (c.expert_split > 1) {
+            a.dcount = static_cast<int *>(scr);
+            a.dpart = reinterpret_cast<float *>(static_cast<uint8_t *>(scr) + down_counter_bytes(H));
+        }
+        const int blocks = a.nrowblk * c.token_split * c.expert_split;
         a.nwaves = blocks * c.waves_per_block;
         a.nblocks = blocks;
         a.wpb = c.waves_per_block;
@@ -387,18 +445,29 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids, const uint8_t *w_g
 
 int wd_down(const uint16_t *act, const int32_t *topk_ids, const float *topk_w, const uint8_t *w_d,
             const uint8_t *s_d, uint16_t *out, int B, int K, int E, int H, int I, void *stream) {
-    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, false);
+    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, false, nullptr, 0);
 }
 
 int wd_down_ex(const uint16_t *act, const int32_t *topk_ids, const float *topk_w, const uint8_t *w_d,
                const uint8_t *s_d, uint16_t *out, int B, int K, int E, int H, int I,
                const wd_launch *cfg, void *stream) {
-    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, cfg, stream, false);
+    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, cfg, stream, false, nullptr, 0);
 }
 
 size_t wd_workspace_bytes(int B, int K, int I) {
     if (B < 0 || K < 1 || I < 32 || I % 32) return 0;
     return (size_t)B * (size_t)K * (size_t)I * 2u;
+}
+
+size_t wd_down_scratch_bytes(int B, int H) {
+    if (B < 1 || H < 32 || H % 32) return 0;
+    return down_scratch_bytes(B, H);
+}
+
+size_t wd_layer_workspace_bytes(int B, int K, int H, int I) {
+    const size_t act = wd_workspace_bytes(B, K, I);
+    if (B < 1 || act == 0 || H < 32 || H % 32) return act;
+    return round256(act) + down_scratch_bytes(B, H);
 }
 
 int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
@@ -418,9 +487,7 @@ int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_
         return WD_ERR_ALIGN;
     if (B == 0) return WD_OK;
     if ((rc = check_device())) return rc;
-    rc = gate_up_impl(x, topk_ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, true);
-    if (rc) return rc;
-    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, true);
+    return layer(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, workspace, workspace_bytes, out, B, K, E, H, I, stream);
 }
 
 }  // extern "C"
@@ -472,12 +539,13 @@ int wd_moe_decode_noalloc(const uint16_t *x, const int32_t *topk_ids, const floa
         return WD_ERR_ALIGN;
     if (B == 0) return WD_OK;
     if ((rc = check_device())) return rc;
-    uint16_t *act = static_cast<uint16_t *>(scratch_ptr());
-    if (!act) return WD_ERR_DEVICE;
-    // gate/up writes every act element the down kernel reads, so nothing is cleared
-    rc = gate_up_impl(x, topk_ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, true);
-    if (rc) return rc;
-    return down_impl(act, topk_ids, topk_w, w_d, s_d, out, B, K, E, H, I, nullptr, stream, true);
+    void *ws = scratch_ptr();
+    if (!ws) return WD_ERR_DEVICE;
+    // act at the start; the down kernel's expert-split scratch after it when it fits (its
+    // counters cleared by the gate/up kernel); gate/up writes every act element the down kernel
+    // reads, so nothing else is cleared
+    return layer(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, ws, (size_t)WD_NOALLOC_SCRATCH_BYTES, out,
+                 B, K, E, H, I, stream);
 }
 
 const char *wd_status_string(int status) {

@@ -44,7 +44,21 @@ struct LayerArgs {
     int tsplit;              // down, matrix-core form: workgroups per 16-output block, each for its own tokens
     int nblocks;             // workgroups in the grid
     int wpb;                 // waves per workgroup
+    int esplit;              // down, matrix-core form: workgroups per 16-output block, each for one class of experts
+    float *dpart;            // down, expert split: partial outputs [esplit][H/16][B][16] (FP32)
+    int *dcount;             // down, expert split: per 16-output block, how many of its workgroups finished
+    int *zero_ptr;           // gate/up: words the first workgroup sets to zero before anything else (or null)
+    int zero_n;
 };
+
+// The first workgroup clears zero_n words at zero_ptr (the down kernel's
+// per-block counters of the expert split, when both kernels run as one layer:
+// the down kernel, launched after this one on the same stream, finds them
+// zero).
+__device__ __forceinline__ void zero_words(const LayerArgs &a) {
+    if (a.zero_n > 0 && blockIdx.x == 0)
+        for (int i = (int)threadIdx.x; i < a.zero_n; i += 64 * a.wpb) a.zero_ptr[i] = 0;
+}
 
 // Makes the compiler load the kernel arguments a wave needs first in one
 // batch at the start (an empty asm that takes them as scalar operands), so
@@ -105,6 +119,7 @@ __device__ __forceinline__ int logical_wave(const LayerArgs &a) {
 template <int CPL, int R, int LPR, bool TAIL, int MATH, bool NT>
 __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
     constexpr int G = 64 / LPR;
+    zero_words(a);
     const int lane = threadIdx.x & 63;
     const int grp = lane / LPR, tl = lane % LPR;
     args_early(a);
@@ -213,6 +228,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
 // ---------------------------------------------------------------------------
 template <int CPL, int R, bool TAIL>
 __global__ __launch_bounds__(256) void gate_up_expert_kernel(LayerArgs a) {
+    zero_words(a);
     const int lane = threadIdx.x & 63;
     const int t = logical_wave(a);
     if (t >= a.nwaves) return;
@@ -371,6 +387,7 @@ static_assert(kMfmaSteps == 4, "one 8-byte scale load and 256 bytes per row cove
 
 template <bool SC8>
 __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
+    zero_words(a);
     // per wave: the batch's 16 gate and 16 up rows x 256 bytes, 16-byte slots XOR-swizzled by row,
     // and each lane's E8M0 bytes of the batch (kept in LDS: a register copy of the prefetched
     // bytes would make the compute wait for the whole prefetch)
@@ -587,6 +604,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
 // ---------------------------------------------------------------------------
 template <int WPB>
 __global__ __launch_bounds__(64 * WPB) void gate_up_mfma_lds_kernel(LayerArgs a) {
+    zero_words(a);
     constexpr int kSeg = 8;                                // 16-byte segments per row per batch
     __shared__ u32x4 ring0[WPB][2][16][kSeg];              // slot 0: [wave][gate, up][row][slot]
     __shared__ u32x4 ring1[WPB][2][16][kSeg];              // slot 1
@@ -955,8 +973,10 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
     const int hb = (int)blockIdx.x % a.nrowblk;
+    const int rg = (int)blockIdx.x / a.nrowblk;
+    const int part = rg & (a.esplit - 1);              // expert split: this workgroup's experts are e % esplit == part
     const int tpr = (a.B + a.tsplit - 1) / a.tsplit;   // tokens per range
-    const int tb0 = (int)blockIdx.x / a.nrowblk * tpr; // this workgroup's tokens: [tb0, tb1)
+    const int tb0 = rg / a.esplit * tpr;               // this workgroup's tokens: [tb0, tb1)
     const int tb1 = min(a.B, tb0 + tpr);
     if (tb0 >= tb1) return;                            // workgroup-uniform: a range past the batch
     const int H = a.H, I = a.I, E = a.E;
@@ -991,12 +1011,15 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
             const unsigned e2 = (unsigned)tid[k2] < (unsigned)E ? (unsigned)tid[k2] : (unsigned)E;
             rank += e2 < ek || (e2 == ek && k2 < k);
         }
-        lord[tl * K + rank] = (int16_t)k;
+        // slots whose expert this workgroup does not serve (another class of the expert split, or
+        // an id outside [0, E)) are marked and skipped by the fold
+        const bool mine = ek < (unsigned)E && (int)(ek & (unsigned)(a.esplit - 1)) == part;
+        lord[tl * K + rank] = (int16_t)(k | (mine ? 0 : 0x4000));
     }
     __syncthreads();                                   // lused cleared before it is marked
 #pragma unroll
     for (int u = 0; u < kDnIdRegs; ++u)
-        if ((unsigned)idv[u] < (unsigned)E) lused[idv[u]] = 1;
+        if ((unsigned)idv[u] < (unsigned)E && (idv[u] & (a.esplit - 1)) == part) lused[idv[u]] = 1;
     if (a.tsplit > 1) {
         const int BK = a.B * K;
         for (int t = (int)threadIdx.x; t < BK; t += 64 * W) {
@@ -1220,15 +1243,63 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     }
 
     __syncthreads();
-    for (int t = (int)threadIdx.x; t < (tb1 - tb0) * 16; t += 64 * W) {
-        const int bl = t >> 4, r = t & 15, b = tb0 + bl;
+    // the fold: thread t owns output (token tb0 + t / 16, row t % 16) of the block
+    constexpr int kPer = (kDnMfmaMaxB * 16 + 64 * W - 1) / (64 * W);
+    const int nt = (tb1 - tb0) * 16;
+    float yv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int t = (int)threadIdx.x + 64 * W * j;
         float y = 0.f;
-        for (int i = 0; i < K; ++i) {                  // the token's slots in fold order
-            const int sl = bl * K + lord[bl * K + i];
-            y = __builtin_fmaf(lw[sl], pv[sl][r >> 2][r & 3], y);
+        if (t < nt) {
+            const int bl = t >> 4, r = t & 15;
+            for (int i = 0; i < K; ++i) {              // the token's slots in fold order
+                const int o = lord[bl * K + i];
+                if (o & 0x4000) continue;              // not one of this workgroup's experts
+                const int sl = bl * K + o;
+                y = __builtin_fmaf(lw[sl], pv[sl][r >> 2][r & 3], y);
+            }
+            if ((bad_tok >> (tb0 + bl)) & 1) y = __builtin_nanf("");
         }
-        if ((bad_tok >> b) & 1) y = __builtin_nanf("");
-        a.out[(size_t)b * H + (size_t)hb * 16 + r] = to_bf16(y);
+        yv[j] = y;
+    }
+    if (a.esplit == 1) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int t = (int)threadIdx.x + 64 * W * j;
+            if (t < nt) a.out[(size_t)(tb0 + (t >> 4)) * H + (size_t)hb * 16 + (t & 15)] = to_bf16(yv[j]);
+        }
+        return;
+    }
+    // Expert split (two workgroups per block, all tokens each): this class's sums go to the
+    // scratch; the second of the two workgroups to finish -- found with one counter per block,
+    // nobody waits -- adds the other's in class order, part 0 + part 1, and writes the output,
+    // then clears the counter for the next call.  A token's result still depends on its own
+    // slots only.
+    float *mine = a.dpart + ((size_t)part * a.nrowblk + hb) * ((size_t)a.B * 16);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int t = (int)threadIdx.x + 64 * W * j;
+        if (t < nt) mine[t] = yv[j];
+    }
+    __shared__ int lsecond;
+    __syncthreads();                                   // the workgroup's sums are stored
+    if (threadIdx.x == 0) {
+        const int prev = __hip_atomic_fetch_add(a.dcount + hb, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        lsecond = prev == 1;
+        if (prev == 1) __hip_atomic_store(a.dcount + hb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!lsecond) return;
+    const float *other = a.dpart + ((size_t)(1 - part) * a.nrowblk + hb) * ((size_t)a.B * 16);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int t = (int)threadIdx.x + 64 * W * j;
+        if (t < nt) {
+            const float o = __builtin_nontemporal_load(other + t);
+            const float y = part == 0 ? yv[j] + o : o + yv[j];
+            a.out[(size_t)(tb0 + (t >> 4)) * H + (size_t)hb * 16 + (t & 15)] = to_bf16(y);
+        }
     }
 }
 

@@ -33,7 +33,7 @@ import torch
 __all__ = [
     "LayerSpec", "CONFIGS", "Layer", "Tokens",
     "quantize_mxfp8", "bf16_bits", "make_layer", "make_tokens",
-    "layer_unique_bytes", "expert_bytes", "make_logits",
+    "layer_unique_bytes", "expert_bytes", "make_logits", "expert_weights_fp32",
 ]
 
 BLOCK = 32          # MX block: elements sharing one E8M0 scale
@@ -133,11 +133,18 @@ def _expert_stream(spec: LayerSpec, kind: int, e: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence(spec.seed, spawn_key=(kind, e)))
 
 
-def _draw_expert(spec: LayerSpec, e: int, std: float):
+def expert_weights_fp32(spec: LayerSpec, e: int, std: float = 0.02):
+    """Expert e's weights as drawn, before MXFP8 quantization: (gate/up [2I, H],
+    down [H, I]) float32, from the same streams make_layer quantizes."""
     rg = _expert_stream(spec, _KIND_WGU, e)
     gu = rg.standard_normal((2 * spec.I, spec.H), dtype=np.float32) * np.float32(std)
     rd = _expert_stream(spec, _KIND_WD, e)
     dn = rd.standard_normal((spec.H, spec.I), dtype=np.float32) * np.float32(std)
+    return gu, dn
+
+
+def _draw_expert(spec: LayerSpec, e: int, std: float):
+    gu, dn = expert_weights_fp32(spec, e, std)
     return quantize_mxfp8(gu), quantize_mxfp8(dn)
 
 

@@ -17,4 +17,5 @@ from .ref import (  # noqa: F401
     e4m3_table, e8m0_table, dequant, bf16_value, bf16_rne, round_f32, silu,
     gate_up, down, moe_decode, route, max_threads, lib_path,
     e4m3_encode, mxfp8_quantize, moe_decode_exact, moe_decode_conventional,
+    moe_decode_dense_weights,
 )

@@ -214,3 +214,31 @@ def route(logits, K: int):
 
 def max_threads() -> int:
     return _load().oracle_max_threads()
+
+
+def moe_decode_dense_weights(x, ids, w, gu_of, dn_of):
+    """Reference y[B,H] in FP64 of the layer with arbitrary real weights: for
+    token b, y[b] = sum_k w[b,k] * Wd_e (SiLU(Wg_e x[b]) * (Wu_e x[b])) with
+    e = ids[b,k], no rounding anywhere.  gu_of(e) gives expert e's gate/up
+    rows [2I, H] (gate rows first) and dn_of(e) its down rows [H, I], any
+    float dtype; each expert's weights are fetched once, for all the slots
+    that chose it.  Used with the weights as drawn before MXFP8 quantization,
+    it is the full-precision reference of the accuracy experiment."""
+    xb = np.asarray(x, np.uint16).astype(np.uint32) << 16
+    xf = xb.view(np.float32).astype(np.float64)
+    ids = np.asarray(ids)
+    w = np.asarray(w, np.float64)
+    y = None
+    for e in np.unique(ids):
+        bs, ks = np.nonzero(ids == e)
+        gu = np.asarray(gu_of(int(e)), np.float64)
+        dn = np.asarray(dn_of(int(e)), np.float64)
+        I = gu.shape[0] // 2
+        xs = xf[bs]                                   # [n, H], one row per slot
+        g = xs @ gu[:I].T
+        u = xs @ gu[I:].T
+        a = g / (1.0 + np.exp(-g)) * u                # SiLU(g) * u, [n, I]
+        if y is None:
+            y = np.zeros((ids.shape[0], dn.shape[0]))
+        np.add.at(y, bs, w[bs, ks][:, None] * (a @ dn.T))
+    return y

@@ -282,3 +282,29 @@ def test_lds_gate_up_form_limits():
     assert g(H=96) == -7 and g(H=288) == -7 and g(s=A + 2) == -7 and g(waves_per_block=3) == -7
     assert g(H=8192, B=131072) == -7                     # x of 2 GB: past the buffer resource's range
     assert lib.wd_down_ex(A, A, A, A, A, A, 32, 8, 128, 2048, 768, C.byref(wd.Launch(form=4)), None) == -7
+
+
+def test_down_expert_split_host_checks():
+    """The down kernel's expert split needs scratch of wd_down_scratch_bytes(B, H)
+    (256-byte aligned), the matrix-core form and no token ranges."""
+    assert lib.wd_down_scratch_bytes(32, 2048) == 512 + 2 * 32 * 2048 * 4
+    assert lib.wd_down_scratch_bytes(1, 4096) == 1024 + 2 * 4096 * 4
+    assert lib.wd_down_scratch_bytes(0, 2048) == 0 and lib.wd_down_scratch_bytes(1, 100) == 0
+    assert lib.wd_layer_workspace_bytes(32, 8, 2048, 768) == 32 * 8 * 768 * 2 + lib.wd_down_scratch_bytes(32, 2048)
+    assert lib.wd_layer_workspace_bytes(1, 8, 2048, 96) == 1536 + lib.wd_down_scratch_bytes(1, 2048)
+    assert lib.wd_layer_workspace_bytes(1, 1, 2048, 96) == 256 + lib.wd_down_scratch_bytes(1, 2048)  # act padded
+    need = lib.wd_down_scratch_bytes(32, 2048)
+
+    def dnx(scr=A, nbytes=need, B=32, **kw):
+        cfg = wd.Launch(down_scratch=scr, down_scratch_bytes=nbytes, **kw)
+        return lib.wd_down_ex(A, A, A, A, A, A, B, 8, 128, 2048, 768, C.byref(cfg), None)
+
+    assert dnx(form=3, expert_split=2) == -5
+    assert dnx() == -5                                        # the default takes it
+    assert dnx(form=3, expert_split=2, token_split=2) == -7
+    assert dnx(form=3, expert_split=2, nbytes=need - 1) == -7
+    assert dnx(form=3, expert_split=2, scr=A + 16) == -7      # scratch not 256-byte aligned
+    assert dnx(form=1, expert_split=2) == -7
+    assert dnx(form=3, expert_split=3) == -7
+    assert dnx(scr=None, nbytes=0, form=3, expert_split=2) == -7
+    assert lib.wd_gate_up_ex(A, A, A, A, A, 32, 8, 128, 2048, 768, C.byref(wd.Launch(expert_split=2)), None) == -7

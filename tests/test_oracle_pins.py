@@ -462,6 +462,22 @@ def test_exact_reference_matches_dense_torch():
     np.testing.assert_allclose(y, _dense_exact(t.x, t.ids, t.w, L), rtol=1e-12, atol=1e-15)
 
 
+def test_dense_weights_reference_equals_exact_oracle_on_mxfp8_values():
+    """The FP64 reference with real-valued weights, given the MXFP8 weights'
+    exact values, is the C oracle's unrounded layer (to FP64 summation order);
+    and it is linear in the down weights (doubling them doubles y)."""
+    spec, L = _tiny_layer(12, 3, 192, 96, seed=73, std=0.1)
+    t = gen.make_tokens(spec, 4)
+    t4, t8 = oracle.e4m3_table(), oracle.e8m0_table()
+    gu = lambda e: t4[L.wgu[e]] * np.repeat(t8[L.sgu[e]], 32, axis=-1)
+    dn = lambda e: t4[L.wd[e]] * np.repeat(t8[L.sd[e]], 32, axis=-1)
+    y = oracle.moe_decode_dense_weights(t.x, t.ids, t.w, gu, dn)
+    ref = oracle.moe_decode_exact(t.x, t.ids, t.w, L.wgu, L.sgu, L.wd, L.sd)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+    y2 = oracle.moe_decode_dense_weights(t.x, t.ids, t.w, gu, lambda e: 2.0 * dn(e))
+    np.testing.assert_allclose(y2, 2.0 * y, rtol=1e-14, atol=1e-16)
+
+
 def test_conventional_numerics_match_torch_composition():
     """The conventional path rebuilt from library routines: torch's FP8 and
     BF16 conversions (via the generator's quantizer) and float64 matmuls."""
