@@ -65,7 +65,7 @@ def load_traffic(name: str):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the
     committed rocprofv3 counter summary, if it was taken on the current kernel
     source; else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_b1_b32.txt")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_layer_kernels.txt")
     try:
         lines = open(path).read().splitlines()
     except OSError:
@@ -302,7 +302,9 @@ def measure_large(torch, wd, gen, oracle, read_peak, batches=(1, 8, 32), steps=4
         r = measure(torch, wd, w, steps, warmup)
         cos, err, ymax = sampled_parity(oracle, L, w, [0, steps - 1])
         r.update(parity_cos_min=cos, parity_max_abs_err=err, parity_max_abs_y=ymax,
-                 frac_of_measured_read_peak=r["layer_GBps_graph"] / read_peak)
+                 frac_of_measured_read_peak=r["layer_GBps_graph"] / read_peak,
+                 roofline=roofline(r, "gate_up", f"gate_up_large_b{B}"),
+                 roofline_down=roofline(r, "down", f"down_large_b{B}"))
         eprint(f"[bench] large B={B}: {json.dumps(r)}")
         out.append(r)
         del w

@@ -172,6 +172,12 @@ enum wd_status {
  *                    sums.  Its first H / 16 * 4 bytes must be zero before
  *                    the first call; every call leaves them zero.  Calls that
  *                    overlap in time must not share it.
+ *   slots_per_pass   gate/up, form 3 only: 16 = each pass over an expert's 16-row
+ *                    block serves up to 16 of its slots (an expert with more
+ *                    slots is streamed once per 16); 32 = up to 32 slots per pass
+ *                    (two 16-slot tiles per weight batch; more registers, so
+ *                    fewer resident waves).  Bit-identical results.  0 = default
+ *                    (32 for form 3).
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end
  *                    time into them (hipExtLaunchKernelGGL), so the elapsed
@@ -193,6 +199,7 @@ typedef struct wd_launch {
     int expert_split;
     void *down_scratch;
     size_t down_scratch_bytes;
+    int slots_per_pass;
 } wd_launch;
 
 /* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section

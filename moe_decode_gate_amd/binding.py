@@ -47,7 +47,8 @@ class Launch(C.Structure):
                 ("start_event", C.c_void_p), ("stop_event", C.c_void_p), ("math", C.c_int),
                 ("lanes_per_row", C.c_int), ("form", C.c_int), ("weight_loads", C.c_int),
                 ("token_split", C.c_int), ("lds_bytes", C.c_int), ("expert_split", C.c_int),
-                ("down_scratch", C.c_void_p), ("down_scratch_bytes", C.c_size_t)]
+                ("down_scratch", C.c_void_p), ("down_scratch_bytes", C.c_size_t),
+                ("slots_per_pass", C.c_int)]
 
 
 class ECLaunch(C.Structure):

@@ -22,6 +22,8 @@
 // besides the intermediate and the output.
 #pragma once
 
+#include <type_traits>
+
 #include "wd_device.h"
 
 namespace wd {
@@ -385,7 +387,7 @@ struct MfmaBatch {                      // one wave's loads for kMfmaSteps 64-el
 };
 static_assert(kMfmaSteps == 4, "one 8-byte scale load and 256 bytes per row cover a batch");
 
-template <bool SC8>
+template <bool SC8, int NGMAX>
 __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     zero_words(a);
     // per wave: the batch's 16 gate and 16 up rows x 256 bytes, 16-byte slots XOR-swizzled by row,
@@ -480,30 +482,29 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     };
     refill();
 
-    for (;;) {
-        // the next up-to-16 slots routed to e, in slot order, one per lane 0..15
-        int my_slot = 0, cnt = 0;
-        for (;;) {
+    // One pass per up to 16 * NGMAX slots routed to e: the weight batches stream once per
+    // pass and feed one 16-slot tile, or with NGMAX 2 two when more than 16 slots remain (the
+    // second tile's columns are slots 16..31 of the pass), so an expert with up to 32 slots is
+    // read once; NGMAX 1 streams an expert with more than 16 slots once per 16 (from the L2
+    // when it still holds them) but needs fewer registers.  A (row, slot) sum is the same
+    // sequence of matrix instructions in every case.
+    constexpr int kPass = 16 * NGMAX;
+    auto pass = [&](auto ng_c, int my_slot, int cnt) {
+        constexpr int NG = decltype(ng_c)::value;
+        int slot[NG];
+        bool live[NG];
+        const uint16_t *xr[NG];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                while (mk[u] != 0 && cnt < 16) {
-                    const int s0 = chunk + 64 * u + (int)__builtin_ctzll(mk[u]);
-                    mk[u] &= mk[u] - 1;
-                    if (lane == cnt) my_slot = s0;
-                    ++cnt;
-                }
-            }
-            if (cnt == 16 || next_chunk >= BK) break;
-            refill();
+        for (int g = 0; g < NG; ++g) {
+            slot[g] = __shfl(my_slot, 16 * g + r16);
+            live[g] = 16 * g + r16 < cnt;
+            // lanes of empty columns read column 0's token (their products are never stored)
+            const int slot_any = live[g] ? slot[g] : __shfl(my_slot, 0);
+            xr[g] = a.x + (size_t)(slot_any / a.K) * H;
         }
-        if (cnt == 0) break;
-        const int slot = __shfl(my_slot, r16);
-        const bool live = r16 < cnt;
-        // lanes of empty columns read column 0's token (their products are never stored)
-        const int slot_any = live ? slot : __shfl(my_slot, 0);
-        const uint16_t *xr = a.x + (size_t)(slot_any / a.K) * H;
-
-        f32x4 cg = {0.f, 0.f, 0.f, 0.f}, cu = cg;
+        f32x4 cg[NG], cu[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) cg[g] = cu[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int s0 = s_lo; s0 < s_hi; s0 += kMfmaSteps) {
             // the batch's codes into the wave's LDS tile (LDS operations of one wave complete
             // in order, so the previous batch's reads are done)
@@ -513,32 +514,32 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
             stile[threadIdx.x >> 6][1][lane] = cur.su;
             // keep the prefetch below after these reads of cur, so it can reuse cur's registers
             __builtin_amdgcn_sched_barrier(0);
-            u32x4 x0[kMfmaSteps], x1[kMfmaSteps];
+            u32x4 x0[NG][kMfmaSteps], x1[NG][kMfmaSteps];
 #pragma unroll
-            for (int i = 0; i < kMfmaSteps; ++i) {
-                const int k = 64 * (s0 + i) + 16 * q;
-                const int kc = (s0 + i < s_hi && k < H) ? k : 64 * s_lo;
-                x0[i] = ld16(xr + kc);
-                x1[i] = ld16(xr + kc + 8);
-            }
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int i = 0; i < kMfmaSteps; ++i) {
+                    const int k = 64 * (s0 + i) + 16 * q;
+                    const int kc = (s0 + i < s_hi && k < H) ? k : 64 * s_lo;
+                    x0[g][i] = ld16(xr[g] + kc);
+                    x1[g][i] = ld16(xr[g] + kc + 8);
+                }
             // prefetch into the same registers (their codes are in LDS now): the next batch, this
-            // wave's first batch again for a further group, or else this batch again (unused; its
+            // wave's first batch again for a further pass, or else this batch again (unused; its
             // lines are still in the cache, so the load that keeps every batch alike costs no
             // HBM traffic)
             const bool more = s0 + kMfmaSteps < s_hi;
-            load_batch(more ? s0 + kMfmaSteps : cnt == 16 ? s_lo : s0, cur);
+            load_batch(more ? s0 + kMfmaSteps : cnt == kPass ? s_lo : s0, cur);
 #pragma unroll
             for (int i = 0; i < kMfmaSteps; ++i) {
                 const int k = 64 * (s0 + i) + 16 * q;
                 const bool ok = s0 + i < s_hi && k < H;
-                const bool xo = ok && live;
                 const int sh = 8 * (2 * i + (q >> 1));      // byte of block 2 (s0 + i) + q / 2
                 const uint64_t sgb = stile[threadIdx.x >> 6][0][lane], sub = stile[threadIdx.x >> 6][1][lane];
                 const uint32_t bg = (uint32_t)(sgb >> sh) & 0xFFu, bu = (uint32_t)(sub >> sh) & 0xFFu;
                 const float fg = e8m0_operand(ok ? bg : 127u), fu = e8m0_operand(ok ? bu : 127u);
-                const int slot = (4 * i + q) ^ r16;         // segment 4 i + q of row r16
-                const u32x4 wgi = ok ? wt[0][r16][slot] : zero, wui = ok ? wt[1][r16][slot] : zero;
-                const u32x4 xa = xo ? x0[i] : zero, xb = xo ? x1[i] : zero;
+                const int sl = (4 * i + q) ^ r16;           // segment 4 i + q of row r16
+                const u32x4 wgi = ok ? wt[0][r16][sl] : zero, wui = ok ? wt[1][r16][sl] : zero;
                 uint32_t gw[8], uw[8];
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
@@ -547,30 +548,64 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
                 }
                 const u32x4 g0 = {gw[0], gw[1], gw[2], gw[3]}, g1 = {gw[4], gw[5], gw[6], gw[7]};
                 const u32x4 u0 = {uw[0], uw[1], uw[2], uw[3]}, u1 = {uw[4], uw[5], uw[6], uw[7]};
-                cg = mfma_bf16(g0, xa, cg);
-                cg = mfma_bf16(g1, xb, cg);
-                cu = mfma_bf16(u0, xa, cu);
-                cu = mfma_bf16(u1, xb, cu);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const bool xo = ok && live[g];
+                    const u32x4 xa = xo ? x0[g][i] : zero, xb = xo ? x1[g][i] : zero;
+                    cg[g] = mfma_bf16(g0, xa, cg[g]);
+                    cg[g] = mfma_bf16(g1, xb, cg[g]);
+                    cu[g] = mfma_bf16(u0, xa, cu[g]);
+                    cu[g] = mfma_bf16(u1, xb, cu[g]);
+                }
             }
         }
-        if (live) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (!live[g]) continue;
             uint32_t packed[2];
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
                 uint32_t h2 = 0;
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
-                    const float gv = cg[r + d], uv = cu[r + d];
+                    const float gv = cg[g][r + d], uv = cu[g][r + d];
                     const float en = expf(-__builtin_fabsf(gv));
                     const float sig = gv >= 0.f ? 1.f / (1.f + en) : en / (1.f + en);
                     h2 |= (uint32_t)to_bf16(gv * sig * uv) << (16 * d);
                 }
                 packed[r >> 1] = h2;
             }
-            *reinterpret_cast<uint2 *>(a.out + (size_t)slot * I + (size_t)jb * 16 + 4 * q) =
+            *reinterpret_cast<uint2 *>(a.out + (size_t)slot[g] * I + (size_t)jb * 16 + 4 * q) =
                 make_uint2(packed[0], packed[1]);
         }
-        if (cnt < 16) break;
+    };
+
+    for (;;) {
+        // the next up-to-kPass slots routed to e, in slot order, one per lane 0..kPass-1
+        int my_slot = 0, cnt = 0;
+        for (;;) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                while (mk[u] != 0 && cnt < kPass) {
+                    const int s0 = chunk + 64 * u + (int)__builtin_ctzll(mk[u]);
+                    mk[u] &= mk[u] - 1;
+                    if (lane == cnt) my_slot = s0;
+                    ++cnt;
+                }
+            }
+            if (cnt == kPass || next_chunk >= BK) break;
+            refill();
+        }
+        if (cnt == 0) break;
+        if constexpr (NGMAX == 2) {
+            if (cnt > 16)
+                pass(std::integral_constant<int, 2>{}, my_slot, cnt);
+            else
+                pass(std::integral_constant<int, 1>{}, my_slot, cnt);
+        } else {
+            pass(std::integral_constant<int, 1>{}, my_slot, cnt);
+        }
+        if (cnt < kPass) break;
     }
 }
 
@@ -968,6 +1003,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __shared__ uint32_t lexp[W][kMaxExp];              // per wave: e | first entry << 10 | count << 20
     __shared__ float lw[kDnMfmaMaxSlots];              // router weights of the workgroup's slots, by slot - sl0
     __shared__ int16_t lord[kDnMfmaMaxSlots];          // per token of the range: its slots in fold order
+    __shared__ uint16_t lid[kDnMfmaMaxSlots];          // ids of the workgroup's slots, by slot - sl0 (E for bad ones)
     __shared__ uint8_t lused[kDnMfmaMaxE];             // experts some slot of the range is routed to
     __shared__ uint8_t loth[kDnMfmaMaxE];              // experts some slot of another range is routed to
     const int lane = threadIdx.x & 63;
@@ -999,16 +1035,26 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     }
     for (int t = (int)threadIdx.x; t < E; t += 64 * W) lused[t] = loth[t] = 0;
     const int K = a.K;
+    // the slots' router weights and ids into LDS, every load issued at once (a slot's fold rank
+    // below compares its id with its token's other K - 1 ids: read from memory one after the
+    // other, those were K dependent cache round trips ahead of the first weight load)
+#pragma unroll
+    for (int u = 0; u < kDnIdRegs; ++u) {
+        const int t = 64 * u + lane - sl0;             // idv[u] holds slot 64 u + lane
+        if (t >= 0 && t < sl1 - sl0 && wv == 0)
+            lid[t] = (uint16_t)((unsigned)idv[u] < (unsigned)E ? (unsigned)idv[u] : (unsigned)E);
+    }
+    for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) lw[t] = a.tw[sl0 + t];
+    __syncthreads();                                   // lused cleared and lid written
     for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) {
-        lw[t] = a.tw[sl0 + t];
         // fold order of the slot within its token: by expert, equal experts by slot (ids
         // outside [0, E) last; such tokens are NaN anyway)
         const int tl = t / K, k = t - tl * K;
-        const int32_t *tid = a.ids + sl0 + tl * K;
-        const unsigned ek = (unsigned)tid[k] < (unsigned)E ? (unsigned)tid[k] : (unsigned)E;
+        const uint16_t *tid = lid + tl * K;
+        const unsigned ek = tid[k];
         int rank = 0;
         for (int k2 = 0; k2 < K; ++k2) {
-            const unsigned e2 = (unsigned)tid[k2] < (unsigned)E ? (unsigned)tid[k2] : (unsigned)E;
+            const unsigned e2 = tid[k2];
             rank += e2 < ek || (e2 == ek && k2 < k);
         }
         // slots whose expert this workgroup does not serve (another class of the expert split, or
@@ -1016,7 +1062,6 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         const bool mine = ek < (unsigned)E && (int)(ek & (unsigned)(a.esplit - 1)) == part;
         lord[tl * K + rank] = (int16_t)(k | (mine ? 0 : 0x4000));
     }
-    __syncthreads();                                   // lused cleared before it is marked
 #pragma unroll
     for (int u = 0; u < kDnIdRegs; ++u)
         if ((unsigned)idv[u] < (unsigned)E && (idv[u] & (a.esplit - 1)) == part) lused[idv[u]] = 1;

@@ -217,6 +217,12 @@ def test_matrix_core_form_limits():
     assert gux(form=3, weight_loads=2) == -7
     assert gux(form=5) == -7
     assert gux(form=4, rows_per_wave=2) == -7 and gux(form=4, math=1) == -7
+    # slots per pass over an expert's rows: 16 or 32, the register-staged matrix-core gate/up only
+    assert gux(form=3, slots_per_pass=32) == -5 and gux(form=3, slots_per_pass=16) == -5
+    assert gux(form=3, slots_per_pass=8) == -7 and gux(form=3, slots_per_pass=64) == -7
+    assert gux(form=1, slots_per_pass=32) == -7 and gux(form=4, slots_per_pass=32) == -7
+    assert lib.wd_down_ex(A, A, A, A, A, A, 32, 8, 128, 2048, 768, C.byref(wd.Launch(form=3, slots_per_pass=32)),
+                          None) == -7
 
     # down on the matrix cores: 8 or 16 waves per workgroup, B <= 64, B * K <= 512, E <= 1024;
     # accepted configurations get as far as the device check (-5 here)

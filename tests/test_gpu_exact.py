@@ -291,7 +291,9 @@ def test_gate_up_lds_form_matches_register_form(H, B, routing):
     so the intermediate is bit-identical -- over one and several batches per
     row (H = 256 .. 4096), one and several 16-slot groups per expert (Zipf
     routing over 16 experts: up to ~70 slots on one expert at B = 100), a token
-    that repeats an expert, and experts no slot uses; reruns are identical."""
+    that repeats an expert, and experts no slot uses; reruns are identical.
+    Form 3 with 16 slots per pass over an expert's rows gives the same bits as
+    its default 32 (two 16-slot tiles per weight batch)."""
     spec = gen.LayerSpec(E=16, K=4, H=H, I=320, seed=96 + H + B)
     L = gen.make_layer(spec, threads=16)
     dl = DevLayer(L)
@@ -304,6 +306,8 @@ def test_gate_up_lds_form_matches_register_form(H, B, routing):
     assert np.array_equal(bits_of(a4), bits_of(a3))
     a4b, _ = run_layer(dl, dt, cfg_gu=dict(form=4, waves_per_block=2))
     assert np.array_equal(bits_of(a4b), bits_of(a3))
+    a16, _ = run_layer(dl, dt, cfg_gu=dict(form=3, slots_per_pass=16))
+    assert np.array_equal(bits_of(a16), bits_of(a3))
     if B <= 40:
         ref = oracle.gate_up(t.x, t.ids, L.wgu, L.sgu, nthreads=16)
         frac, ulps, within = act_flip_stats(bits_of(a4), ref)
