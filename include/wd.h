@@ -273,8 +273,8 @@ int wd_moe_decode_noalloc(const uint16_t *x, const int32_t *topk_ids, const floa
                           int B, int K, int E, int H, int I, void *stream);
 
 /* Router (top-k gating ahead of the layer; the pages name it as routing each
- * token to 8 of 128 experts: the Chinese summary's 传统路径的困境 section, p2
- * Method).  For each token b: topk_ids[b, 0..K) = the experts with the K
+ * token to 8 of 128 experts: the Chinese summary's 传统路径的困境 section, the
+ * English summary's Method section).  For each token b: topk_ids[b, 0..K) = the experts with the K
  * largest logits[b, :] (larger first; equal logits: lower expert index
  * first), topk_w[b, k] = softmax over the chosen logits,
  * exp(l_k - l_0) / sum_j exp(l_j - l_0), in FP32.  logits [B, E] fp32, row
