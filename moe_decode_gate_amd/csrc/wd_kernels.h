@@ -1320,28 +1320,33 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // scratch; the second of the two workgroups to finish -- found with one counter per block,
     // nobody waits -- adds the other's in class order, part 0 + part 1, and writes the output,
     // then clears the counter for the next call.  A token's result still depends on its own
-    // slots only.
+    // slots only.  The two workgroups may sit on different XCDs: the partial sums go through
+    // the coherence point (agent-scope stores, written through; agent-scope loads), the
+    // counter is a plain atomic, and no cache is written back or invalidated (an
+    // acquire-release atomic would write back the XCD's L2 in every workgroup).
     float *mine = a.dpart + ((size_t)part * a.nrowblk + hb) * ((size_t)a.B * 16);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int t = (int)threadIdx.x + 64 * W * j;
-        if (t < nt) mine[t] = yv[j];
+        if (t < nt) __hip_atomic_store(mine + t, yv[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __shared__ int lsecond;
-    __syncthreads();                                   // the workgroup's sums are stored
+    wait_vmcnt<0>();                                   // this wave's sums have reached the coherence point
+    __syncthreads();                                   // ... and every wave's
     if (threadIdx.x == 0) {
-        const int prev = __hip_atomic_fetch_add(a.dcount + hb, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int prev = __hip_atomic_fetch_add(a.dcount + hb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         lsecond = prev == 1;
         if (prev == 1) __hip_atomic_store(a.dcount + hb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!lsecond) return;
+    // issued after the counter said the other workgroup had added (its sums complete before)
     const float *other = a.dpart + ((size_t)(1 - part) * a.nrowblk + hb) * ((size_t)a.B * 16);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int t = (int)threadIdx.x + 64 * W * j;
         if (t < nt) {
-            const float o = __builtin_nontemporal_load(other + t);
+            const float o = __hip_atomic_load(other + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const float y = part == 0 ? yv[j] + o : o + yv[j];
             a.out[(size_t)(tb0 + (t >> 4)) * H + (size_t)hb * 16 + (t & 15)] = to_bf16(y);
         }
