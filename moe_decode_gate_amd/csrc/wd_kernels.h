@@ -15,11 +15,13 @@
 // Expert forms on the matrix cores (the defaults from 24 tokens, where tokens
 // share experts; a departure from the pages' design): gate/up takes one wave
 // per (expert, 16 intermediate rows) and down one workgroup per (16 output
-// dims, token range); both stage weight tiles through LDS (their own wave's
-// region, or with the down kernel's workgroup barrier the per-slot products),
-// and compute the same FP32 sums of exact products on
-// v_mfma_f32_16x16x32_bf16 in another order.  Still no atomic and no buffer
-// besides the intermediate and the output.
+// dims, token range or class of experts); both stage weight tiles through LDS
+// (their own wave's region, or with the down kernel's workgroup barrier the
+// per-slot products), and compute the same FP32 sums of exact products on
+// v_mfma_f32_16x16x32_bf16 in another order.  Gate/up keeps no atomic and no
+// buffer besides the intermediate; the down kernel's expert split adds one
+// counter per 16-output block and a scratch of FP32 partial sums, which the
+// second of the block's two workgroups adds in a fixed order.
 #pragma once
 
 #include <type_traits>
