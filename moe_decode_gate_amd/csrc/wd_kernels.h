@@ -450,9 +450,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
             }
         }
     };
-    // The first batch does not depend on the routing: issue it before reading topk_ids.
     MfmaBatch cur;
-    load_batch(s_lo, cur);
 
     if (e == 0) {              // NaN rows for slots whose id is outside [0, E)
         for (int base = 0; base < BK; base += 64) {
@@ -483,6 +481,15 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
         next_chunk += 512;
     };
     refill();
+    // The first batch only once the routing shows a slot for e (or the ids need more than one
+    // scan): a wave whose expert no slot uses reads no weights.
+    {
+        uint64_t any = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) any |= mk[u];
+        if (any == 0 && next_chunk >= BK) return;
+    }
+    load_batch(s_lo, cur);
 
     // One pass per up to 16 * NGMAX slots routed to e: the weight batches stream once per
     // pass and feed one 16-slot tile, or with NGMAX 2 two when more than 16 slots remain (the
