@@ -125,7 +125,7 @@ enum wd_status {
  *                    ahead in registers; needs H a multiple of 256, s_gu
  *                    4-byte aligned, B * H * 2 <= 0x7FFF0000 and 2 or 4
  *                    waves per workgroup (default 4).
- *                    Default: 3 when B >= 24 (B >= 16 when H >= 4096) and
+ *                    Default: 3 when B >= 20 (B >= 8 when H >= 4096) and
  *                    none of rows_per_wave, lanes_per_row, math,
  *                    weight_loads is set, else 1.
  *                    down: 1 = one wave per (token, block of output dims);
@@ -177,7 +177,7 @@ enum wd_status {
  *                    slots is streamed once per 16); 32 = up to 32 slots per pass
  *                    (two 16-slot tiles per weight batch; more registers, so
  *                    fewer resident waves).  Bit-identical results.  0 = default
- *                    (32 for form 3).
+ *                    (32 for form 3 from B = 16, else 16).
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end
  *                    time into them (hipExtLaunchKernelGGL), so the elapsed
@@ -206,8 +206,8 @@ typedef struct wd_launch {
  * "How the two kernels work"; the Chinese summary's "Gate/Up Kernel"):
  * act[b,k,j] = BF16(SiLU(g) * u) with g, u the dot products of x[b] with gate
  * row j and up row I+j of expert e = topk_ids[b,k], MXFP8 converted exactly
- * as it is read, FP32 accumulation, x read once for both.  Below 24 tokens
- * (16 when H >= 4096; the default token form) one 64-lane wave serves each
+ * as it is read, FP32 accumulation, x read once for both.  Below 20 tokens
+ * (8 when H >= 4096; the default token form) one 64-lane wave serves each
  * (token, slot, block of rows) and reduces across its lanes: no LDS, no
  * barrier.  From there on the default is the expert form on the matrix cores
  * (wd_launch.form 3; form 4 is an equivalent variant): one wave per

@@ -57,10 +57,13 @@ int check_dims(int B, int K, int E, int H, int I) {
 //   gate/up, B 5..23: 32 lanes per row, 4 rows per lane group (8 per wave),
 //          row-block-major order with XCD-contiguous numbering, so the tokens
 //          that share an expert row read it from the same L2 while resident;
-//   gate/up, B >= 24 (B >= 16 when H >= 4096): the expert form on the matrix
-//          cores (one wave per expert row block; equal at B = 24, 70 against
-//          85 us at B = 32 and 75 against 136 us at B = 64; on the 4096 / 1536
-//          layer 158 against 181 us at B = 16, 120 against 99 at B = 8),
+//   gate/up, B >= 20 (B >= 8 when H >= 4096): the expert form on the matrix
+//          cores (one wave per expert row block, and none for an expert no slot
+//          uses; Qwen-3 layer 58.6 against 61.5 us at B = 20, 70 against 85 at
+//          B = 32, 75 against 136 at B = 64, the token form ahead at B = 16, 52.9
+//          against 55.0; on the 4096 / 1536 layer with Zipf routing 96.2 against
+//          98.3 us at B = 8, 121.7 against 138.8 at B = 12, the token form ahead at
+//          B = 4),
 //          register-staged (form 3; the form that
 //          streams its codes into LDS measured no faster: 70.9 against 71.7 us
 //          at B = 32, and slower on the 4096 / 1536 layer, 137 against 121 us
@@ -92,7 +95,7 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.form == 0) {
         const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 24) && B <= wd::kDnMfmaMaxB &&
                                      (long long)B * K <= wd::kDnMfmaMaxSlots && E <= wd::kDnMfmaMaxE
-                               : untuned && (B >= 24 || (H >= 4096 && B >= 16));
+                               : untuned && (B >= 20 || (H >= 4096 && B >= 8));
         c.form = mfma ? 3 : 1;
     }
     if (c.form >= 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
@@ -164,11 +167,12 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.token_split != 1 && c.token_split != 2 && c.token_split != 4) return WD_ERR_UNSUPPORTED;
     if (c.token_split != 1 && !(down && c.form == 3)) return WD_ERR_UNSUPPORTED;
     if (c.lds_bytes < 0 || c.lds_bytes > 65536) return WD_ERR_UNSUPPORTED;
-    // slots per pass of the matrix-core gate/up over an expert's rows: 16 or 32.  Default 32:
-    // an expert with 17..32 slots is streamed once instead of twice (4096 / 1536 layer, Zipf
-    // routing: B = 16 164 -> 156 us, B = 32 218 -> 198 us; Qwen-3 layer B = 24..64 within 1%,
-    // where no expert has more than 16 slots)
-    if (c.slots_per_pass == 0) c.slots_per_pass = (!down && c.form == 3) ? 32 : 16;
+    // slots per pass of the matrix-core gate/up over an expert's rows: 16 or 32.  Default 32
+    // from B = 16: an expert with 17..32 slots is streamed once instead of twice (4096 / 1536
+    // layer, Zipf routing: B = 16 164 -> 156 us, B = 32 218 -> 198 us; Qwen-3 layer B = 24..64
+    // within 1%, where no expert has more than 16 slots); below, 16 (fewer registers; B = 8..12
+    // 1-2% faster)
+    if (c.slots_per_pass == 0) c.slots_per_pass = (!down && c.form == 3 && B >= 16) ? 32 : 16;
     if (c.slots_per_pass != 16 && c.slots_per_pass != 32) return WD_ERR_UNSUPPORTED;
     if (c.slots_per_pass == 32 && !(!down && c.form == 3)) return WD_ERR_UNSUPPORTED;
     // the expert split: the matrix-core down only, with scratch, not combined with token ranges

@@ -5,14 +5,14 @@
 // claims, section "How the two kernels work", and the Chinese summary's
 // 技术原理 section with its Gate/Up and Down kernel subsections.
 //
-// Token forms (the pages' design; the defaults below 24 tokens): each 64-lane
+// Token forms (the pages' design; the defaults for small batches): each 64-lane
 // wave owns output values for its whole life, streams the MXFP8 weight rows
 // it needs straight from HBM into registers, converts them as it reads them,
 // keeps a private FP32 accumulator and finishes with a cross-lane butterfly;
 // waves never exchange data, so there is no LDS traffic, no barrier and no
 // atomic.
 //
-// Expert forms on the matrix cores (the defaults from 24 tokens, where tokens
+// Expert forms on the matrix cores (the defaults from about 20 tokens, where tokens
 // share experts; a departure from the pages' design): gate/up takes one wave
 // per (expert, 16 intermediate rows) and down one workgroup per (16 output
 // dims, token range or class of experts); both stage weight tiles through LDS
