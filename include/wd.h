@@ -138,13 +138,16 @@ enum wd_status {
  *                    accumulation) and keeps each slot's 16 values in LDS;
  *                    each output then folds its token's router weights in,
  *                    one FMA per slot in expert order (rows_per_wave 1,
- *                    lanes_per_row 64, math 2, weight_loads 1; B <= 64;
- *                    B * K <= 512; E <= 1024).  Default: 3
- *                    when B <= 64, B * K <= 512, E <= 1024, none of
- *                    rows_per_wave, lanes_per_row, math, weight_loads,
- *                    waves_per_block is set and B >= 24 (B >= 8 when
- *                    K * I > 6144), else 1; with form 3 the default is
- *                    16 waves with several token ranges, else 8.
+ *                    lanes_per_row 64, math 2, weight_loads 1; B <= 128,
+ *                    B * K <= 1024, and with 16 waves B <= 64, B * K <=
+ *                    512; E <= 1024).  Default: 3 when B <= 128, B * K <=
+ *                    1024, E <= 1024, none of rows_per_wave,
+ *                    lanes_per_row, math, weight_loads, waves_per_block is
+ *                    set and B >= 24 (B >= 8 when K * I > 6144), else 1;
+ *                    with form 3 the default is the expert split (8 waves)
+ *                    when scratch is given and H / 16 < 256, else 16 waves
+ *                    with two token ranges when H / 16 < 256 and B <= 64,
+ *                    B * K <= 512, else 8 waves and one range.
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
  *                    streamed once and not kept in the caches)
  *   token_split      down, form 3 only: 1, 2 or 4 workgroups per block of 16
@@ -228,7 +231,7 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
  * form (the default below 24 tokens) one wave per (token b, output dims)
  * walks the K routed experts' rows, reduces across its 64 lanes with DPP row
  * operations and one lane read (no LDS) and writes out[b,h].  From B = 24
- * (B = 8 when K * I > 6144; up to 64 tokens and 512 slots) the default is
+ * (B = 8 when K * I > 6144; up to 128 tokens and 1,024 slots) the default is
  * the expert form on the matrix cores (wd_launch.form 3): one workgroup per
  * 16 output dims and token range reads each Wd row block once per range for
  * all the range's tokens routed to its expert, keeps each slot's products in

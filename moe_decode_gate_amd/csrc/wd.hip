@@ -70,7 +70,7 @@ int check_dims(int B, int K, int E, int H, int I) {
 //          at B = 8);
 //   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
 //   down, B 3..5: 4 rows per wave, FP32 math; B 6..55: 8 rows per wave;
-//   down, B 24..64 (B * K <= 512): the expert form on the matrix cores, one
+//   down, B 24..128 (B * K <= 1024): the expert form on the matrix cores, one
 //          16-wave workgroup per 16 outputs and token range, the batch cut in
 //          two ranges when H / 16 workgroups would leave CUs idle (equal at
 //          B = 24, 42 against 46 us at B = 28, 44 against 49 at B = 32, 58
@@ -93,8 +93,9 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     // is read once per expert however many tokens share it
     const bool untuned = c.rows_per_wave == 0 && c.lanes_per_row == 0 && c.math == 0 && c.weight_loads == 0;
     if (c.form == 0) {
-        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 24) && B <= wd::kDnMfmaMaxB &&
-                                     (long long)B * K <= wd::kDnMfmaMaxSlots && E <= wd::kDnMfmaMaxE
+        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 24) &&
+                                     B <= wd::kDnMfmaMaxBWide && (long long)B * K <= wd::kDnMfmaMaxSlotsWide &&
+                                     E <= wd::kDnMfmaMaxE
                                : untuned && (B >= 20 || (H >= 4096 && B >= 8));
         c.form = mfma ? 3 : 1;
     }
@@ -111,11 +112,14 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
         // instead (even / odd ids, all tokens each): every Wd row is read once, and each
         // workgroup streams about half the routed experts where a token range streams the
         // union of its tokens' experts, about two thirds of them at B = 32.
+        // past 64 tokens or 512 slots only the 8-wave variant with room for 1,024 slots applies
+        // (one token range unless asked for)
+        const bool big = B > wd::kDnMfmaMaxB || (long long)B * K > wd::kDnMfmaMaxSlots;
         const bool few_blocks = H / 16 < 256 && B >= 2;
         if (c.expert_split == 0)
             c.expert_split = (have_scratch && few_blocks && (c.token_split == 0 || c.token_split == 1)) ? 2 : 1;
-        if (c.token_split == 0) c.token_split = (few_blocks && c.expert_split == 1) ? 2 : 1;
-        if (c.waves_per_block == 0) c.waves_per_block = c.token_split > 1 ? 16 : 8;
+        if (c.token_split == 0) c.token_split = (few_blocks && c.expert_split == 1 && !big) ? 2 : 1;
+        if (c.waves_per_block == 0) c.waves_per_block = (c.token_split > 1 && !big) ? 16 : 8;
     }
     if (c.waves_per_block == 0)
         c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch || c.form == 4 ? 4 : 1);
@@ -383,14 +387,20 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
     if (c.form == 3) {
         // every slot's id held in registers (8 per lane), per-wave accumulators for 64 tokens,
         // expert ids packed in 10 bits
-        if (B > wd::kDnMfmaMaxB || (long long)B * K > wd::kDnMfmaMaxSlots || E > wd::kDnMfmaMaxE)
+        if (B > wd::kDnMfmaMaxBWide || (long long)B * K > wd::kDnMfmaMaxSlotsWide || E > wd::kDnMfmaMaxE)
             return WD_ERR_UNSUPPORTED;
+        // every wave keeps the ids of all B * K slots (of every range) in registers: past 64
+        // tokens or 512 slots only the 8-wave variant with room for 1,024 applies
+        const bool big = B > wd::kDnMfmaMaxB || (long long)B * K > wd::kDnMfmaMaxSlots;
+        if (big && c.waves_per_block != 8) return WD_ERR_UNSUPPORTED;
         // rows of a multiple of 8 E8M0 bytes: every batch's 8 bytes lie inside its row, one load
         const bool sc8 = (I / 32) % 8 == 0 && aligned(s_d, 4);
         // 8 waves: groups of 8 slots; 16 waves (register budget of four waves per SIMD): 4
+        constexpr int S = wd::kDnMfmaMaxSlots, SW = wd::kDnMfmaMaxSlotsWide;
         void (*fn)(LayerArgs) =
-            c.waves_per_block == 16 ? (sc8 ? wd::down_mfma_kernel<16, 4, true> : wd::down_mfma_kernel<16, 4, false>)
-                                    : (sc8 ? wd::down_mfma_kernel<8, 8, true> : wd::down_mfma_kernel<8, 8, false>);
+            c.waves_per_block == 16 ? (sc8 ? wd::down_mfma_kernel<16, 4, true, S> : wd::down_mfma_kernel<16, 4, false, S>)
+            : big                   ? (sc8 ? wd::down_mfma_kernel<8, 8, true, SW> : wd::down_mfma_kernel<8, 8, false, SW>)
+                                    : (sc8 ? wd::down_mfma_kernel<8, 8, true, S> : wd::down_mfma_kernel<8, 8, false, S>);
         if (B == 0) return WD_OK;
         if (!checked_device && (rc = check_device())) return rc;
         LayerArgs a{};

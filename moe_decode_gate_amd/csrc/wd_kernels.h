@@ -982,12 +982,15 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // S workgroups of a block sit on the same XCD.  This fills the CUs that H / 16
 // workgroups leave idle.
 // Limits: B <= 64, B * K <= 512 (the wave keeps every slot's id in registers,
-// 8 per lane, and each slot's 16 products in LDS), E <= 1024.
+// 8 per lane, and each slot's 16 products in LDS), E <= 1024; the 8-wave
+// variant with MAXS = 1,024 takes B <= 128, B * K <= 1,024 (16 ids per lane,
+// 64 KB of products; 159 KB of LDS in all).
 // ---------------------------------------------------------------------------
 constexpr int kDnMfmaMaxB = 64;
 constexpr int kDnMfmaMaxSlots = 512;
+constexpr int kDnMfmaMaxBWide = 128;                    // the 8-wave variant with room for 1,024 slots
+constexpr int kDnMfmaMaxSlotsWide = 1024;
 constexpr int kDnMfmaMaxE = 1024;
-constexpr int kDnIdRegs = kDnMfmaMaxSlots / 64;
 
 template <int G>
 struct DownSet {
@@ -1001,18 +1004,21 @@ struct DownCursor {    // position in a wave's task sequence
     int e, start, cnt; // that expert, its first entry in the wave's slot list, its slot count
 };
 
-template <int W, int G, bool SC8>
+template <int W, int G, bool SC8, int MAXS>
 __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
+    static_assert(MAXS == kDnMfmaMaxSlots || (MAXS == kDnMfmaMaxSlotsWide && W == 8), "slot capacity");
+    constexpr int kIdRegs = MAXS / 64;                 // slot ids per lane
+    constexpr int kMaxB = MAXS == kDnMfmaMaxSlots ? kDnMfmaMaxB : kDnMfmaMaxBWide;
     constexpr int kXRow = 33;                          // u32x4 per act row in LDS: 256 bf16 + 16 bytes of padding
     constexpr int kMaxExp = (kDnMfmaMaxE + W - 1) / W; // experts one wave can be given
     __shared__ u32x4 tile[W][16][16];                  // per wave: 16 rows x 256 bytes of codes, swizzled
     __shared__ u32x4 xtile[W][G][kXRow];               // per wave: the group's act for the batch
-    __shared__ f32x4 pv[kDnMfmaMaxSlots][4];           // per slot - sl0: P[0..15] of its expert's rows
-    __shared__ int16_t lslot[W][kDnMfmaMaxSlots];      // per wave: slots of its experts, expert by expert
+    __shared__ f32x4 pv[MAXS][4];           // per slot - sl0: P[0..15] of its expert's rows
+    __shared__ int16_t lslot[W][MAXS];      // per wave: slots of its experts, expert by expert
     __shared__ uint32_t lexp[W][kMaxExp];              // per wave: e | first entry << 10 | count << 20
-    __shared__ float lw[kDnMfmaMaxSlots];              // router weights of the workgroup's slots, by slot - sl0
-    __shared__ int16_t lord[kDnMfmaMaxSlots];          // per token of the range: its slots in fold order
-    __shared__ uint16_t lid[kDnMfmaMaxSlots];          // ids of the workgroup's slots, by slot - sl0 (E for bad ones)
+    __shared__ float lw[MAXS];              // router weights of the workgroup's slots, by slot - sl0
+    __shared__ int16_t lord[MAXS];          // per token of the range: its slots in fold order
+    __shared__ uint16_t lid[MAXS];          // ids of the workgroup's slots, by slot - sl0 (E for bad ones)
     __shared__ uint8_t lused[kDnMfmaMaxE];             // experts some slot of the range is routed to
     __shared__ uint8_t loth[kDnMfmaMaxE];              // experts some slot of another range is routed to
     const int lane = threadIdx.x & 63;
@@ -1036,9 +1042,9 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     const int nsb = (s_hi + kMfmaSteps - 1) / kMfmaSteps;   // batches per expert
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    int idv[kDnIdRegs];                                // id of slot 64 u + lane (-1: not this workgroup's)
+    int idv[kIdRegs];                                // id of slot 64 u + lane (-1: not this workgroup's)
 #pragma unroll
-    for (int u = 0; u < kDnIdRegs; ++u) {
+    for (int u = 0; u < kIdRegs; ++u) {
         const int sl = 64 * u + lane;
         idv[u] = sl >= sl0 && sl < sl1 ? a.ids[sl] : -1;
     }
@@ -1048,7 +1054,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // below compares its id with its token's other K - 1 ids: read from memory one after the
     // other, those were K dependent cache round trips ahead of the first weight load)
 #pragma unroll
-    for (int u = 0; u < kDnIdRegs; ++u) {
+    for (int u = 0; u < kIdRegs; ++u) {
         const int t = 64 * u + lane - sl0;             // idv[u] holds slot 64 u + lane
         if (t >= 0 && t < sl1 - sl0 && wv == 0)
             lid[t] = (uint16_t)((unsigned)idv[u] < (unsigned)E ? (unsigned)idv[u] : (unsigned)E);
@@ -1072,7 +1078,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         lord[tl * K + rank] = (int16_t)(k | (mine ? 0 : 0x4000));
     }
 #pragma unroll
-    for (int u = 0; u < kDnIdRegs; ++u)
+    for (int u = 0; u < kIdRegs; ++u)
         if ((unsigned)idv[u] < (unsigned)E && (idv[u] & (a.esplit - 1)) == part) lused[idv[u]] = 1;
     if (a.tsplit > 1) {
         const int BK = a.B * K;
@@ -1084,15 +1090,18 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __syncthreads();                                   // lused, loth, lw, lord complete
 
     // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
-    uint64_t bad_tok = 0;
+    uint64_t bad_tok[kMaxB / 64] = {};                 // bit b % 64 of word b / 64: token b
 #pragma unroll
-    for (int u = 0; u < kDnIdRegs; ++u) {
+    for (int u = 0; u < kIdRegs; ++u) {
         const int sl = 64 * u + lane;
         uint64_t m = __builtin_amdgcn_ballot_w64(sl >= sl0 && sl < sl1 && (unsigned)idv[u] >= (unsigned)E);
         while (m) {
             const int sl = 64 * u + (int)__builtin_ctzll(m);
             m &= m - 1;
-            bad_tok |= 1ull << (sl / a.K);
+            const int tok = sl / a.K;
+#pragma unroll
+            for (int wd = 0; wd < kMaxB / 64; ++wd)
+                if (tok >> 6 == wd) bad_tok[wd] |= 1ull << (tok & 63);
         }
     }
 
@@ -1118,7 +1127,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
                 mine &= mine - 1;
                 const int first = ns;
 #pragma unroll
-                for (int u = 0; u < kDnIdRegs; ++u) {
+                for (int u = 0; u < kIdRegs; ++u) {
                     const bool m = idv[u] == e;
                     const uint64_t bm = __builtin_amdgcn_ballot_w64(m);
                     const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
@@ -1298,7 +1307,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
 
     __syncthreads();
     // the fold: thread t owns output (token tb0 + t / 16, row t % 16) of the block
-    constexpr int kPer = (kDnMfmaMaxB * 16 + 64 * W - 1) / (64 * W);
+    constexpr int kPer = (kMaxB * 16 + 64 * W - 1) / (64 * W);
     const int nt = (tb1 - tb0) * 16;
     float yv[kPer];
 #pragma unroll
@@ -1313,7 +1322,11 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
                 const int sl = bl * K + o;
                 y = __builtin_fmaf(lw[sl], pv[sl][r >> 2][r & 3], y);
             }
-            if ((bad_tok >> (tb0 + bl)) & 1) y = __builtin_nanf("");
+            const int tok = tb0 + bl;
+            uint64_t bw = bad_tok[0];
+#pragma unroll
+            for (int wd = 1; wd < kMaxB / 64; ++wd) bw = tok >> 6 == wd ? bad_tok[wd] : bw;
+            if ((bw >> (tok & 63)) & 1) y = __builtin_nanf("");
         }
         yv[j] = y;
     }

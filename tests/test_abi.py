@@ -234,8 +234,12 @@ def test_matrix_core_form_limits():
     assert dnx(B=32, form=3, waves_per_block=16) == -5
     assert dnx(B=33, form=3, waves_per_block=16, token_split=1) == -5
     assert dnx(B=64, form=3, waves_per_block=16, token_split=1) == -5
-    assert dnx(B=65, form=3) == -7
-    assert dnx(B=40, K=16, form=3) == -7           # 640 slots
+    # past 64 tokens or 512 slots: the 8-wave variant with room for 128 tokens and 1,024 slots
+    assert dnx(B=65, form=3) == -5 and dnx(B=128, form=3) == -5 and dnx(B=40, K=16, form=3) == -5
+    assert dnx(B=128, form=3, token_split=2) == -5
+    assert dnx(B=65, form=3, waves_per_block=16) == -7 and dnx(B=40, K=16, form=3, waves_per_block=16) == -7
+    assert dnx(B=129, form=3) == -7
+    assert dnx(B=72, K=16, form=3) == -7           # 1,152 slots
     assert dnx(E=1025, K=8, form=3) == -7
     assert dnx(form=3, waves_per_block=4) == -7
     assert dnx(form=3, rows_per_wave=2) == -7

@@ -166,3 +166,72 @@ def test_expert_split_bad_ids():
     keep = [b for b in range(B) if b not in (3, 7)]
     assert np.array_equal(bad[keep], ok[keep])
     assert _counters_zero(scr, spec.H)
+
+
+WIDE = [
+    ("qwen3", gen.LayerSpec(E=128, K=8, H=2048, I=768, seed=130), 96, "softmax"),
+    ("qwen3", gen.LayerSpec(E=128, K=8, H=2048, I=768, seed=131), 128, "softmax"),
+    ("zipf16", gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=132), 100, "zipf"),
+    ("odd_h", gen.LayerSpec(E=24, K=6, H=800, I=256, seed=133), 80, "zipf"),
+]
+
+
+@pytest.mark.parametrize("name,spec,B,routing", WIDE, ids=[f"{c[0]}-B{c[2]}" for c in WIDE])
+def test_down_wide_variant(name, spec, B, routing):
+    """Past 64 tokens or 512 slots the matrix-core down runs its 8-wave variant
+    with room for 128 tokens and 1,024 slots: with the expert split (scratch),
+    with one token range and with two (no scratch); each held to the oracle's
+    down projection of the GPU's own intermediate; one and two ranges agree bit
+    for bit (a token's result depends on its own slots only), and a token
+    permutation permutes the outputs exactly."""
+    from moe_decode_gate_amd import binding as wd
+    L = gen.make_layer(spec, threads=16)
+    dl = DevLayer(L)
+    t = gen.make_tokens(spec, B, routing=routing)
+    t.ids[0, 1] = t.ids[0, 0]                         # a repeated expert
+    dt = DevTokens(t)
+    act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu)
+    torch.cuda.synchronize()
+    y64 = oracle.down(bits_of(act), t.ids, t.w, L.wd, L.sd, nthreads=16)
+    k = unit_shift(y64)
+    sd = shifted(dl.sd, k)
+    scr = wd.down_scratch(B, spec.H)
+    unit = 0.5 <= np.abs(y64 * 2.0 ** k).max() < 1.0
+    log(f"[wide down] {name} B={B}: slots {B * spec.K}, max slots per expert {np.bincount(t.ids.ravel()).max()}")
+    split = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, down_scratch=scr), sd)
+    one = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=1), sd)
+    two = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=2, waves_per_block=8), sd)
+    for got, what in ((split, "expert split"), (one, "one range"), (two, "two ranges")):
+        assert_output_parity(got, y64 * 2.0 ** k, f"wide down {name} B={B} {what}", unit_scale=unit)
+    assert np.array_equal(one, two)
+    assert _counters_zero(scr, spec.H)
+    perm = np.random.default_rng(B).permutation(B)
+    pt = torch.from_numpy(perm).cuda()
+    assert np.array_equal(_down(wd, act[pt].contiguous(), dt.ids[pt].contiguous(), dt.w[pt].contiguous(), dl,
+                                dict(form=3, down_scratch=scr), sd), split[perm])
+    # the layer entry point picks this variant by default
+    full = wd.moe_decode(dt.x, dt.ids, dt.w, dl.wgu, dl.sgu, dl.wd, sd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(full), split)
+
+
+def test_down_wide_variant_bad_ids():
+    """A bad id at B = 96: that token's outputs are NaN (tokens past 64 included),
+    the others keep their bits."""
+    from moe_decode_gate_amd import binding as wd
+    spec = gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=134)
+    dl = DevLayer(gen.make_layer(spec, threads=16))
+    B = 96
+    t = gen.make_tokens(spec, B)
+    dt = DevTokens(t)
+    act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu)
+    cfg = dict(form=3, down_scratch=wd.down_scratch(B, spec.H))
+    ok = _down(wd, act, dt.ids, dt.w, dl, cfg)
+    ids = dt.ids.clone()
+    ids[5, 1] = 16
+    ids[90, 3] = -2
+    bad = _down(wd, act, ids, dt.w, dl, cfg)
+    f = (bad & 0x7FFF) > 0x7F80
+    assert f[5].all() and f[90].all()
+    keep = [b for b in range(B) if b not in (5, 90)]
+    assert np.array_equal(bad[keep], ok[keep])
