@@ -48,6 +48,22 @@ int check_dims(int B, int K, int E, int H, int I) {
     return WD_OK;
 }
 
+// Token ranges the matrix-core down needs at least for B tokens of K slots: the smallest
+// S in {1, 2, 4} whose ranges of ceil(B / S) tokens fit the 1,024-slot variant (128 tokens,
+// 1,024 slots each); 0 when none does.
+int down_min_ranges(int B, int K) {
+    for (int S : {1, 2, 4}) {
+        const long long tpr = (B + S - 1) / S;
+        if (tpr <= wd::kDnMfmaMaxBWide && tpr * K <= wd::kDnMfmaMaxSlotsWide) return S;
+    }
+    return 0;
+}
+
+// A token range of tpr tokens needs the 1,024-slot variant (8 waves) past 64 tokens or 512 slots.
+bool down_big_range(int tpr, int K) {
+    return tpr > wd::kDnMfmaMaxB || (long long)tpr * K > wd::kDnMfmaMaxSlots;
+}
+
 // Resolve a launch configuration: fill unset fields with the defaults for
 // this batch size, then validate.  Defaults come from sweeps of every
 // configuration on MI355X at the 128-expert / top-8 / H 2048 / I 768 layer
@@ -70,7 +86,7 @@ int check_dims(int B, int K, int E, int H, int I) {
 //          at B = 8);
 //   down, B <= 2: one row per wave, BF16-pair dot products, non-temporal;
 //   down, B 3..5: 4 rows per wave, FP32 math; B 6..55: 8 rows per wave;
-//   down, B 24..128 (B * K <= 1024): the expert form on the matrix cores, one
+//   down, B 24..512 (B * K <= 4096): the expert form on the matrix cores, one
 //          16-wave workgroup per 16 outputs and token range, the batch cut in
 //          two ranges when H / 16 workgroups would leave CUs idle (equal at
 //          B = 24, 42 against 46 us at B = 28, 44 against 49 at B = 32, 58
@@ -94,8 +110,7 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     const bool untuned = c.rows_per_wave == 0 && c.lanes_per_row == 0 && c.math == 0 && c.weight_loads == 0;
     if (c.form == 0) {
         const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 24) &&
-                                     B <= wd::kDnMfmaMaxBWide && (long long)B * K <= wd::kDnMfmaMaxSlotsWide &&
-                                     E <= wd::kDnMfmaMaxE
+                                     down_min_ranges(B, K) > 0 && E <= wd::kDnMfmaMaxE
                                : untuned && (B >= 20 || (H >= 4096 && B >= 8));
         c.form = mfma ? 3 : 1;
     }
@@ -112,14 +127,21 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
         // instead (even / odd ids, all tokens each): every Wd row is read once, and each
         // workgroup streams about half the routed experts where a token range streams the
         // union of its tokens' experts, about two thirds of them at B = 32.
-        // past 64 tokens or 512 slots only the 8-wave variant with room for 1,024 slots applies
-        // (one token range unless asked for)
-        const bool big = B > wd::kDnMfmaMaxB || (long long)B * K > wd::kDnMfmaMaxSlots;
+        // A range past 64 tokens or 512 slots takes the 8-wave variant with room for 128 tokens
+        // and 1,024 slots; past 128 tokens or 1,024 slots the batch is cut into the fewest
+        // ranges of that size (each range streams the experts its tokens use; the ranges of a
+        // block sit on one XCD, so a second read of shared rows can come from the L2).
+        const int smin = down_min_ranges(B, K);
         const bool few_blocks = H / 16 < 256 && B >= 2;
         if (c.expert_split == 0)
-            c.expert_split = (have_scratch && few_blocks && (c.token_split == 0 || c.token_split == 1)) ? 2 : 1;
-        if (c.token_split == 0) c.token_split = (few_blocks && c.expert_split == 1 && !big) ? 2 : 1;
-        if (c.waves_per_block == 0) c.waves_per_block = (c.token_split > 1 && !big) ? 16 : 8;
+            c.expert_split = (have_scratch && few_blocks && smin == 1 && (c.token_split == 0 || c.token_split == 1))
+                                 ? 2 : 1;
+        if (c.token_split == 0)
+            c.token_split = smin > 1 ? smin
+                                     : (few_blocks && c.expert_split == 1 && !down_big_range(B, K)) ? 2 : 1;
+        if (c.waves_per_block == 0)
+            c.waves_per_block = (c.token_split > 1 && !down_big_range((B + c.token_split - 1) / c.token_split, K))
+                                    ? 16 : 8;
     }
     if (c.waves_per_block == 0)
         c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch || c.form == 4 ? 4 : 1);
@@ -387,11 +409,12 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
     if (c.form == 3) {
         // every slot's id held in registers (8 per lane), per-wave accumulators for 64 tokens,
         // expert ids packed in 10 bits
-        if (B > wd::kDnMfmaMaxBWide || (long long)B * K > wd::kDnMfmaMaxSlotsWide || E > wd::kDnMfmaMaxE)
+        // every wave keeps the ids of its token range's slots in registers: a range of up to 64
+        // tokens and 512 slots, or with the 8-wave 1,024-slot variant up to 128 and 1,024
+        const int tpr = (B + c.token_split - 1) / c.token_split;
+        if (tpr > wd::kDnMfmaMaxBWide || (long long)tpr * K > wd::kDnMfmaMaxSlotsWide || E > wd::kDnMfmaMaxE)
             return WD_ERR_UNSUPPORTED;
-        // every wave keeps the ids of all B * K slots (of every range) in registers: past 64
-        // tokens or 512 slots only the 8-wave variant with room for 1,024 applies
-        const bool big = B > wd::kDnMfmaMaxB || (long long)B * K > wd::kDnMfmaMaxSlots;
+        const bool big = down_big_range(tpr, K);
         if (big && c.waves_per_block != 8) return WD_ERR_UNSUPPORTED;
         // rows of a multiple of 8 E8M0 bytes: every batch's 8 bytes lie inside its row, one load
         const bool sc8 = (I / 32) % 8 == 0 && aligned(s_d, 4);

@@ -1042,11 +1042,11 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     const int nsb = (s_hi + kMfmaSteps - 1) / kMfmaSteps;   // batches per expert
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    int idv[kIdRegs];                                // id of slot 64 u + lane (-1: not this workgroup's)
+    int idv[kIdRegs];                                // id of slot sl0 + 64 u + lane (-1: past the range)
 #pragma unroll
     for (int u = 0; u < kIdRegs; ++u) {
-        const int sl = 64 * u + lane;
-        idv[u] = sl >= sl0 && sl < sl1 ? a.ids[sl] : -1;
+        const int sl = sl0 + 64 * u + lane;
+        idv[u] = sl < sl1 ? a.ids[sl] : -1;
     }
     for (int t = (int)threadIdx.x; t < E; t += 64 * W) lused[t] = loth[t] = 0;
     const int K = a.K;
@@ -1055,8 +1055,8 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // other, those were K dependent cache round trips ahead of the first weight load)
 #pragma unroll
     for (int u = 0; u < kIdRegs; ++u) {
-        const int t = 64 * u + lane - sl0;             // idv[u] holds slot 64 u + lane
-        if (t >= 0 && t < sl1 - sl0 && wv == 0)
+        const int t = 64 * u + lane;                   // idv[u] holds slot sl0 + 64 u + lane
+        if (t < sl1 - sl0 && wv == 0)
             lid[t] = (uint16_t)((unsigned)idv[u] < (unsigned)E ? (unsigned)idv[u] : (unsigned)E);
     }
     for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) lw[t] = a.tw[sl0 + t];
@@ -1090,15 +1090,15 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __syncthreads();                                   // lused, loth, lw, lord complete
 
     // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
-    uint64_t bad_tok[kMaxB / 64] = {};                 // bit b % 64 of word b / 64: token b
+    uint64_t bad_tok[kMaxB / 64] = {};                 // bit b % 64 of word b / 64: token tb0 + b
 #pragma unroll
     for (int u = 0; u < kIdRegs; ++u) {
-        const int sl = 64 * u + lane;
-        uint64_t m = __builtin_amdgcn_ballot_w64(sl >= sl0 && sl < sl1 && (unsigned)idv[u] >= (unsigned)E);
+        const int t = 64 * u + lane;                   // slot sl0 + t
+        uint64_t m = __builtin_amdgcn_ballot_w64(t < sl1 - sl0 && (unsigned)idv[u] >= (unsigned)E);
         while (m) {
-            const int sl = 64 * u + (int)__builtin_ctzll(m);
+            const int t = 64 * u + (int)__builtin_ctzll(m);
             m &= m - 1;
-            const int tok = sl / a.K;
+            const int tok = t / a.K;                   // sl0 is a multiple of K
 #pragma unroll
             for (int wd = 0; wd < kMaxB / 64; ++wd)
                 if (tok >> 6 == wd) bad_tok[wd] |= 1ull << (tok & 63);
@@ -1131,7 +1131,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
                     const bool m = idv[u] == e;
                     const uint64_t bm = __builtin_amdgcn_ballot_w64(m);
                     const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-                    if (m) lslot[wv][ns + rank] = (int16_t)(64 * u + lane);
+                    if (m) lslot[wv][ns + rank] = (int16_t)(sl0 + 64 * u + lane);
                     ns += __builtin_popcountll(bm);
                 }
                 if (lane == 0) lexp[wv][nx] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)(ns - first) << 20;
@@ -1322,7 +1322,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
                 const int sl = bl * K + o;
                 y = __builtin_fmaf(lw[sl], pv[sl][r >> 2][r & 3], y);
             }
-            const int tok = tb0 + bl;
+            const int tok = bl;                        // relative to tb0
             uint64_t bw = bad_tok[0];
 #pragma unroll
             for (int wd = 1; wd < kMaxB / 64; ++wd) bw = tok >> 6 == wd ? bad_tok[wd] : bw;

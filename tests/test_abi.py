@@ -238,8 +238,12 @@ def test_matrix_core_form_limits():
     assert dnx(B=65, form=3) == -5 and dnx(B=128, form=3) == -5 and dnx(B=40, K=16, form=3) == -5
     assert dnx(B=128, form=3, token_split=2) == -5
     assert dnx(B=65, form=3, waves_per_block=16) == -7 and dnx(B=40, K=16, form=3, waves_per_block=16) == -7
-    assert dnx(B=129, form=3) == -7
-    assert dnx(B=72, K=16, form=3) == -7           # 1,152 slots
+    # past 128 tokens or 1,024 slots: token ranges of up to 128 tokens and 1,024 slots each
+    assert dnx(B=129, form=3) == -5 and dnx(B=256, form=3) == -5 and dnx(B=512, form=3) == -5
+    assert dnx(B=72, K=16, form=3) == -5           # 1,152 slots: two ranges
+    assert dnx(B=129, form=3, token_split=1) == -7 and dnx(B=72, K=16, form=3, token_split=1) == -7
+    assert dnx(B=256, form=3, token_split=4) == -5 and dnx(B=256, form=3, token_split=2, waves_per_block=16) == -7
+    assert dnx(B=513, form=3) == -7 and dnx(B=512, form=3, token_split=2) == -7
     assert dnx(E=1025, K=8, form=3) == -7
     assert dnx(form=3, waves_per_block=4) == -7
     assert dnx(form=3, rows_per_wave=2) == -7

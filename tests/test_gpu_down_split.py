@@ -173,6 +173,8 @@ WIDE = [
     ("qwen3", gen.LayerSpec(E=128, K=8, H=2048, I=768, seed=131), 128, "softmax"),
     ("zipf16", gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=132), 100, "zipf"),
     ("odd_h", gen.LayerSpec(E=24, K=6, H=800, I=256, seed=133), 80, "zipf"),
+    ("qwen3", gen.LayerSpec(E=128, K=8, H=2048, I=768, seed=135), 256, "softmax"),
+    ("zipf16", gen.LayerSpec(E=16, K=4, H=1536, I=320, seed=136), 300, "zipf"),
 ]
 
 
@@ -180,8 +182,9 @@ WIDE = [
 def test_down_wide_variant(name, spec, B, routing):
     """Past 64 tokens or 512 slots the matrix-core down runs its 8-wave variant
     with room for 128 tokens and 1,024 slots: with the expert split (scratch),
-    with one token range and with two (no scratch); each held to the oracle's
-    down projection of the GPU's own intermediate; one and two ranges agree bit
+    with one token range and with two (no scratch); past 128 tokens or 1,024
+    slots in token ranges of at most that size.  Each held to the oracle's down
+    projection of the GPU's own intermediate; different range cuts agree bit
     for bit (a token's result depends on its own slots only), and a token
     permutation permutes the outputs exactly."""
     from moe_decode_gate_amd import binding as wd
@@ -198,10 +201,17 @@ def test_down_wide_variant(name, spec, B, routing):
     scr = wd.down_scratch(B, spec.H)
     unit = 0.5 <= np.abs(y64 * 2.0 ** k).max() < 1.0
     log(f"[wide down] {name} B={B}: slots {B * spec.K}, max slots per expert {np.bincount(t.ids.ravel()).max()}")
-    split = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, down_scratch=scr), sd)
-    one = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=1), sd)
-    two = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=2, waves_per_block=8), sd)
-    for got, what in ((split, "expert split"), (one, "one range"), (two, "two ranges")):
+    split = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, down_scratch=scr), sd)   # the default
+    if B <= 128:
+        one = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=1), sd)
+        two = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=2, waves_per_block=8), sd)
+        runs = ((split, "expert split"), (one, "one range"), (two, "two ranges"))
+    else:                                             # past 128 tokens: two (or four) ranges
+        one = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=4), sd)
+        two = _down(wd, act, dt.ids, dt.w, dl, dict(form=3, token_split=4, waves_per_block=8), sd)
+        runs = ((split, "default ranges"), (one, "four ranges"), (two, "four ranges, 8 waves"))
+        assert np.array_equal(split, one)             # a token's result: its own slots only
+    for got, what in runs:
         assert_output_parity(got, y64 * 2.0 ** k, f"wide down {name} B={B} {what}", unit_scale=unit)
     assert np.array_equal(one, two)
     assert _counters_zero(scr, spec.H)
