@@ -138,24 +138,31 @@ enum wd_status {
  *                    accumulation) and keeps each slot's 16 values in LDS;
  *                    each output then folds its token's router weights in,
  *                    one FMA per slot in expert order (rows_per_wave 1,
- *                    lanes_per_row 64, math 2, weight_loads 1; B <= 128,
- *                    B * K <= 1024, and with 16 waves B <= 64, B * K <=
- *                    512; E <= 1024).  Default: 3 when B <= 128, B * K <=
- *                    1024, E <= 1024, none of rows_per_wave,
+ *                    lanes_per_row 64, math 2, weight_loads 1; E <= 1024;
+ *                    each token range at most 128 tokens and 1,024 slots
+ *                    with 8 waves, 64 tokens and 512 slots with 16).
+ *                    Default: 3 when E <= 1024, none of rows_per_wave,
  *                    lanes_per_row, math, weight_loads, waves_per_block is
- *                    set and B >= 24 (B >= 8 when K * I > 6144), else 1;
- *                    with form 3 the default is the expert split (8 waves)
- *                    when scratch is given and H / 16 < 256, else 16 waves
- *                    with two token ranges when H / 16 < 256 and B <= 64,
- *                    B * K <= 512, else 8 waves and one range.
+ *                    set, B >= 24 (B >= 8 when K * I > 6144) and the batch
+ *                    fits 4 ranges (B <= 512, ceil(B / 4) * K <= 1024), else
+ *                    1.  With form 3 the defaults are: when one range holds
+ *                    the batch (B <= 128, B * K <= 1024), the expert split
+ *                    (8 waves) if scratch is given and H / 16 < 256, else two
+ *                    ranges of 16 waves if H / 16 < 256 and B <= 64, B * K <=
+ *                    512, else one range of 8 waves; a larger batch takes the
+ *                    fewest ranges (2 or 4) that hold it, 16 waves when each
+ *                    range has at most 64 tokens and 512 slots, else 8.
  *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
  *                    streamed once and not kept in the caches)
  *   token_split      down, form 3 only: 1, 2 or 4 workgroups per block of 16
  *                    output dims, each serving its own contiguous range of
  *                    ceil(B / token_split) tokens (an expert shared by
  *                    several ranges is read once per range; the output does
- *                    not depend on it bit for bit).  0 = default: 2 when
- *                    H / 16 < 256 (fewer blocks than the 256 CUs), else 1.
+ *                    not depend on it bit for bit).  0 = default: the fewest
+ *                    ranges that hold the batch when one does not, else 2
+ *                    when H / 16 < 256 (fewer blocks than the 256 CUs), the
+ *                    expert split is off and the batch has at most 64 tokens
+ *                    and 512 slots, else 1.
  *   lds_bytes        extra LDS per workgroup requested at launch (0..65536),
  *                    unused by the kernel: fewer workgroups then share a CU
  *                    (an occupancy knob for tuning)
@@ -231,7 +238,8 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
  * form (the default below 24 tokens) one wave per (token b, output dims)
  * walks the K routed experts' rows, reduces across its 64 lanes with DPP row
  * operations and one lane read (no LDS) and writes out[b,h].  From B = 24
- * (B = 8 when K * I > 6144; up to 128 tokens and 1,024 slots) the default is
+ * (B = 8 when K * I > 6144; up to 512 tokens in at most 4 ranges of 128
+ * tokens and 1,024 slots) the default is
  * the expert form on the matrix cores (wd_launch.form 3): one workgroup per
  * 16 output dims and token range reads each Wd row block once per range for
  * all the range's tokens routed to its expert, keeps each slot's products in

@@ -90,7 +90,10 @@ bool down_big_range(int tpr, int K) {
 //          16-wave workgroup per 16 outputs and token range, the batch cut in
 //          two ranges when H / 16 workgroups would leave CUs idle (equal at
 //          B = 24, 42 against 46 us at B = 28, 44 against 49 at B = 32, 58
-//          against 83 at B = 64; at B = 16 the token form wins, 32 against 32.3).
+//          against 83 at B = 64; at B = 16 the token form wins, 32 against 32.3);
+//          past 64 tokens one 8-wave workgroup per range of up to 128 tokens and
+//          1,024 slots, in 1, 2 or 4 ranges (B = 128 68 us, 256 102, 512 190,
+//          where the token form took 139, 246 and 443).
 // The token-form down keeps K * I / 1024 act chunks per lane in registers; past
 // 6 (K * I > 6144) its FP32-math variants need more than 200 VGPRs (one or two
 // waves per SIMD), so there it takes the BF16-pair math, 2 B rows per wave at

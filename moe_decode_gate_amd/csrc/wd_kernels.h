@@ -981,10 +981,11 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // once per range, from the L2 after the first: with H / 16 a multiple of 8 the
 // S workgroups of a block sit on the same XCD.  This fills the CUs that H / 16
 // workgroups leave idle.
-// Limits: B <= 64, B * K <= 512 (the wave keeps every slot's id in registers,
-// 8 per lane, and each slot's 16 products in LDS), E <= 1024; the 8-wave
-// variant with MAXS = 1,024 takes B <= 128, B * K <= 1,024 (16 ids per lane,
-// 64 KB of products; 159 KB of LDS in all).
+// Limits per token range: 64 tokens and 512 slots (the wave keeps every slot
+// id of its range in registers, 8 per lane, indexed from the range's first
+// slot, and each slot's 16 products in LDS); the 8-wave variant with
+// MAXS = 1,024 takes 128 tokens and 1,024 slots (16 ids per lane, 64 KB of
+// products; 159 KB of LDS in all).  E <= 1024.
 // ---------------------------------------------------------------------------
 constexpr int kDnMfmaMaxB = 64;
 constexpr int kDnMfmaMaxSlots = 512;
