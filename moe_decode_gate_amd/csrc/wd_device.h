@@ -244,6 +244,22 @@ __device__ __forceinline__ int wave_min(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: lane l gets v_0 + ... + v_l.
+// Within each row of 16 lanes, row_shr 1, 2, 4 and 8 (a lane whose source lies
+// before its row's start adds 0); across rows, row_bcast:15 adds the last lane
+// of row 0 into row 1 and of row 2 into row 3, then row_bcast:31 adds lane 31
+// (rows 0 and 1 in all) into rows 2 and 3.  Integer, so exact.  Must run with
+// all 64 lanes active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 // Sum over each group of LPR consecutive lanes (LPR = 16, 32 or 64), returned
 // to every lane of the group (bit-identical within a group).  The in-row
 // butterfly is the one of wave_sum; for 32-lane groups row_bcast:15 adds row

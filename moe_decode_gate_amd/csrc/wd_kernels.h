@@ -961,8 +961,12 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // order).  Each output is owned by one workgroup: no atomic, no buffer besides
 // the output.  Every Wd byte is read once per call.
 //
-// At the start each wave lists its routed experts and their slots (slot
-// order) in LDS.  Its work is then a sequence of tasks (expert, group of up to
+// At the start the workgroup copies its slots' ids and router weights to LDS,
+// counts the slots per expert (LDS atomics, one thread per slot) and computes
+// each slot's fold rank; every wave then finds its experts and the start of
+// each expert's run of slot entries (a wave prefix sum of the counts, 64
+// experts per step) and files its experts' slots into their runs.  A wave's
+// work is then a sequence of tasks (expert, group of up to
 // G slots, batch of 4 64-element steps).  The loads of a task (the 16 rows'
 // codes, coalesced as in the matrix-core gate/up; the rows' E8M0 bytes; the
 // group's act, coalesced, two slots per instruction) go to one of three
@@ -981,11 +985,10 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // once per range, from the L2 after the first: with H / 16 a multiple of 8 the
 // S workgroups of a block sit on the same XCD.  This fills the CUs that H / 16
 // workgroups leave idle.
-// Limits per token range: 64 tokens and 512 slots (the wave keeps every slot
-// id of its range in registers, 8 per lane, indexed from the range's first
-// slot, and each slot's 16 products in LDS); the 8-wave variant with
-// MAXS = 1,024 takes 128 tokens and 1,024 slots (16 ids per lane, 64 KB of
-// products; 159 KB of LDS in all).  E <= 1024.
+// Limits per token range: MAXS slots (each slot's 16 products, its id, router
+// weight, fold rank and run entry are kept in LDS) and MAXS / 8 tokens; 512
+// slots with 16 waves (147 KB of LDS), 512 or 1,024 with 8 (115 or 152 KB).
+// E <= 1024.
 // ---------------------------------------------------------------------------
 constexpr int kDnMfmaMaxB = 64;
 constexpr int kDnMfmaMaxSlots = 512;
@@ -1008,19 +1011,19 @@ struct DownCursor {    // position in a wave's task sequence
 template <int W, int G, bool SC8, int MAXS>
 __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     static_assert(MAXS == kDnMfmaMaxSlots || (MAXS == kDnMfmaMaxSlotsWide && W == 8), "slot capacity");
-    constexpr int kIdRegs = MAXS / 64;                 // slot ids per lane
     constexpr int kMaxB = MAXS == kDnMfmaMaxSlots ? kDnMfmaMaxB : kDnMfmaMaxBWide;
     constexpr int kXRow = 33;                          // u32x4 per act row in LDS: 256 bf16 + 16 bytes of padding
     constexpr int kMaxExp = (kDnMfmaMaxE + W - 1) / W; // experts one wave can be given
     __shared__ u32x4 tile[W][16][16];                  // per wave: 16 rows x 256 bytes of codes, swizzled
     __shared__ u32x4 xtile[W][G][kXRow];               // per wave: the group's act for the batch
     __shared__ f32x4 pv[MAXS][4];           // per slot - sl0: P[0..15] of its expert's rows
-    __shared__ int16_t lslot[W][MAXS];      // per wave: slots of its experts, expert by expert
+    __shared__ int16_t lslot[MAXS];         // slots of the workgroup's experts, one run per expert
     __shared__ uint32_t lexp[W][kMaxExp];              // per wave: e | first entry << 10 | count << 20
     __shared__ float lw[MAXS];              // router weights of the workgroup's slots, by slot - sl0
     __shared__ int16_t lord[MAXS];          // per token of the range: its slots in fold order
     __shared__ uint16_t lid[MAXS];          // ids of the workgroup's slots, by slot - sl0 (E for bad ones)
-    __shared__ uint8_t lused[kDnMfmaMaxE];             // experts some slot of the range is routed to
+    __shared__ uint32_t lcnt[kDnMfmaMaxE];             // slots of the range per expert it serves
+    __shared__ uint32_t lcur[kDnMfmaMaxE];             // owning wave << 16 | next free entry of its run
     __shared__ uint8_t loth[kDnMfmaMaxE];              // experts some slot of another range is routed to
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
@@ -1043,28 +1046,37 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     const int nsb = (s_hi + kMfmaSteps - 1) / kMfmaSteps;   // batches per expert
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    int idv[kIdRegs];                                // id of slot sl0 + 64 u + lane (-1: past the range)
-#pragma unroll
-    for (int u = 0; u < kIdRegs; ++u) {
-        const int sl = sl0 + 64 * u + lane;
-        idv[u] = sl < sl1 ? a.ids[sl] : -1;
-    }
-    for (int t = (int)threadIdx.x; t < E; t += 64 * W) lused[t] = loth[t] = 0;
+    const int nsl = sl1 - sl0;
     const int K = a.K;
-    // the slots' router weights and ids into LDS, every load issued at once (a slot's fold rank
-    // below compares its id with its token's other K - 1 ids: read from memory one after the
-    // other, those were K dependent cache round trips ahead of the first weight load)
-#pragma unroll
-    for (int u = 0; u < kIdRegs; ++u) {
-        const int t = 64 * u + lane;                   // idv[u] holds slot sl0 + 64 u + lane
-        if (t < sl1 - sl0 && wv == 0)
-            lid[t] = (uint16_t)((unsigned)idv[u] < (unsigned)E ? (unsigned)idv[u] : (unsigned)E);
+    for (int t = (int)threadIdx.x; t < E; t += 64 * W) {
+        lcnt[t] = 0;
+        lcur[t] = 0xFFFFFFFFu;
+        loth[t] = 0;
     }
-    for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) lw[t] = a.tw[sl0 + t];
-    __syncthreads();                                   // lused cleared and lid written
-    for (int t = (int)threadIdx.x; t < sl1 - sl0; t += 64 * W) {
+    // the range's ids and router weights into LDS, every load issued before the first is used
+    {
+        constexpr int kIt = (MAXS + 64 * W - 1) / (64 * W);
+        int idr[kIt];
+        float twr[kIt];
+#pragma unroll
+        for (int j = 0; j < kIt; ++j) {
+            const int t = (int)threadIdx.x + 64 * W * j;
+            idr[j] = t < nsl ? a.ids[sl0 + t] : 0;
+            twr[j] = t < nsl ? a.tw[sl0 + t] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kIt; ++j) {
+            const int t = (int)threadIdx.x + 64 * W * j;
+            if (t < nsl) {
+                lid[t] = (uint16_t)((unsigned)idr[j] < (unsigned)E ? (unsigned)idr[j] : (unsigned)E);
+                lw[t] = twr[j];
+            }
+        }
+    }
+    __syncthreads();                                   // lcnt, lcur, loth cleared; lid, lw written
+    for (int t = (int)threadIdx.x; t < nsl; t += 64 * W) {
         // fold order of the slot within its token: by expert, equal experts by slot (ids
-        // outside [0, E) last; such tokens are NaN anyway)
+        // outside [0, E) last)
         const int tl = t / K, k = t - tl * K;
         const uint16_t *tid = lid + tl * K;
         const unsigned ek = tid[k];
@@ -1074,13 +1086,13 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
             rank += e2 < ek || (e2 == ek && k2 < k);
         }
         // slots whose expert this workgroup does not serve (another class of the expert split, or
-        // an id outside [0, E)) are marked and skipped by the fold
-        const bool mine = ek < (unsigned)E && (int)(ek & (unsigned)(a.esplit - 1)) == part;
-        lord[tl * K + rank] = (int16_t)(k | (mine ? 0 : 0x4000));
+        // an id outside [0, E)) are marked and skipped by the fold; an id outside [0, E) also
+        // makes its token's outputs NaN
+        const bool valid = ek < (unsigned)E;
+        const bool mine = valid && (int)(ek & (unsigned)(a.esplit - 1)) == part;
+        lord[tl * K + rank] = (int16_t)(k | (mine ? 0 : 0x4000) | (valid ? 0 : 0x2000));
+        if (mine) atomicAdd(&lcnt[ek], 1u);            // the range's slots per expert
     }
-#pragma unroll
-    for (int u = 0; u < kIdRegs; ++u)
-        if ((unsigned)idv[u] < (unsigned)E && (idv[u] & (a.esplit - 1)) == part) lused[idv[u]] = 1;
     if (a.tsplit > 1) {
         const int BK = a.B * K;
         for (int t = (int)threadIdx.x; t < BK; t += 64 * W) {
@@ -1088,57 +1100,69 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
             if ((unsigned)id < (unsigned)E) loth[id] = 1;
         }
     }
-    __syncthreads();                                   // lused, loth, lw, lord complete
+    __syncthreads();                                   // lcnt, loth, lord complete
 
-    // tokens with an id outside [0, E) get NaN outputs (those slots match no expert)
-    uint64_t bad_tok[kMaxB / 64] = {};                 // bit b % 64 of word b / 64: token tb0 + b
-#pragma unroll
-    for (int u = 0; u < kIdRegs; ++u) {
-        const int t = 64 * u + lane;                   // slot sl0 + t
-        uint64_t m = __builtin_amdgcn_ballot_w64(t < sl1 - sl0 && (unsigned)idv[u] >= (unsigned)E);
-        while (m) {
-            const int t = 64 * u + (int)__builtin_ctzll(m);
-            m &= m - 1;
-            const int tok = t / a.K;                   // sl0 is a multiple of K
-#pragma unroll
-            for (int wd = 0; wd < kMaxB / 64; ++wd)
-                if (tok >> 6 == wd) bad_tok[wd] |= 1ull << (tok & 63);
-        }
-    }
-
-    // the wave's experts (routed experts n = wv, wv + W, ... in turn) and their slots, in
-    // expert then slot order.  Experts that other token ranges use as well come first, in
-    // expert order, then the rest: the workgroups of the other ranges of this output block
-    // stream the shared rows at about the same time, so the later reads find them in the
-    // L2.  (The order of experts changes no result: each slot's products are kept and
-    // folded per token in expert order at the end.)
+    // The routed experts this workgroup serves are dealt to the waves in turn (the n-th to wave
+    // n % W) in expert order, experts that other token ranges use as well first, then the rest:
+    // the workgroups of the other ranges of this output block stream the shared rows at about
+    // the same time, so the later reads find them in the L2.  Each expert owns a run of lslot
+    // entries, runs in dealing order; every wave computes all run starts (a prefix sum of the
+    // counts, 64 experts at a time) and keeps its own experts' (e, first entry, count) in lexp
+    // and its own in lcur (wave << 16 | first entry), then files its experts' slots into their
+    // runs.  (Neither the order of experts nor the order of slots within a run changes a
+    // result: each slot's products depend on its own act column only and are kept per slot,
+    // and the fold takes them per token in expert order.)
     int nx = 0;
     {
-        int ns = 0, seen = 0;
+        int gs = 0, seen = 0;                         // entries and experts dealt so far
         for (int pass = 0; pass < 2; ++pass)
-        for (int base = 0; base < E; base += 64) {
-            const bool used = base + lane < E && lused[base + lane] != 0 &&
-                              (loth[base + lane] != 0) == (pass == 0);
-            const uint64_t um = __builtin_amdgcn_ballot_w64(used);
-            const int n = seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
-            uint64_t mine = __builtin_amdgcn_ballot_w64(used && n % W == wv);
-            seen += __builtin_popcountll(um);
-            while (mine) {
-                const int e = base + (int)__builtin_ctzll(mine);
-                mine &= mine - 1;
-                const int first = ns;
-#pragma unroll
-                for (int u = 0; u < kIdRegs; ++u) {
-                    const bool m = idv[u] == e;
-                    const uint64_t bm = __builtin_amdgcn_ballot_w64(m);
-                    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-                    if (m) lslot[wv][ns + rank] = (int16_t)(sl0 + 64 * u + lane);
-                    ns += __builtin_popcountll(bm);
+            for (int base = 0; base < E && (pass == 1 || a.tsplit > 1); base += 64) {   // one range: no shared expert
+                const int e = base + lane;
+                const int c = e < E ? (int)lcnt[e] : 0;
+                const bool used = c > 0 && (loth[e < E ? e : 0] != 0) == (pass == 0);
+                const int cu = used ? c : 0;
+                const int first = gs + wave_incl_scan(cu) - cu;
+                const uint64_t um = __builtin_amdgcn_ballot_w64(used);
+                const int n = seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
+                const bool own = used && n % W == wv;
+                if (own) lcur[e] = (uint32_t)wv << 16 | (uint32_t)first;
+                uint64_t mine = __builtin_amdgcn_ballot_w64(own);
+                while (mine) {
+                    const int l = (int)__builtin_ctzll(mine);
+                    mine &= mine - 1;
+                    const uint32_t f = (uint32_t)__builtin_amdgcn_readlane(first, l);
+                    const uint32_t cn = (uint32_t)__builtin_amdgcn_readlane(cu, l);
+                    if (lane == 0) lexp[wv][nx] = (uint32_t)(base + l) | f << 10 | cn << 20;
+                    ++nx;
                 }
-                if (lane == 0) lexp[wv][nx] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)(ns - first) << 20;
-                ++nx;
+                seen += __builtin_popcountll(um);
+                gs = __builtin_amdgcn_readlane(first + cu, 63);   // entries of the experts dealt so far
             }
+    }
+    // this wave's slots into their experts' runs (lcur of another wave's expert reads either the
+    // cleared value or that wave's; neither names this wave).  With 8 waves (registers to spare)
+    // each step's LDS operations are issued for all of the range's slots before the next step
+    // waits for them.
+    if constexpr (W >= 16) {
+        for (int t = lane; t < nsl; t += 64) {
+            const unsigned e = lid[t];
+            if (e < (unsigned)E && lcur[e] >> 16 == (uint32_t)wv)
+                lslot[atomicAdd(&lcur[e], 1u) & 0xFFFFu] = (int16_t)(sl0 + t);
         }
+    } else {
+        constexpr int kC = MAXS / 64;
+        unsigned ev[kC];
+#pragma unroll
+        for (int j = 0; j < kC; ++j) ev[j] = 64 * j + lane < nsl ? (unsigned)lid[64 * j + lane] : (unsigned)E;
+        bool own[kC];
+#pragma unroll
+        for (int j = 0; j < kC; ++j) own[j] = ev[j] < (unsigned)E && lcur[ev[j] < (unsigned)E ? ev[j] : 0] >> 16 == (uint32_t)wv;
+        uint32_t pos[kC];
+#pragma unroll
+        for (int j = 0; j < kC; ++j) pos[j] = own[j] ? atomicAdd(&lcur[ev[j]], 1u) & 0xFFFFu : 0u;
+#pragma unroll
+        for (int j = 0; j < kC; ++j)
+            if (own[j]) lslot[pos[j]] = (int16_t)(sl0 + 64 * j + lane);
     }
 
     // ---- task sequence ----
@@ -1186,7 +1210,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
 #pragma unroll
             for (int j = 0; j < G / 2; ++j) {
                 const int col = 2 * j + (lane >> 5);
-                xo[j] = col < gn ? (int)lslot[wv][base + col] * I : 0;
+                xo[j] = col < gn ? (int)lslot[base + col] * I : 0;
             }
         }
         const int e = ld.e;
@@ -1228,7 +1252,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
             const int gn = min(G, cp.cnt - cp.grp * G);
             live = r16 < gn;
             // every lane reads a slot of the group (lanes past its end: the first)
-            slot = (int)lslot[wv][cp.start + cp.grp * G + (live ? r16 : 0)];
+            slot = (int)lslot[cp.start + cp.grp * G + (live ? r16 : 0)];
             c = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         // the task's data into the wave's LDS tiles (the wave's reads of the previous task are
@@ -1317,17 +1341,15 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         float y = 0.f;
         if (t < nt) {
             const int bl = t >> 4, r = t & 15;
+            bool bad = false;
             for (int i = 0; i < K; ++i) {              // the token's slots in fold order
                 const int o = lord[bl * K + i];
+                bad |= (o & 0x2000) != 0;              // an id outside [0, E)
                 if (o & 0x4000) continue;              // not one of this workgroup's experts
                 const int sl = bl * K + o;
                 y = __builtin_fmaf(lw[sl], pv[sl][r >> 2][r & 3], y);
             }
-            const int tok = bl;                        // relative to tb0
-            uint64_t bw = bad_tok[0];
-#pragma unroll
-            for (int wd = 1; wd < kMaxB / 64; ++wd) bw = tok >> 6 == wd ? bad_tok[wd] : bw;
-            if ((bw >> (tok & 63)) & 1) y = __builtin_nanf("");
+            if (bad) y = __builtin_nanf("");
         }
         yv[j] = y;
     }
