@@ -188,6 +188,14 @@ enum wd_status {
  *                    (two 16-slot tiles per weight batch; more registers, so
  *                    fewer resident waves).  Bit-identical results.  0 = default
  *                    (32 for form 3 from B = 16, else 16).
+ *   h_split          gate/up, form 3 only: 1 = one wave per (expert, 16 rows) streams
+ *                    the whole H axis; 2 = a workgroup of two waves per (expert, 16
+ *                    rows), each streaming half of the H axis, the second handing its
+ *                    FP32 sums to the first, which adds them (first half + second half)
+ *                    and writes the results: half as many weight batches per wave, so
+ *                    the last waves of a launch finish sooner.  Needs H a multiple of
+ *                    512; waves_per_block must be 0 or 2.  0 = default: 2 from
+ *                    H = 4096 (H a multiple of 512, waves_per_block 0 or 2), else 1.
  *   start_event,     optional hipEvent_t handles (created by the caller); when
  *   stop_event       set, the kernel's own dispatch records its start and end
  *                    time into them (hipExtLaunchKernelGGL), so the elapsed
@@ -210,6 +218,7 @@ typedef struct wd_launch {
     void *down_scratch;
     size_t down_scratch_bytes;
     int slots_per_pass;
+    int h_split;
 } wd_launch;
 
 /* Gate/up kernel (the summary's moe_gate_up_3d_batched; Key claims, section

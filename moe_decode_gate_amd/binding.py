@@ -48,7 +48,7 @@ class Launch(C.Structure):
                 ("lanes_per_row", C.c_int), ("form", C.c_int), ("weight_loads", C.c_int),
                 ("token_split", C.c_int), ("lds_bytes", C.c_int), ("expert_split", C.c_int),
                 ("down_scratch", C.c_void_p), ("down_scratch_bytes", C.c_size_t),
-                ("slots_per_pass", C.c_int)]
+                ("slots_per_pass", C.c_int), ("h_split", C.c_int)]
 
 
 class ECLaunch(C.Structure):

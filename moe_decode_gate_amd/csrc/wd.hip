@@ -146,6 +146,20 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
             c.waves_per_block = (c.token_split > 1 && !down_big_range((B + c.token_split - 1) / c.token_split, K))
                                     ? 16 : 8;
     }
+    // gate/up on the matrix cores: the H axis split over a pair of waves (needs whole 256-element
+    // batches in each half).  Default from H = 4096, where a wave's 16 or more weight batches made
+    // the last waves of a launch a long tail (128-expert / H 4096 / I 1536 layer, Zipf routing:
+    // B = 8 96 -> 85 us, B = 16 141 -> 125, B = 32 187 -> 171); at H = 2048 (8 batches per wave)
+    // the pair's fixed costs outweigh it (Qwen-3 layer: B = 32 70 -> 72 us, B = 64 77 -> 82)
+    if (c.h_split == 0)
+        c.h_split = (!down && c.form == 3 && H >= 4096 && H % 512 == 0 &&
+                     (c.waves_per_block == 0 || c.waves_per_block == 2)) ? 2 : 1;
+    if (c.h_split != 1 && c.h_split != 2) return WD_ERR_UNSUPPORTED;
+    if (c.h_split == 2) {
+        if (down || c.form != 3 || H % 512 != 0) return WD_ERR_UNSUPPORTED;
+        if (c.waves_per_block == 0) c.waves_per_block = 2;
+        if (c.waves_per_block != 2) return WD_ERR_UNSUPPORTED;
+    }
     if (c.waves_per_block == 0)
         c.waves_per_block = down ? (B == 1 ? 2 : 1) : (batch || c.form == 4 ? 4 : 1);
     // gate/up expert forms: expert-major order (consecutive waves stream consecutive row blocks
@@ -296,6 +310,16 @@ KernelFn down_fn(int cpl, int R, int tail, int math, int nt) {
     });
 }
 
+KernelFn gate_up_mfma_fn(bool sc8, int ngmax, int hs) {
+    return dispatch(sc8 ? 1 : 0, Ints<0, 1>{}, [&](auto S) {
+        return dispatch(ngmax, Ints<1, 2>{}, [&](auto N) {
+            return dispatch(hs, Ints<1, 2>{}, [&](auto Hs) -> KernelFn {
+                return wd::gate_up_mfma_kernel<S != 0, N, Hs>;
+            });
+        });
+    });
+}
+
 // Smallest compiled chunks-per-lane >= need.
 int round_cpl_gate_up(int need) {
     for (int c : {1, 2, 4, 8}) if (c >= need) return c;
@@ -341,9 +365,7 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     const bool sc8 = (H / 32) % 8 == 0 && aligned(s_gu, 4);
     KernelFn fn = c.form == 4   ? (c.waves_per_block == 2 ? wd::gate_up_mfma_lds_kernel<2>
                                                           : wd::gate_up_mfma_lds_kernel<4>)
-                  : c.form == 3 ? (c.slots_per_pass == 32
-                                       ? (sc8 ? wd::gate_up_mfma_kernel<true, 2> : wd::gate_up_mfma_kernel<false, 2>)
-                                       : (sc8 ? wd::gate_up_mfma_kernel<true, 1> : wd::gate_up_mfma_kernel<false, 1>))
+                  : c.form == 3 ? gate_up_mfma_fn(sc8, c.slots_per_pass == 32 ? 2 : 1, c.h_split)
                   : c.form == 2 ? gate_up_expert_fn(cpl, c.rows_per_wave, tail)
                                 : gate_up_fn(cpl, c.rows_per_wave, lpr, tail, c.math, c.weight_loads == 2);
     if (!fn) return WD_ERR_UNSUPPORTED;
@@ -353,7 +375,7 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     a.x = x; a.ids = ids; a.w = w_gu; a.s = s_gu; a.out = act;
     a.B = B; a.K = K; a.E = E; a.H = H; a.I = I;
     a.nrowblk = I / rows_per_wave;
-    a.nwaves = (c.form == 1 ? B * K : E) * a.nrowblk;
+    a.nwaves = (c.form == 1 ? B * K : E) * a.nrowblk * (c.form == 3 ? c.h_split : 1);
     a.order = c.order; a.remap = c.xcd_remap;
     a.zero_ptr = zero_ptr; a.zero_n = zero_ptr ? zero_n : 0;
     return launch(fn, a, c, (hipStream_t)stream);

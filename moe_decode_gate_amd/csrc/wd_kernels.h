@@ -389,17 +389,25 @@ struct MfmaBatch {                      // one wave's loads for kMfmaSteps 64-el
 };
 static_assert(kMfmaSteps == 4, "one 8-byte scale load and 256 bytes per row cover a batch");
 
-template <bool SC8, int NGMAX>
+template <bool SC8, int NGMAX, int HS>
 __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
+    static_assert(HS == 1 || HS == 2, "one wave per unit, or a pair splitting H");
+    constexpr int kWpb = HS == 2 ? 2 : 4;             // waves per workgroup
     zero_words(a);
     // per wave: the batch's 16 gate and 16 up rows x 256 bytes, 16-byte slots XOR-swizzled by row,
     // and each lane's E8M0 bytes of the batch (kept in LDS: a register copy of the prefetched
     // bytes would make the compute wait for the whole prefetch)
-    __shared__ u32x4 tile[4][2][16][16];
-    __shared__ uint64_t stile[4][2][64];
+    __shared__ u32x4 tile[kWpb][2][16][16];
+    __shared__ uint64_t stile[kWpb][2][64];
+    __shared__ f32x4 xch[HS == 2 ? NGMAX : 1][2][64];  // HS 2: the second wave's sums for the first
     const int lane = threadIdx.x & 63;
-    const int unit = logical_wave(a);
-    if (unit >= a.nwaves) return;
+    const int lw = logical_wave(a);
+    if (lw >= a.nwaves) return;                       // with HS 2, nwaves is even: pairs exit together
+    // HS 2: the two waves of a workgroup serve one unit, each over its half of the H axis (an
+    // equal number of whole 256-element batches); the second hands its FP32 sums to the first,
+    // which adds them to its own (first half + second half) and writes the results
+    const int unit = HS == 2 ? lw >> 1 : lw;
+    const int half = HS == 2 ? lw & 1 : 0;
     int e, jb;
     expert_unit(a, unit, e, jb);
     const int BK = a.B * a.K, H = a.H, I = a.I;
@@ -410,7 +418,8 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     const size_t grow = (size_t)e * 2 * I + (size_t)jb * 16 + r16;
     const uint8_t *sg = a.s + grow * nbr;
     const uint8_t *su = sg + (size_t)I * nbr;
-    const int s_lo = 0, s_hi = (H + 63) >> 6;        // 64-element steps
+    const int s_all = (H + 63) >> 6;                  // 64-element steps of a row
+    const int s_lo = half * (s_all / HS), s_hi = HS == 2 && half == 0 ? s_all / 2 : s_all;
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
     // Weight and scale loads are unconditional (offsets past H are clamped; the selects
@@ -452,7 +461,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     };
     MfmaBatch cur;
 
-    if (e == 0) {              // NaN rows for slots whose id is outside [0, E)
+    if (e == 0 && half == 0) {   // NaN rows for slots whose id is outside [0, E)
         for (int base = 0; base < BK; base += 64) {
             const int sl = base + lane;
             const int id = sl < BK ? a.ids[sl] : 0;
@@ -567,6 +576,20 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
                     cu[g] = mfma_bf16(u1, xb, cu[g]);
                 }
             }
+        }
+        if constexpr (HS == 2) {
+            // the pair's sums: the second wave's go through LDS, the first adds them to its own
+            if (half == 1) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g) { xch[g][0][lane] = cg[g]; xch[g][1][lane] = cu[g]; }
+            }
+            __syncthreads();
+            if (half == 0) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g) { cg[g] += xch[g][0][lane]; cu[g] += xch[g][1][lane]; }
+            }
+            __syncthreads();                          // xch free for the next pass
+            if (half == 1) return;
         }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {

@@ -223,6 +223,16 @@ def test_matrix_core_form_limits():
     assert gux(form=1, slots_per_pass=32) == -7 and gux(form=4, slots_per_pass=32) == -7
     assert lib.wd_down_ex(A, A, A, A, A, A, 32, 8, 128, 2048, 768, C.byref(wd.Launch(form=3, slots_per_pass=32)),
                           None) == -7
+    # the H axis split over a pair of waves: the register-staged matrix-core gate/up, H a multiple
+    # of 512, two waves per workgroup
+    assert gux(form=3, h_split=2) == -5 and gux(form=3, h_split=1) == -5
+    assert gux(form=3, h_split=2, waves_per_block=2) == -5
+    assert gux(form=3, h_split=2, waves_per_block=4) == -7 and gux(form=3, h_split=3) == -7
+    assert gux(form=1, h_split=2) == -7 and gux(form=4, h_split=2) == -7
+    assert lib.wd_gate_up_ex(A, A, A, A, A, 1, 8, 128, 1536 + 256, 768, C.byref(wd.Launch(form=3, h_split=2)),
+                             None) == -7
+    assert lib.wd_down_ex(A, A, A, A, A, A, 32, 8, 128, 2048, 768, C.byref(wd.Launch(form=3, h_split=2)),
+                          None) == -7
 
     # down on the matrix cores: 8 or 16 waves per workgroup, B <= 64, B * K <= 512, E <= 1024;
     # accepted configurations get as far as the device check (-5 here)

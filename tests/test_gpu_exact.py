@@ -293,25 +293,60 @@ def test_gate_up_lds_form_matches_register_form(H, B, routing):
     routing over 16 experts: up to ~70 slots on one expert at B = 100), a token
     that repeats an expert, and experts no slot uses; reruns are identical.
     Form 3 with 16 slots per pass over an expert's rows gives the same bits as
-    its default 32 (two 16-slot tiles per weight batch)."""
+    32 (two 16-slot tiles per weight batch).  Both without the H split, which
+    sums the two halves of H separately."""
     spec = gen.LayerSpec(E=16, K=4, H=H, I=320, seed=96 + H + B)
     L = gen.make_layer(spec, threads=16)
     dl = DevLayer(L)
     t = gen.make_tokens(spec, B, routing=routing)
     t.ids[0, 1] = t.ids[0, 0]
     dt = DevTokens(t)
-    a3, _ = run_layer(dl, dt, cfg_gu=dict(form=3))
+    a3, _ = run_layer(dl, dt, cfg_gu=dict(form=3, h_split=1))
     a4, _ = run_layer(dl, dt, cfg_gu=dict(form=4))
     log(f"[lds form] H={H} B={B}: max slots per expert {np.bincount(t.ids.ravel()).max()}")
     assert np.array_equal(bits_of(a4), bits_of(a3))
     a4b, _ = run_layer(dl, dt, cfg_gu=dict(form=4, waves_per_block=2))
     assert np.array_equal(bits_of(a4b), bits_of(a3))
-    a16, _ = run_layer(dl, dt, cfg_gu=dict(form=3, slots_per_pass=16))
+    a16, _ = run_layer(dl, dt, cfg_gu=dict(form=3, h_split=1, slots_per_pass=16))
     assert np.array_equal(bits_of(a16), bits_of(a3))
     if B <= 40:
         ref = oracle.gate_up(t.x, t.ids, L.wgu, L.sgu, nthreads=16)
         frac, ulps, within = act_flip_stats(bits_of(a4), ref)
         assert_act_flips(frac, ref.size, within, f"lds gate/up H={H} B={B}")
+
+
+@pytest.mark.parametrize("H,B,routing", [(512, 3, "zipf"), (1024, 24, "softmax"), (2048, 32, "softmax"),
+                                          (1536, 40, "zipf"), (4096, 8, "zipf"), (1536, 100, "zipf")])
+def test_gate_up_h_split(H, B, routing):
+    """The matrix-core gate/up with each (expert, 16 rows) served by a pair of
+    waves, one per half of the H axis (h_split 2): held to the oracle's
+    intermediate like the other forms; 16 and 32 slots per pass give the same
+    bits; reruns are identical; a token's values do not depend on the other
+    tokens (a reversed batch gives the reversed intermediate bit for bit); ids
+    outside [0, E) give NaN rows."""
+    spec = gen.LayerSpec(E=16, K=4, H=H, I=320, seed=196 + H + B)
+    L = gen.make_layer(spec, threads=16)
+    dl = DevLayer(L)
+    t = gen.make_tokens(spec, B, routing=routing)
+    t.ids[0, 1] = t.ids[0, 0]
+    dt = DevTokens(t)
+    a2, _ = run_layer(dl, dt, cfg_gu=dict(form=3, h_split=2))
+    log(f"[h split] H={H} B={B}: max slots per expert {np.bincount(t.ids.ravel()).max()}")
+    again, _ = run_layer(dl, dt, cfg_gu=dict(form=3, h_split=2))
+    assert np.array_equal(bits_of(again), bits_of(a2))
+    a16, _ = run_layer(dl, dt, cfg_gu=dict(form=3, h_split=2, slots_per_pass=16))
+    assert np.array_equal(bits_of(a16), bits_of(a2))
+    rev = gen.Tokens(x=t.x[::-1].copy(), ids=t.ids[::-1].copy(), w=t.w[::-1].copy())
+    ar, _ = run_layer(dl, DevTokens(rev), cfg_gu=dict(form=3, h_split=2))
+    assert np.array_equal(bits_of(ar)[::-1], bits_of(a2))
+    if B <= 40:
+        ref = oracle.gate_up(t.x, t.ids, L.wgu, L.sgu, nthreads=16)
+        frac, ulps, within = act_flip_stats(bits_of(a2), ref)
+        assert_act_flips(frac, ref.size, within, f"h-split gate/up H={H} B={B}")
+    ids = t.ids.copy(); ids[1, 2] = 16; ids[B - 1, 0] = -5
+    ab, _ = run_layer(dl, DevTokens(gen.Tokens(x=t.x, ids=ids, w=t.w)), cfg_gu=dict(form=3, h_split=2))
+    af = ab.float().cpu().numpy()
+    assert np.isnan(af[1, 2]).all() and np.isnan(af[B - 1, 0]).all()
 
 
 def test_gate_up_lds_form_bad_ids_and_default():
