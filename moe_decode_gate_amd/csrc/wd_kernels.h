@@ -1149,45 +1149,25 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
                 const int n = seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
                 const bool own = used && n % W == wv;
                 if (own) lcur[e] = (uint32_t)wv << 16 | (uint32_t)first;
-                uint64_t mine = __builtin_amdgcn_ballot_w64(own);
-                while (mine) {
-                    const int l = (int)__builtin_ctzll(mine);
-                    mine &= mine - 1;
-                    const uint32_t f = (uint32_t)__builtin_amdgcn_readlane(first, l);
-                    const uint32_t cn = (uint32_t)__builtin_amdgcn_readlane(cu, l);
-                    if (lane == 0) lexp[wv][nx] = (uint32_t)(base + l) | f << 10 | cn << 20;
-                    ++nx;
+                uint64_t om = __builtin_amdgcn_ballot_w64(own);
+                if constexpr (W < 16) {                // the wave's experts of the 64 in one masked store
+                    const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(om >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)om, 0u));
+                    if (own) lexp[wv][nx + r] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)cu << 20;
+                    nx += __builtin_popcountll(om);
+                } else {                               // one at a time (fewer registers)
+                    while (om) {
+                        const int l = (int)__builtin_ctzll(om);
+                        om &= om - 1;
+                        const uint32_t f = (uint32_t)__builtin_amdgcn_readlane(first, l);
+                        const uint32_t cn = (uint32_t)__builtin_amdgcn_readlane(cu, l);
+                        if (lane == 0) lexp[wv][nx] = (uint32_t)(base + l) | f << 10 | cn << 20;
+                        ++nx;
+                    }
                 }
                 seen += __builtin_popcountll(um);
                 gs = __builtin_amdgcn_readlane(first + cu, 63);   // entries of the experts dealt so far
             }
     }
-    // this wave's slots into their experts' runs (lcur of another wave's expert reads either the
-    // cleared value or that wave's; neither names this wave).  With 8 waves (registers to spare)
-    // each step's LDS operations are issued for all of the range's slots before the next step
-    // waits for them.
-    if constexpr (W >= 16) {
-        for (int t = lane; t < nsl; t += 64) {
-            const unsigned e = lid[t];
-            if (e < (unsigned)E && lcur[e] >> 16 == (uint32_t)wv)
-                lslot[atomicAdd(&lcur[e], 1u) & 0xFFFFu] = (int16_t)(sl0 + t);
-        }
-    } else {
-        constexpr int kC = MAXS / 64;
-        unsigned ev[kC];
-#pragma unroll
-        for (int j = 0; j < kC; ++j) ev[j] = 64 * j + lane < nsl ? (unsigned)lid[64 * j + lane] : (unsigned)E;
-        bool own[kC];
-#pragma unroll
-        for (int j = 0; j < kC; ++j) own[j] = ev[j] < (unsigned)E && lcur[ev[j] < (unsigned)E ? ev[j] : 0] >> 16 == (uint32_t)wv;
-        uint32_t pos[kC];
-#pragma unroll
-        for (int j = 0; j < kC; ++j) pos[j] = own[j] ? atomicAdd(&lcur[ev[j]], 1u) & 0xFFFFu : 0u;
-#pragma unroll
-        for (int j = 0; j < kC; ++j)
-            if (own[j]) lslot[pos[j]] = (int16_t)(sl0 + 64 * j + lane);
-    }
-
     // ---- task sequence ----
     auto fetch = [&](DownCursor &cu) {                 // the expert at list index x
         if (cu.x < nx) {
@@ -1226,16 +1206,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // used counts exactly the younger sets' loads.  Past the end of the sequence the cursor
     // keeps naming the last expert (and expert 0 for a wave with none), so the loads stay
     // in bounds; their data is never used.
-    auto issue = [&](DownSet<G> &st) {
-        if (ld.sb == 0) {                              // a new group: this lane's act rows
-            const int gn = min(G, ld.cnt - ld.grp * G);
-            const int base = ld.start + ld.grp * G;
-#pragma unroll
-            for (int j = 0; j < G / 2; ++j) {
-                const int col = 2 * j + (lane >> 5);
-                xo[j] = col < gn ? (int)lslot[base + col] * I : 0;
-            }
-        }
+    auto issue_w = [&](DownSet<G> &st) {              // the task's weight codes and E8M0 bytes
         const int e = ld.e;
         const int s0 = ld.sb * kMfmaSteps;
         const uint8_t *pw = a.w + ((size_t)e * H + (size_t)hb * 16) * (size_t)I + 64 * s0;
@@ -1253,11 +1224,29 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
 #pragma unroll
             for (int b = 0; b < 8; ++b) st.sc |= (uint64_t)ps[2 * s0 + b < nbr ? 2 * s0 + b : 0] << (8 * b);
         }
-        const int kx = 64 * s0 + 8 * (lane & 31);
+    };
+    auto rows_x = [&]() {                             // at a new group: this lane's act rows
+        if (ld.sb == 0) {
+            const int gn = min(G, ld.cnt - ld.grp * G);
+            const int base = ld.start + ld.grp * G;
+#pragma unroll
+            for (int j = 0; j < G / 2; ++j) {
+                const int col = 2 * j + (lane >> 5);
+                xo[j] = col < gn ? (int)lslot[base + col] * I : 0;
+            }
+        }
+    };
+    auto issue_x = [&](DownSet<G> &st) {              // the task's act, then the cursor moves on
+        const int kx = 64 * (ld.sb * kMfmaSteps) + 8 * (lane & 31);
         const int kxc = kx < I ? kx : 0;
 #pragma unroll
         for (int j = 0; j < G / 2; ++j) st.x[j] = ld16(a.act_in + xo[j] + kxc);
         advance(ld);
+    };
+    auto issue = [&](DownSet<G> &st) {
+        rows_x();
+        issue_w(st);
+        issue_x(st);
     };
 
     // ---- compute side ----
@@ -1344,7 +1333,41 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     };
 
     DownSet<G> sa, sb, sc;
-    issue(sa);
+    // with 8 waves the first task's weights are in flight while the wave files its slots (its act
+    // rows need them); with 16 (128 registers) the slots are filed first
+    if constexpr (W < 16) issue_w(sa);
+    // this wave's slots into their experts' runs (lcur of another wave's expert reads either the
+    // cleared value or that wave's; neither names this wave).  With 8 waves (registers to spare)
+    // each step's LDS operations are issued for all of the range's slots before the next step
+    // waits for them.
+    if constexpr (W >= 16) {
+        for (int t = lane; t < nsl; t += 64) {
+            const unsigned e = lid[t];
+            if (e < (unsigned)E && lcur[e] >> 16 == (uint32_t)wv)
+                lslot[atomicAdd(&lcur[e], 1u) & 0xFFFFu] = (int16_t)(sl0 + t);
+        }
+    } else {
+        constexpr int kC = MAXS / 64;
+        unsigned ev[kC];
+#pragma unroll
+        for (int j = 0; j < kC; ++j) ev[j] = 64 * j + lane < nsl ? (unsigned)lid[64 * j + lane] : (unsigned)E;
+        bool own[kC];
+#pragma unroll
+        for (int j = 0; j < kC; ++j) own[j] = ev[j] < (unsigned)E && lcur[ev[j] < (unsigned)E ? ev[j] : 0] >> 16 == (uint32_t)wv;
+        uint32_t pos[kC];
+#pragma unroll
+        for (int j = 0; j < kC; ++j) pos[j] = own[j] ? atomicAdd(&lcur[ev[j]], 1u) & 0xFFFFu : 0u;
+#pragma unroll
+        for (int j = 0; j < kC; ++j)
+            if (own[j]) lslot[pos[j]] = (int16_t)(sl0 + 64 * j + lane);
+    }
+
+    if constexpr (W < 16) {
+        rows_x();
+        issue_x(sa);
+    } else {
+        issue(sa);
+    }
     issue(sb);
     if constexpr (W < 16) issue(sc);
     while (cp.x < nx) {
