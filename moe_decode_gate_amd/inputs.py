@@ -24,6 +24,9 @@ experts were generated, and generation parallelises over experts.
 from __future__ import annotations
 
 import dataclasses
+import hashlib
+import json
+import os
 from concurrent.futures import ThreadPoolExecutor
 from typing import Optional, Sequence
 
@@ -34,6 +37,7 @@ __all__ = [
     "LayerSpec", "CONFIGS", "Layer", "Tokens",
     "quantize_mxfp8", "bf16_bits", "make_layer", "make_tokens",
     "layer_unique_bytes", "expert_bytes", "make_logits", "expert_weights_fp32",
+    "save_layer", "load_layer", "MANIFEST_FORMAT",
 ]
 
 BLOCK = 32          # MX block: elements sharing one E8M0 scale
@@ -222,3 +226,79 @@ def layer_unique_bytes(spec: LayerSpec, ids: np.ndarray) -> int:
     """Weight bytes a layer step must read at least once: every expert routed
     by at least one token, counted once."""
     return int(np.unique(np.asarray(ids)).size) * expert_bytes(spec)
+
+
+# ---- weight sets on disk ----------------------------------------------------
+
+MANIFEST_FORMAT = "moe-decode-mxfp8-layer/1"
+_ARRAYS = ("wgu", "sgu", "wd", "sd")
+
+
+def _sha256(path: str) -> str:
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        for chunk in iter(lambda: f.read(1 << 22), b""):
+            h.update(chunk)
+    return h.hexdigest()
+
+
+def save_layer(L: Layer, path: str, std: float = 0.02) -> dict:
+    """Write a layer's weight set to directory `path`: wgu/sgu/wd/sd as .npy files
+    (uint8 codes and E8M0 bytes, exactly the bits the kernels read) and
+    manifest.json holding the shape, the seed and the quantizer rule that
+    produced them, and each file's shape, dtype and SHA-256, so a run can be
+    reproduced from the files or regenerated from the manifest alone.  Returns
+    the manifest."""
+    os.makedirs(path, exist_ok=True)
+    arrays = {}
+    for name in _ARRAYS:
+        a = np.ascontiguousarray(getattr(L, name))
+        fn = name + ".npy"
+        np.save(os.path.join(path, fn), a, allow_pickle=False)
+        arrays[name] = {"file": fn, "shape": list(a.shape), "dtype": str(a.dtype),
+                        "sha256": _sha256(os.path.join(path, fn))}
+    sp = L.spec
+    man = {
+        "format": MANIFEST_FORMAT,
+        "spec": {"E": sp.E, "K": sp.K, "H": sp.H, "I": sp.I, "seed": sp.seed},
+        "experts": [int(e) for e in L.experts],
+        "std": std,
+        "generator": "per expert and tensor kind a numpy SeedSequence(seed, spawn_key=(kind, expert)) "
+                     "stream (kind 0: gate/up [2I, H], 1: down [H, I]), N(0, std) in float32; "
+                     "experts not listed are exact zeros (code 0, scale byte 127)",
+        "quantizer": {"block": BLOCK, "element": "OCP E4M3FN", "scale": "OCP E8M0, bias 127",
+                      "shared_exponent": "floor(log2(max|v| of the block)) - 8, byte clamped to [0, 254]; "
+                                         "an all-zero block gets byte 0",
+                      "elements": "v / 2^shared clamped to +-448, rounded to nearest E4M3FN, ties to even"},
+        "layout": {"wgu": "[E, 2I, H] rows [0, I) gate, [I, 2I) up", "sgu": "[E, 2I, H/32]",
+                   "wd": "[E, H, I]", "sd": "[E, H, I/32]"},
+        "arrays": arrays,
+    }
+    with open(os.path.join(path, "manifest.json"), "w") as f:
+        json.dump(man, f, indent=1, sort_keys=True)
+    return man
+
+
+def load_layer(path: str, verify: bool = True) -> Layer:
+    """Read a weight set written by save_layer.  Arrays are loaded without
+    unpickling (allow_pickle=False); their shapes and dtypes must match the
+    manifest and the layer shape it states, and with `verify` each file's
+    SHA-256 must match too.  Raises ValueError on any mismatch."""
+    with open(os.path.join(path, "manifest.json")) as f:
+        man = json.load(f)
+    if man.get("format") != MANIFEST_FORMAT:
+        raise ValueError(f"unknown weight-set format {man.get('format')!r}")
+    spec = LayerSpec(**man["spec"])
+    E, H, I = spec.E, spec.H, spec.I
+    want = {"wgu": (E, 2 * I, H), "sgu": (E, 2 * I, H // BLOCK), "wd": (E, H, I), "sd": (E, H, I // BLOCK)}
+    out = {}
+    for name in _ARRAYS:
+        ent = man["arrays"][name]
+        fn = os.path.join(path, ent["file"])
+        if verify and _sha256(fn) != ent["sha256"]:
+            raise ValueError(f"{ent['file']}: SHA-256 does not match the manifest")
+        a = np.load(fn, allow_pickle=False)
+        if a.dtype != np.uint8 or tuple(a.shape) != want[name] or list(a.shape) != ent["shape"]:
+            raise ValueError(f"{ent['file']}: {a.dtype} {a.shape}, the manifest's layer needs uint8 {want[name]}")
+        out[name] = a
+    return Layer(spec, out["wgu"], out["sgu"], out["wd"], out["sd"], tuple(man["experts"]))
