@@ -29,10 +29,14 @@
  *   act      [B, K, I]     BF16 intermediate SiLU(g) * u, rounded to nearest even
  *   out      [B, H]        BF16 output, rounded to nearest even from FP32
  *
- * Arithmetic: MXFP8 weights are converted to FP32 as they are read (the
- * conversion is exact), activations stay BF16 in memory, all products and sums
- * are FP32.  Summation order is fixed by the kernel's lane layout, so repeated
- * calls with the same inputs give bit-identical results.
+ * Arithmetic: MXFP8 weights are converted as they are read, to FP32 or to BF16
+ * (whichever the kernel multiplies in; exact for every normal value),
+ * activations stay BF16 in memory, all products and sums are FP32 (FMA, BF16
+ * pair dot products or the BF16 matrix cores).  The summation order is fixed
+ * by the kernel and its launch configuration, so repeated calls with the same
+ * inputs give bit-identical results; under one configuration a token's
+ * outputs do not depend on the other tokens' values or order (the defaults
+ * pick the configuration from the batch size, so they can change with it).
  *
  * Ownership: the caller owns every buffer (device memory) and the stream; the
  * compute entry points allocate, free and synchronise nothing, so they may be
@@ -230,10 +234,10 @@ typedef struct wd_launch {
  * (token, slot, block of rows) and reduces across its lanes: no LDS, no
  * barrier.  From there on the default is the expert form on the matrix cores
  * (wd_launch.form 3; form 4 is an equivalent variant): one wave per
- * (expert, 16 rows) reads each
- * weight row once for all slots routed to that expert, stages its codes in
- * its own LDS region and computes the same sums on v_mfma_f32_16x16x32_bf16
- * in another order. */
+ * (expert, 16 rows), from H = 4096 a pair of waves each over half of the H
+ * axis (wd_launch.h_split), reads each weight row once for all slots routed
+ * to that expert, stages its codes in its own LDS region and computes the
+ * same sums on v_mfma_f32_16x16x32_bf16 in another order. */
 int wd_gate_up(const uint16_t *x, const int32_t *topk_ids,
                const uint8_t *w_gu, const uint8_t *s_gu, uint16_t *act,
                int B, int K, int E, int H, int I, void *stream);
