@@ -129,7 +129,7 @@ enum wd_status {
  *                    ahead in registers; needs H a multiple of 256, s_gu
  *                    4-byte aligned, B * H * 2 <= 0x7FFF0000 and 2 or 4
  *                    waves per workgroup (default 4).
- *                    Default: 3 when B >= 20 (B >= 8 when H >= 4096) and
+ *                    Default: 3 when B >= 20 (B >= 4 when H >= 4096) and
  *                    none of rows_per_wave, lanes_per_row, math,
  *                    weight_loads is set, else 1.
  *                    down: 1 = one wave per (token, block of output dims);
@@ -147,7 +147,8 @@ enum wd_status {
  *                    with 8 waves, 64 tokens and 512 slots with 16).
  *                    Default: 3 when E <= 1024, none of rows_per_wave,
  *                    lanes_per_row, math, weight_loads, waves_per_block is
- *                    set, B >= 24 (B >= 8 when K * I > 6144) and the batch
+ *                    set, B >= 24 (B >= 13 with down_scratch; B >= 3 when
+ *                    K * I > 6144) and the batch
  *                    fits 4 ranges (B <= 512, ceil(B / 4) * K <= 1024), else
  *                    1.  With form 3 the defaults are: when one range holds
  *                    the batch (B <= 128, B * K <= 1024), the expert split
@@ -230,7 +231,7 @@ typedef struct wd_launch {
  * act[b,k,j] = BF16(SiLU(g) * u) with g, u the dot products of x[b] with gate
  * row j and up row I+j of expert e = topk_ids[b,k], MXFP8 converted exactly
  * as it is read, FP32 accumulation, x read once for both.  Below 20 tokens
- * (8 when H >= 4096; the default token form) one 64-lane wave serves each
+ * (4 when H >= 4096; the default token form) one 64-lane wave serves each
  * (token, slot, block of rows) and reduces across its lanes: no LDS, no
  * barrier.  From there on the default is the expert form on the matrix cores
  * (wd_launch.form 3; form 4 is an equivalent variant): one wave per
@@ -248,10 +249,12 @@ int wd_gate_up_ex(const uint16_t *x, const int32_t *topk_ids,
 /* Down kernel (moe_down_3d_batched; same sections; the Chinese summary's
  * "Down Kernel"): out[b,h] = BF16(sum_k topk_w[b,k] * Wd[e_k,h,:] . act[b,k,:])
  * with the router weight folded into the FP32 accumulator.  In the token
- * form (the default below 24 tokens) one wave per (token b, output dims)
+ * form (the default below 24 tokens, 13 with expert-split scratch, 3 when
+ * K * I > 6144) one wave per (token b, output dims)
  * walks the K routed experts' rows, reduces across its 64 lanes with DPP row
  * operations and one lane read (no LDS) and writes out[b,h].  From B = 24
- * (B = 8 when K * I > 6144; up to 512 tokens in at most 4 ranges of 128
+ * (B = 13 with expert-split scratch, B = 3 when K * I > 6144; up to 512
+ * tokens in at most 4 ranges of 128
  * tokens and 1,024 slots) the default is
  * the expert form on the matrix cores (wd_launch.form 3): one workgroup per
  * 16 output dims and token range reads each Wd row block once per range for

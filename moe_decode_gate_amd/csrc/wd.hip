@@ -73,13 +73,13 @@ bool down_big_range(int tpr, int K) {
 //   gate/up, B 5..23: 32 lanes per row, 4 rows per lane group (8 per wave),
 //          row-block-major order with XCD-contiguous numbering, so the tokens
 //          that share an expert row read it from the same L2 while resident;
-//   gate/up, B >= 20 (B >= 8 when H >= 4096): the expert form on the matrix
+//   gate/up, B >= 20 (B >= 4 when H >= 4096): the expert form on the matrix
 //          cores (one wave per expert row block, and none for an expert no slot
 //          uses; Qwen-3 layer 58.6 against 61.5 us at B = 20, 70 against 85 at
 //          B = 32, 75 against 136 at B = 64, the token form ahead at B = 16, 52.9
-//          against 55.0; on the 4096 / 1536 layer with Zipf routing 96.2 against
-//          98.3 us at B = 8, 121.7 against 138.8 at B = 12, the token form ahead at
-//          B = 4),
+//          against 55.0; on the 4096 / 1536 layer with Zipf routing, with the H
+//          split, 59.8 against 65.0 us at B = 4, 74.4 against 79.8 at B = 6, the
+//          token form ahead at B = 2, 33 against 40),
 //          register-staged (form 3; the form that
 //          streams its codes into LDS measured no faster: 70.9 against 71.7 us
 //          at B = 32, and slower on the 4096 / 1536 layer, 137 against 121 us
@@ -91,6 +91,9 @@ bool down_big_range(int tpr, int K) {
 //          two ranges when H / 16 workgroups would leave CUs idle (equal at
 //          B = 24, 42 against 46 us at B = 28, 44 against 49 at B = 32, 58
 //          against 83 at B = 64; at B = 16 the token form wins, 32 against 32.3);
+//          with scratch for the expert split from B = 13 (Qwen-3 layer, split
+//          against the token form: B = 13 27.8 against 30.0 us, B = 16 30.5
+//          against 32.0, B = 20 33.7 against 35.3; B = 12 26.7 against 23.2);
 //          past 64 tokens one 8-wave workgroup per range of up to 128 tokens and
 //          1,024 slots, in 1, 2 or 4 ranges (B = 128 68 us, 256 102, 512 190,
 //          where the token form took 139, 246 and 443).
@@ -98,8 +101,10 @@ bool down_big_range(int tpr, int K) {
 // 6 (K * I > 6144) its FP32-math variants need more than 200 VGPRs (one or two
 // waves per SIMD), so there it takes the BF16-pair math, 2 B rows per wave at
 // B <= 2 (the 128-expert / top-8 / H 4096 / I 1536 layer: 10.0 against 12.4 us
-// at B = 1, 16.1 against 17.5 at B = 2) and, from B = 8, the matrix-core form
-// (43 against 49 us at B = 8, where the FP32 math took 225 us).
+// at B = 1, 16.1 against 17.5 at B = 2) and, from B = 3, the matrix-core form
+// (26.5 against 30.7 us at B = 3, 35.0 against 44.9 at B = 5, 43 against 49 at
+// B = 8, where the FP32 math took 225 us; the token form ahead at B = 2, 16.5
+// against 21.0).
 // form4_ok: the gate/up kernel that streams codes into LDS applies (rows of a multiple of 256
 // elements, 4-byte-aligned scale bytes, x within one 2 GB buffer resource).
 // have_scratch: the down kernel was given scratch for its expert split.
@@ -112,9 +117,9 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     // is read once per expert however many tokens share it
     const bool untuned = c.rows_per_wave == 0 && c.lanes_per_row == 0 && c.math == 0 && c.weight_loads == 0;
     if (c.form == 0) {
-        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 8 : 24) &&
+        const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 3 : have_scratch ? 13 : 24) &&
                                      down_min_ranges(B, K) > 0 && E <= wd::kDnMfmaMaxE
-                               : untuned && (B >= 20 || (H >= 4096 && B >= 8));
+                               : untuned && (B >= 20 || (H >= 4096 && B >= 4));
         c.form = mfma ? 3 : 1;
     }
     if (c.form >= 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave
