@@ -1048,6 +1048,9 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __shared__ uint32_t lcnt[kDnMfmaMaxE];             // slots of the range per expert it serves
     __shared__ uint32_t lcur[kDnMfmaMaxE];             // owning wave << 16 | next free entry of its run
     __shared__ uint8_t loth[kDnMfmaMaxE];              // experts some slot of another range is routed to
+    __shared__ uint32_t lq[kDnMfmaMaxE];               // dynamic deal: e | first entry << 10 | count << 20, in deal order
+    __shared__ int lnext;                              // dynamic deal: the next expert to hand out
+    __shared__ int lheavy;                             // some expert holds more than 2 G of the range's slots
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
     const int hb = (int)blockIdx.x % a.nrowblk;
@@ -1075,6 +1078,10 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         lcnt[t] = 0;
         lcur[t] = 0xFFFFFFFFu;
         loth[t] = 0;
+    }
+    if (threadIdx.x == 0) {
+        lnext = W;                                     // experts 0 .. W-1 of the deal go to waves 0 .. W-1
+        lheavy = 0;
     }
     // the range's ids and router weights into LDS, every load issued before the first is used
     {
@@ -1114,7 +1121,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         const bool valid = ek < (unsigned)E;
         const bool mine = valid && (int)(ek & (unsigned)(a.esplit - 1)) == part;
         lord[tl * K + rank] = (int16_t)(k | (mine ? 0 : 0x4000) | (valid ? 0 : 0x2000));
-        if (mine) atomicAdd(&lcnt[ek], 1u);            // the range's slots per expert
+        if (mine && atomicAdd(&lcnt[ek], 1u) == 2u * G) lheavy = 1;   // the range's slots per expert
     }
     if (a.tsplit > 1) {
         const int BK = a.B * K;
@@ -1135,20 +1142,27 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // runs.  (Neither the order of experts nor the order of slots within a run changes a
     // result: each slot's products depend on its own act column only and are kept per slot,
     // and the fold takes them per token in expert order.)
-    int nx = 0;
+    // With one token range and an expert holding more than 2 G slots (three or more groups, so
+    // several times the work of the others), the deal is dynamic: experts with several groups
+    // first, then the rest, each wave taking the next one from a shared counter when it moves on,
+    // so waves given heavy experts take fewer.  (Which wave serves an expert changes no result.)
+    const bool dyn = W < 16 && a.tsplit == 1 && __builtin_amdgcn_readfirstlane(lheavy) != 0;   // 16 waves: static
+    int nx = 0, nused = 0;
     {
         int gs = 0, seen = 0;                         // entries and experts dealt so far
         for (int pass = 0; pass < 2; ++pass)
-            for (int base = 0; base < E && (pass == 1 || a.tsplit > 1); base += 64) {   // one range: no shared expert
+            for (int base = 0; base < E && (pass == 1 || a.tsplit > 1 || dyn); base += 64) {   // one range: no shared expert
                 const int e = base + lane;
                 const int c = e < E ? (int)lcnt[e] : 0;
-                const bool used = c > 0 && (loth[e < E ? e : 0] != 0) == (pass == 0);
+                const bool sel = dyn ? (c > G) == (pass == 0) : (loth[e < E ? e : 0] != 0) == (pass == 0);
+                const bool used = c > 0 && sel;
                 const int cu = used ? c : 0;
                 const int first = gs + wave_incl_scan(cu) - cu;
                 const uint64_t um = __builtin_amdgcn_ballot_w64(used);
                 const int n = seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
                 const bool own = used && n % W == wv;
                 if (own) lcur[e] = (uint32_t)wv << 16 | (uint32_t)first;
+                if (dyn && own) lq[n] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)cu << 20;
                 uint64_t om = __builtin_amdgcn_ballot_w64(own);
                 if constexpr (W < 16) {                // the wave's experts of the 64 in one masked store
                     const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(om >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)om, 0u));
@@ -1167,213 +1181,254 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
                 seen += __builtin_popcountll(um);
                 gs = __builtin_amdgcn_readlane(first + cu, 63);   // entries of the experts dealt so far
             }
+        nused = seen;
     }
-    // ---- task sequence ----
-    auto fetch = [&](DownCursor &cu) {                 // the expert at list index x
-        if (cu.x < nx) {
-            const uint32_t v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lexp[wv][cu.x]);
+    if (dyn) nx = INT_MAX;                             // known once the deal runs out
+    // The task sequence, compiled twice: with the static deal (each wave's list fixed by the scan)
+    // and with the dynamic one, so the loop of each carries only its own bookkeeping.
+    auto tasks = [&](auto dyn_c) {
+        constexpr bool D = decltype(dyn_c)::value;
+        // ---- task sequence ----
+        auto set_cursor = [&](DownCursor &cu, uint32_t v) {
             cu.e = (int)(v & 1023u);
             cu.start = (int)((v >> 10) & 1023u);
             cu.cnt = (int)(v >> 20);
-        }
-    };
-    auto advance = [&](DownCursor &cu) {
-        if (++cu.sb < nsb) return;
-        cu.sb = 0;
-        if (++cu.grp * G < cu.cnt) return;
-        cu.grp = 0;
-        ++cu.x;
-        fetch(cu);
-    };
+        };
+        // the compute side reads the wave's list; with the dynamic deal, a ring of the experts the
+        // load side (at most three tasks ahead) has taken
+        auto fetch = [&](DownCursor &cu) {                 // the expert at list index x
+            if (cu.x < nx) set_cursor(cu, (uint32_t)__builtin_amdgcn_readfirstlane((int)lexp[wv][D ? cu.x & 7 : cu.x]));
+        };
+        auto fetch_ld = [&](DownCursor &cu) {              // the load side: the static list, or the next expert dealt
+            if constexpr (!D) {
+                fetch(cu);
+            } else if (cu.x < nx) {
+                int n = wv;
+                if (cu.x > 0) {
+                    if (lane == 0) n = atomicAdd(&lnext, 1);
+                    n = __builtin_amdgcn_readfirstlane(n);
+                }
+                if (n < nused) {
+                    const uint32_t v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lq[n]);
+                    if (lane == 0) lexp[wv][cu.x & 7] = v;
+                    set_cursor(cu, v);
+                } else {
+                    nx = cu.x;                             // the deal ran out: the wave's last expert stays named
+                }
+            }
+        };
+        auto advance = [&](DownCursor &cu, bool load_side) {
+            if (++cu.sb < nsb) return;
+            cu.sb = 0;
+            if (++cu.grp * G < cu.cnt) return;
+            cu.grp = 0;
+            ++cu.x;
+            if (load_side)
+                fetch_ld(cu);
+            else
+                fetch(cu);
+        };
 
-    // per-lane offsets that do not change from task to task
-    int coff[4];                                       // code instruction j: row 4 j + l / 16, segment (l % 16) ^ row
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 4 * j + wrow;
-        coff[j] = r * I + 16 * (wslot ^ r);
-    }
-    const int soff = r16 * nbr;                        // the lane's row's E8M0 bytes
-
-    // ---- load side: three tasks ahead ----
-    DownCursor ld{0, 0, 0, 0, 0, 0};
-    fetch(ld);
-    DownCursor cp = ld;
-    int xo[G / 2];                                     // act row offset (elements) of instruction j for this lane
-#pragma unroll
-    for (int j = 0; j < G / 2; ++j) xo[j] = 0;
-    // Every call issues the same loads, in one straight block, so the wait before a set is
-    // used counts exactly the younger sets' loads.  Past the end of the sequence the cursor
-    // keeps naming the last expert (and expert 0 for a wave with none), so the loads stay
-    // in bounds; their data is never used.
-    auto issue_w = [&](DownSet<G> &st) {              // the task's weight codes and E8M0 bytes
-        const int e = ld.e;
-        const int s0 = ld.sb * kMfmaSteps;
-        const uint8_t *pw = a.w + ((size_t)e * H + (size_t)hb * 16) * (size_t)I + 64 * s0;
-        const int lim = I - 64 * s0;                   // bytes of each row left from this batch on
-#pragma unroll
+        // per-lane offsets that do not change from task to task
+        int coff[4];                                       // code instruction j: row 4 j + l / 16, segment (l % 16) ^ row
+    #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int seg = 16 * (wslot ^ (4 * j + wrow));
-            st.v[j] = ld16(pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0));   // past I: the row's start, zeroed when read
+            const int r = 4 * j + wrow;
+            coff[j] = r * I + 16 * (wslot ^ r);
         }
-        const uint8_t *ps = a.s + ((size_t)e * H + (size_t)hb * 16) * (size_t)nbr + soff;
-        if constexpr (SC8) {       // rows of a multiple of 8 E8M0 bytes (I % 256 == 0): one 8-byte load
-            st.sc = *reinterpret_cast<const uint64_t *>(ps + (2 * s0 + 8 <= nbr ? 2 * s0 : 0));
-        } else {
-            st.sc = 0;
-#pragma unroll
-            for (int b = 0; b < 8; ++b) st.sc |= (uint64_t)ps[2 * s0 + b < nbr ? 2 * s0 + b : 0] << (8 * b);
-        }
-    };
-    auto rows_x = [&]() {                             // at a new group: this lane's act rows
-        if (ld.sb == 0) {
-            const int gn = min(G, ld.cnt - ld.grp * G);
-            const int base = ld.start + ld.grp * G;
-#pragma unroll
-            for (int j = 0; j < G / 2; ++j) {
-                const int col = 2 * j + (lane >> 5);
-                xo[j] = col < gn ? (int)lslot[base + col] * I : 0;
-            }
-        }
-    };
-    auto issue_x = [&](DownSet<G> &st) {              // the task's act, then the cursor moves on
-        const int kx = 64 * (ld.sb * kMfmaSteps) + 8 * (lane & 31);
-        const int kxc = kx < I ? kx : 0;
-#pragma unroll
-        for (int j = 0; j < G / 2; ++j) st.x[j] = ld16(a.act_in + xo[j] + kxc);
-        advance(ld);
-    };
-    auto issue = [&](DownSet<G> &st) {
-        rows_x();
-        issue_w(st);
-        issue_x(st);
-    };
+        const int soff = r16 * nbr;                        // the lane's row's E8M0 bytes
 
-    // ---- compute side ----
-    int slot = 0;
-    bool live = false;
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    const int xr = r16 < G ? r16 : 0;
-    // One task: its data into the wave's LDS tiles, the set refilled with the task three
-    // ahead, then (for a real task) the 4 steps on the matrix cores and, at a group's last
-    // batch, the fold.  Past the end of the sequence only the first two run, so the loop
-    // below has no exit between its three calls and each set keeps its registers.
-    auto process = [&](DownSet<G> &st) {
-        const bool real = cp.x < nx;
-        if (real && cp.sb == 0) {
-            const int gn = min(G, cp.cnt - cp.grp * G);
-            live = r16 < gn;
-            // every lane reads a slot of the group (lanes past its end: the first)
-            slot = (int)lslot[cp.start + cp.grp * G + (live ? r16 : 0)];
-            c = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        // the task's data into the wave's LDS tiles (the wave's reads of the previous task are
-        // complete: LDS operations of one wave execute in order)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wt[4 * j + wrow][wslot] = st.v[j];
-#pragma unroll
-        for (int j = 0; j < G / 2; ++j) xt[2 * j + (lane >> 5)][lane & 31] = st.x[j];
-        const uint64_t scb = st.sc;
-        const int s0 = cp.sb * kMfmaSteps;
-        issue(st);                                     // refill the set with the task three ahead
-        if (!real) return;
-        // Columns past the group's slots hold stale act; each result column depends only
-        // on its own act column, and those columns are never folded.
-        if (s0 + kMfmaSteps <= s_full) {               // all 4 steps inside the row
-            // with registers to spare, every LDS read of the task first, so their latencies overlap
-            constexpr int kPre = W < 16 ? kMfmaSteps : 1;
-            u32x4 wqs[kPre], xas[kPre], xbs[kPre];
-            if constexpr (W < 16) {
-#pragma unroll
+        // ---- load side: three tasks ahead ----
+        DownCursor ld{0, 0, 0, 0, 0, 0};
+        fetch_ld(ld);
+        DownCursor cp = ld;
+        int xo[G / 2];                                     // act row offset (elements) of instruction j for this lane
+    #pragma unroll
+        for (int j = 0; j < G / 2; ++j) xo[j] = 0;
+        // Every call issues the same loads, in one straight block, so the wait before a set is
+        // used counts exactly the younger sets' loads.  Past the end of the sequence the cursor
+        // keeps naming the last expert (and expert 0 for a wave with none), so the loads stay
+        // in bounds; their data is never used.
+        auto issue_w = [&](DownSet<G> &st) {              // the task's weight codes and E8M0 bytes
+            const int e = ld.e;
+            const int s0 = ld.sb * kMfmaSteps;
+            const uint8_t *pw = a.w + ((size_t)e * H + (size_t)hb * 16) * (size_t)I + 64 * s0;
+            const int lim = I - 64 * s0;                   // bytes of each row left from this batch on
+    #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int seg = 16 * (wslot ^ (4 * j + wrow));
+                st.v[j] = ld16(pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0));   // past I: the row's start, zeroed when read
+            }
+            const uint8_t *ps = a.s + ((size_t)e * H + (size_t)hb * 16) * (size_t)nbr + soff;
+            if constexpr (SC8) {       // rows of a multiple of 8 E8M0 bytes (I % 256 == 0): one 8-byte load
+                st.sc = *reinterpret_cast<const uint64_t *>(ps + (2 * s0 + 8 <= nbr ? 2 * s0 : 0));
+            } else {
+                st.sc = 0;
+    #pragma unroll
+                for (int b = 0; b < 8; ++b) st.sc |= (uint64_t)ps[2 * s0 + b < nbr ? 2 * s0 + b : 0] << (8 * b);
+            }
+        };
+        auto rows_x = [&]() {                             // at a new group: this lane's act rows
+            if (ld.sb == 0) {
+                const int gn = min(G, ld.cnt - ld.grp * G);
+                const int base = ld.start + ld.grp * G;
+    #pragma unroll
+                for (int j = 0; j < G / 2; ++j) {
+                    const int col = 2 * j + (lane >> 5);
+                    xo[j] = col < gn ? (int)lslot[base + col] * I : 0;
+                }
+            }
+        };
+        auto issue_x = [&](DownSet<G> &st) {              // the task's act, then the cursor moves on
+            const int kx = 64 * (ld.sb * kMfmaSteps) + 8 * (lane & 31);
+            const int kxc = kx < I ? kx : 0;
+    #pragma unroll
+            for (int j = 0; j < G / 2; ++j) st.x[j] = ld16(a.act_in + xo[j] + kxc);
+            advance(ld, true);
+        };
+        auto issue = [&](DownSet<G> &st) {
+            rows_x();
+            issue_w(st);
+            issue_x(st);
+        };
+
+        // ---- compute side ----
+        int slot = 0;
+        bool live = false;
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        const int xr = r16 < G ? r16 : 0;
+        // One task: its data into the wave's LDS tiles, the set refilled with the task three
+        // ahead, then (for a real task) the 4 steps on the matrix cores and, at a group's last
+        // batch, the fold.  Past the end of the sequence only the first two run, so the loop
+        // below has no exit between its three calls and each set keeps its registers.
+        auto process = [&](DownSet<G> &st) {
+            const bool real = cp.x < nx;
+            if (real && cp.sb == 0) {
+                const int gn = min(G, cp.cnt - cp.grp * G);
+                live = r16 < gn;
+                // every lane reads a slot of the group (lanes past its end: the first)
+                slot = (int)lslot[cp.start + cp.grp * G + (live ? r16 : 0)];
+                c = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            // the task's data into the wave's LDS tiles (the wave's reads of the previous task are
+            // complete: LDS operations of one wave execute in order)
+    #pragma unroll
+            for (int j = 0; j < 4; ++j) wt[4 * j + wrow][wslot] = st.v[j];
+    #pragma unroll
+            for (int j = 0; j < G / 2; ++j) xt[2 * j + (lane >> 5)][lane & 31] = st.x[j];
+            const uint64_t scb = st.sc;
+            const int s0 = cp.sb * kMfmaSteps;
+            issue(st);                                     // refill the set with the task three ahead
+            if (!real) return;
+            // Columns past the group's slots hold stale act; each result column depends only
+            // on its own act column, and those columns are never folded.
+            if (s0 + kMfmaSteps <= s_full) {               // all 4 steps inside the row
+                // with registers to spare, every LDS read of the task first, so their latencies overlap
+                constexpr int kPre = W < 16 ? kMfmaSteps : 1;
+                u32x4 wqs[kPre], xas[kPre], xbs[kPre];
+                if constexpr (W < 16) {
+    #pragma unroll
+                    for (int i = 0; i < kMfmaSteps; ++i) {
+                        wqs[i] = wt[r16][(4 * i + q) ^ r16];
+                        xas[i] = xt[xr][8 * i + 2 * q];
+                        xbs[i] = xt[xr][8 * i + 2 * q + 1];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+    #pragma unroll
                 for (int i = 0; i < kMfmaSteps; ++i) {
-                    wqs[i] = wt[r16][(4 * i + q) ^ r16];
-                    xas[i] = xt[xr][8 * i + 2 * q];
-                    xbs[i] = xt[xr][8 * i + 2 * q + 1];
+                    const float f = e8m0_operand((uint32_t)(scb >> (8 * (2 * i + (q >> 1)))) & 0xFFu);
+                    const int ip = W < 16 ? i : 0;
+                    if constexpr (W >= 16) {
+                        wqs[0] = wt[r16][(4 * i + q) ^ r16];    // segment 4 i + q of row r16
+                        xas[0] = xt[xr][8 * i + 2 * q];         // elements 64 i + 16 q .. + 7
+                        xbs[0] = xt[xr][8 * i + 2 * q + 1];     // .. + 8 .. + 15
+                    }
+                    const u32x4 wq = wqs[ip], xa = xas[ip], xb = xbs[ip];
+                    uint32_t ww[8];
+    #pragma unroll
+                    for (int d = 0; d < 4; ++d) mx_word_bf16(wq[d], f, ww[2 * d], ww[2 * d + 1]);
+                    const u32x4 w0 = {ww[0], ww[1], ww[2], ww[3]}, w1 = {ww[4], ww[5], ww[6], ww[7]};
+                    c = mfma_bf16(w0, xa, c);
+                    c = mfma_bf16(w1, xb, c);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+            } else {
+    #pragma unroll
+                for (int i = 0; i < kMfmaSteps; ++i) {
+                    const int k = 64 * (s0 + i) + 16 * q;
+                    const bool ok = s0 + i < s_hi && k < I;
+                    const uint32_t bs = (uint32_t)(scb >> (8 * (2 * i + (q >> 1)))) & 0xFFu;
+                    const float f = e8m0_operand(ok ? bs : 127u);
+                    const u32x4 wq = ok ? wt[r16][(4 * i + q) ^ r16] : zero;
+                    const u32x4 xa = ok ? xt[xr][8 * i + 2 * q] : zero;
+                    const u32x4 xb = ok ? xt[xr][8 * i + 2 * q + 1] : zero;
+                    uint32_t ww[8];
+    #pragma unroll
+                    for (int d = 0; d < 4; ++d) mx_word_bf16(wq[d], f, ww[2 * d], ww[2 * d + 1]);
+                    const u32x4 w0 = {ww[0], ww[1], ww[2], ww[3]}, w1 = {ww[4], ww[5], ww[6], ww[7]};
+                    c = mfma_bf16(w0, xa, c);
+                    c = mfma_bf16(w1, xb, c);
+                }
             }
-#pragma unroll
-            for (int i = 0; i < kMfmaSteps; ++i) {
-                const float f = e8m0_operand((uint32_t)(scb >> (8 * (2 * i + (q >> 1)))) & 0xFFu);
-                const int ip = W < 16 ? i : 0;
-                if constexpr (W >= 16) {
-                    wqs[0] = wt[r16][(4 * i + q) ^ r16];    // segment 4 i + q of row r16
-                    xas[0] = xt[xr][8 * i + 2 * q];         // elements 64 i + 16 q .. + 7
-                    xbs[0] = xt[xr][8 * i + 2 * q + 1];     // .. + 8 .. + 15
-                }
-                const u32x4 wq = wqs[ip], xa = xas[ip], xb = xbs[ip];
-                uint32_t ww[8];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) mx_word_bf16(wq[d], f, ww[2 * d], ww[2 * d + 1]);
-                const u32x4 w0 = {ww[0], ww[1], ww[2], ww[3]}, w1 = {ww[4], ww[5], ww[6], ww[7]};
-                c = mfma_bf16(w0, xa, c);
-                c = mfma_bf16(w1, xb, c);
+            // lane (column r16, quad q) holds P[4 q + j][r16]: the slot's rows 4 q .. 4 q + 3
+            if (cp.sb == nsb - 1 && live) pv[slot - sl0][q] = c;
+            advance(cp, false);
+        };
+
+        DownSet<G> sa, sb, sc;
+        // with 8 waves the first task's weights are in flight while the wave files its slots (its act
+        // rows need them); with 16 (128 registers) the slots are filed first
+        if constexpr (W < 16) issue_w(sa);
+        // this wave's slots into their experts' runs (lcur of another wave's expert reads either the
+        // cleared value or that wave's; neither names this wave).  With 8 waves (registers to spare)
+        // each step's LDS operations are issued for all of the range's slots before the next step
+        // waits for them.
+        if constexpr (W >= 16) {
+            for (int t = lane; t < nsl; t += 64) {
+                const unsigned e = lid[t];
+                if (e < (unsigned)E && lcur[e] >> 16 == (uint32_t)wv)
+                    lslot[atomicAdd(&lcur[e], 1u) & 0xFFFFu] = (int16_t)(sl0 + t);
             }
         } else {
-#pragma unroll
-            for (int i = 0; i < kMfmaSteps; ++i) {
-                const int k = 64 * (s0 + i) + 16 * q;
-                const bool ok = s0 + i < s_hi && k < I;
-                const uint32_t bs = (uint32_t)(scb >> (8 * (2 * i + (q >> 1)))) & 0xFFu;
-                const float f = e8m0_operand(ok ? bs : 127u);
-                const u32x4 wq = ok ? wt[r16][(4 * i + q) ^ r16] : zero;
-                const u32x4 xa = ok ? xt[xr][8 * i + 2 * q] : zero;
-                const u32x4 xb = ok ? xt[xr][8 * i + 2 * q + 1] : zero;
-                uint32_t ww[8];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) mx_word_bf16(wq[d], f, ww[2 * d], ww[2 * d + 1]);
-                const u32x4 w0 = {ww[0], ww[1], ww[2], ww[3]}, w1 = {ww[4], ww[5], ww[6], ww[7]};
-                c = mfma_bf16(w0, xa, c);
-                c = mfma_bf16(w1, xb, c);
-            }
+            constexpr int kC = MAXS / 64;
+            unsigned ev[kC];
+    #pragma unroll
+            for (int j = 0; j < kC; ++j) ev[j] = 64 * j + lane < nsl ? (unsigned)lid[64 * j + lane] : (unsigned)E;
+            bool own[kC];
+    #pragma unroll
+            for (int j = 0; j < kC; ++j) own[j] = ev[j] < (unsigned)E && lcur[ev[j] < (unsigned)E ? ev[j] : 0] >> 16 == (uint32_t)wv;
+            uint32_t pos[kC];
+    #pragma unroll
+            for (int j = 0; j < kC; ++j) pos[j] = own[j] ? atomicAdd(&lcur[ev[j]], 1u) & 0xFFFFu : 0u;
+    #pragma unroll
+            for (int j = 0; j < kC; ++j)
+                if (own[j]) lslot[pos[j]] = (int16_t)(sl0 + 64 * j + lane);
         }
-        // lane (column r16, quad q) holds P[4 q + j][r16]: the slot's rows 4 q .. 4 q + 3
-        if (cp.sb == nsb - 1 && live) pv[slot - sl0][q] = c;
-        advance(cp);
+        // dynamic deal: every wave's runs filed and its deal entries written before any wave takes an
+        // expert another wave filed (workgroup-uniform condition)
+        if constexpr (D) __syncthreads();
+
+        if constexpr (W < 16) {
+            rows_x();
+            issue_x(sa);
+        } else {
+            issue(sa);
+        }
+        issue(sb);
+        if constexpr (W < 16) issue(sc);
+        while (cp.x < nx) {
+            process(sa);
+            process(sb);
+            if constexpr (W < 16) process(sc);     // 16 waves: two sets (register budget 128)
+        }
     };
-
-    DownSet<G> sa, sb, sc;
-    // with 8 waves the first task's weights are in flight while the wave files its slots (its act
-    // rows need them); with 16 (128 registers) the slots are filed first
-    if constexpr (W < 16) issue_w(sa);
-    // this wave's slots into their experts' runs (lcur of another wave's expert reads either the
-    // cleared value or that wave's; neither names this wave).  With 8 waves (registers to spare)
-    // each step's LDS operations are issued for all of the range's slots before the next step
-    // waits for them.
-    if constexpr (W >= 16) {
-        for (int t = lane; t < nsl; t += 64) {
-            const unsigned e = lid[t];
-            if (e < (unsigned)E && lcur[e] >> 16 == (uint32_t)wv)
-                lslot[atomicAdd(&lcur[e], 1u) & 0xFFFFu] = (int16_t)(sl0 + t);
-        }
-    } else {
-        constexpr int kC = MAXS / 64;
-        unsigned ev[kC];
-#pragma unroll
-        for (int j = 0; j < kC; ++j) ev[j] = 64 * j + lane < nsl ? (unsigned)lid[64 * j + lane] : (unsigned)E;
-        bool own[kC];
-#pragma unroll
-        for (int j = 0; j < kC; ++j) own[j] = ev[j] < (unsigned)E && lcur[ev[j] < (unsigned)E ? ev[j] : 0] >> 16 == (uint32_t)wv;
-        uint32_t pos[kC];
-#pragma unroll
-        for (int j = 0; j < kC; ++j) pos[j] = own[j] ? atomicAdd(&lcur[ev[j]], 1u) & 0xFFFFu : 0u;
-#pragma unroll
-        for (int j = 0; j < kC; ++j)
-            if (own[j]) lslot[pos[j]] = (int16_t)(sl0 + 64 * j + lane);
-    }
-
     if constexpr (W < 16) {
-        rows_x();
-        issue_x(sa);
+        if (dyn)
+            tasks(std::true_type{});
+        else
+            tasks(std::false_type{});
     } else {
-        issue(sa);
-    }
-    issue(sb);
-    if constexpr (W < 16) issue(sc);
-    while (cp.x < nx) {
-        process(sa);
-        process(sb);
-        if constexpr (W < 16) process(sc);     // 16 waves: two sets (register budget 128)
+        tasks(std::false_type{});
     }
 
     __syncthreads();
