@@ -970,7 +970,9 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 //
 // The experts that at least one slot is routed to are dealt to the waves in
 // turn (the n-th routed expert, in expert order, to wave n mod W), so every
-// wave gets the same number of experts to within one.  For each of its experts
+// wave gets the same number of experts to within one; when some expert holds
+// three or more groups of slots, waves instead take experts from a shared
+// counter, those experts first.  For each of its experts
 // a wave forms, G slots at a time (slot order), the tile
 // P[h][c] = sum_i Wd[e][h][i] * act[slot c][i] with v_mfma_f32_16x16x32_bf16
 // (weight codes converted exactly to BF16, act as stored, FP32 accumulation;
