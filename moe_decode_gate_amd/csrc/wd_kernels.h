@@ -968,11 +968,11 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // Down, expert form on the matrix cores: one workgroup of W waves per block of
 // 16 output dims h, serving every token of the batch.
 //
-// The experts that at least one slot is routed to are dealt to the waves in
-// turn (the n-th routed expert, in expert order, to wave n mod W), so every
-// wave gets the same number of experts to within one; when some expert holds
-// three or more groups of slots, waves instead take experts from a shared
-// counter, those experts first.  For each of its experts
+// The experts that at least one slot is routed to are handed to the waves
+// from a shared counter, experts with more than one group of slots first, so
+// a wave that drew a heavy expert takes fewer (with 16 waves, or several token
+// ranges, they are dealt in turn instead: the n-th routed expert to wave
+// n mod W).  For each of its experts
 // a wave forms, G slots at a time (slot order), the tile
 // P[h][c] = sum_i Wd[e][h][i] * act[slot c][i] with v_mfma_f32_16x16x32_bf16
 // (weight codes converted exactly to BF16, act as stored, FP32 accumulation;
@@ -1052,7 +1052,6 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __shared__ uint8_t loth[kDnMfmaMaxE];              // experts some slot of another range is routed to
     __shared__ uint32_t lq[kDnMfmaMaxE];               // dynamic deal: e | first entry << 10 | count << 20, in deal order
     __shared__ int lnext;                              // dynamic deal: the next expert to hand out
-    __shared__ int lheavy;                             // some expert holds more than 2 G of the range's slots
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
     const int hb = (int)blockIdx.x % a.nrowblk;
@@ -1083,7 +1082,6 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     }
     if (threadIdx.x == 0) {
         lnext = W;                                     // experts 0 .. W-1 of the deal go to waves 0 .. W-1
-        lheavy = 0;
     }
     // the range's ids and router weights into LDS, every load issued before the first is used
     {
@@ -1123,7 +1121,7 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         const bool valid = ek < (unsigned)E;
         const bool mine = valid && (int)(ek & (unsigned)(a.esplit - 1)) == part;
         lord[tl * K + rank] = (int16_t)(k | (mine ? 0 : 0x4000) | (valid ? 0 : 0x2000));
-        if (mine && atomicAdd(&lcnt[ek], 1u) == 2u * G) lheavy = 1;   // the range's slots per expert
+        if (mine) atomicAdd(&lcnt[ek], 1u);           // the range's slots per expert
     }
     if (a.tsplit > 1) {
         const int BK = a.B * K;
@@ -1144,11 +1142,12 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // runs.  (Neither the order of experts nor the order of slots within a run changes a
     // result: each slot's products depend on its own act column only and are kept per slot,
     // and the fold takes them per token in expert order.)
-    // With one token range and an expert holding more than 2 G slots (three or more groups, so
-    // several times the work of the others), the deal is dynamic: experts with several groups
+    // With 8 waves and one token range the deal is dynamic: experts with more than one group
     // first, then the rest, each wave taking the next one from a shared counter when it moves on,
-    // so waves given heavy experts take fewer.  (Which wave serves an expert changes no result.)
-    const bool dyn = W < 16 && a.tsplit == 1 && __builtin_amdgcn_readfirstlane(lheavy) != 0;   // 16 waves: static
+    // so a wave given a heavy expert takes fewer, and a wave that streams slower than the others
+    // (the memory system serves them unevenly) is not left with a fixed share.  (Which wave
+    // serves an expert changes no result.)
+    const bool dyn = W < 16 && a.tsplit == 1;   // 16 waves: static
     int nx = 0, nused = 0;
     {
         int gs = 0, seen = 0;                         // entries and experts dealt so far
