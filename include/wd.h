@@ -174,19 +174,21 @@ enum wd_status {
  *   expert_split     down, form 3 only: 2 = two workgroups per block of 16
  *                    output dims, one for the experts with even ids and one
  *                    for odd, all tokens each; each workgroup keeps its
- *                    class's partial sums in FP32, and the second of the two
- *                    to finish adds them (class 0 + class 1) and writes the
- *                    output, so every Wd row is read once.  Needs
+ *                    class's partial sums in FP32, the two hand them over
+ *                    through one scratch cell per output (an atomic
+ *                    exchange), and whichever comes second adds them (class
+ *                    0 + class 1) and writes the output, so every Wd row is
+ *                    read once.  Needs
  *                    down_scratch (not combined with token_split > 1).
  *                    1 = off.  0 = default: 2 when down_scratch is given and
  *                    the token ranges would otherwise be used (H / 16 < 256,
  *                    B >= 2), else 1.
  *   down_scratch,    down: device memory for the expert split, at least
  *   down_scratch_bytes  wd_down_scratch_bytes(B, H) bytes, 256-byte aligned:
- *                    one counter per block of 16 outputs, then the partial
- *                    sums.  Its first H / 16 * 4 bytes must be zero before
- *                    the first call; every call leaves them zero.  Calls that
- *                    overlap in time must not share it.
+ *                    one 8-byte cell per output.  The cells the call uses
+ *                    (the first wd_down_scratch_bytes(B, H) bytes) must be
+ *                    zero before the first call; every call leaves them
+ *                    zero.  Calls that overlap in time must not share it.
  *   slots_per_pass   gate/up, form 3 only: 16 = each pass over an expert's 16-row
  *                    block serves up to 16 of its slots (an expert with more
  *                    slots is streamed once per 16); 32 = up to 32 slots per pass
@@ -271,7 +273,7 @@ int wd_down_ex(const uint16_t *act, const int32_t *topk_ids, const float *topk_w
  * both on `stream`.  workspace_bytes must be >= wd_workspace_bytes(B, K, I).
  * With workspace_bytes >= wd_layer_workspace_bytes(B, K, H, I) (and the
  * workspace 256-byte aligned) the rest of the workspace serves the down
- * kernel's expert split (see wd_launch.expert_split); its counters are
+ * kernel's expert split (see wd_launch.expert_split); its cells are
  * cleared by this call's gate/up kernel, so the workspace needs no
  * preparation. */
 int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
@@ -312,8 +314,7 @@ int wd_route(const float *logits, int B, int E, int K, int32_t *topk_ids, float 
 size_t wd_workspace_bytes(int B, int K, int I);
 
 /* Bytes of the down kernel's expert-split scratch (wd_launch.down_scratch):
- * H / 16 counters padded to 256 bytes, then 2 * B * H FP32 partial sums;
- * 0 for invalid sizes. */
+ * one 8-byte cell per output, B * H * 8; 0 for invalid sizes. */
 size_t wd_down_scratch_bytes(int B, int H);
 
 /* Workspace of wd_moe_decode that also holds the expert-split scratch:

@@ -218,7 +218,7 @@ def layer_workspace_bytes(B: int, K: int, H: int, I: int) -> int:
 
 def down_scratch(B: int, H: int, device="cuda") -> torch.Tensor:
     """Zeroed scratch for the down kernel's expert split (wd_launch.down_scratch);
-    every call leaves its counters zero again, so it can be reused by calls in
+    every call leaves its cells zero again, so it can be reused by calls in
     stream order."""
     return torch.zeros(max(down_scratch_bytes(B, H), 256), dtype=torch.uint8, device=device)
 

@@ -350,7 +350,7 @@ int launch(KernelFn fn, LayerArgs a, const wd_launch &c, hipStream_t s) {
 
 int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, const uint8_t *s_gu,
                  uint16_t *act, int B, int K, int E, int H, int I, const wd_launch *cfg,
-                 void *stream, bool checked_device, int *zero_ptr = nullptr, int zero_n = 0) {
+                 void *stream, bool checked_device, void *zero_ptr = nullptr, int zero_n = 0) {
     int rc = check_dims(B, K, E, H, I);
     if (rc) return rc;
     if (!w_gu || !s_gu) return WD_ERR_NULL;
@@ -382,14 +382,13 @@ int gate_up_impl(const uint16_t *x, const int32_t *ids, const uint8_t *w_gu, con
     a.nrowblk = I / rows_per_wave;
     a.nwaves = (c.form == 1 ? B * K : E) * a.nrowblk * (c.form == 3 ? c.h_split : 1);
     a.order = c.order; a.remap = c.xcd_remap;
-    a.zero_ptr = zero_ptr; a.zero_n = zero_ptr ? zero_n : 0;
+    a.zero_ptr = static_cast<uint4 *>(zero_ptr); a.zero_n = zero_ptr ? zero_n : 0;
     return launch(fn, a, c, (hipStream_t)stream);
 }
 
-// Bytes of the down kernel's expert-split scratch: one counter per 16-output
-// block (padded to 256 bytes), then the partial outputs [2][H/16][B][16] FP32.
-size_t down_counter_bytes(int H) { return ((size_t)(H / 16) * 4 + 255) / 256 * 256; }
-size_t down_scratch_bytes(int B, int H) { return down_counter_bytes(H) + (size_t)2 * B * H * 4; }
+// Bytes of the down kernel's expert-split scratch: one 8-byte cell per output,
+// [H/16][B][16].
+size_t down_scratch_bytes(int B, int H) { return (size_t)B * H * 8; }
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const uint8_t *w_d,
@@ -398,8 +397,8 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
               void *scratch_in, size_t scratch_bytes_in);
 
 // Both kernels of one layer step on `stream`, act[B,K,I] at the start of `ws`; when `ws` also
-// holds the down kernel's expert-split scratch after it, the gate/up kernel clears that
-// scratch's counters first (the down kernel leaves them zero again).  Arguments already checked.
+// holds the down kernel's expert-split scratch after it, the gate/up kernel's workgroups clear
+// that scratch first (the down kernel leaves it zero again).  Arguments already checked.
 int layer(const uint16_t *x, const int32_t *ids, const float *tw, const uint8_t *w_gu, const uint8_t *s_gu,
           const uint8_t *w_d, const uint8_t *s_d, void *ws, size_t ws_bytes, uint16_t *out,
           int B, int K, int E, int H, int I, void *stream) {
@@ -407,13 +406,12 @@ int layer(const uint16_t *x, const int32_t *ids, const float *tw, const uint8_t 
     const size_t act_bytes = round256((size_t)B * K * I * 2u);
     uint8_t *scr = nullptr;
     size_t scr_bytes = 0;
-    int *counters = nullptr;
     if (ws_bytes >= act_bytes + down_scratch_bytes(B, H) && aligned(ws, 256)) {
         scr = static_cast<uint8_t *>(ws) + act_bytes;
         scr_bytes = ws_bytes - act_bytes;
-        counters = reinterpret_cast<int *>(scr);
     }
-    int rc = gate_up_impl(x, ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, true, counters, H / 16);
+    int rc = gate_up_impl(x, ids, w_gu, s_gu, act, B, K, E, H, I, nullptr, stream, true, scr,
+                          (int)(down_scratch_bytes(B, H) / 16));
     if (rc) return rc;
     return down_impl(act, ids, tw, w_d, s_d, out, B, K, E, H, I, nullptr, stream, true, scr, scr_bytes);
 }
@@ -462,10 +460,7 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         a.nrowblk = H / 16;
         a.tsplit = c.token_split;
         a.esplit = c.expert_split;
-        if (c.expert_split > 1) {
-            a.dcount = static_cast<int *>(scr);
-            a.dpart = reinterpret_cast<float *>(static_cast<uint8_t *>(scr) + down_counter_bytes(H));
-        }
+        if (c.expert_split > 1) a.dcell = static_cast<uint64_t *>(scr);
         const int blocks = a.nrowblk * c.token_split * c.expert_split;
         a.nwaves = blocks * c.waves_per_block;
         a.nblocks = blocks;
@@ -618,7 +613,7 @@ int wd_moe_decode_noalloc(const uint16_t *x, const int32_t *topk_ids, const floa
     void *ws = scratch_ptr();
     if (!ws) return WD_ERR_DEVICE;
     // act at the start; the down kernel's expert-split scratch after it when it fits (its
-    // counters cleared by the gate/up kernel); gate/up writes every act element the down kernel
+    // cells cleared by the gate/up kernel); gate/up writes every act element the down kernel
     // reads, so nothing else is cleared
     return layer(x, topk_ids, topk_w, w_gu, s_gu, w_d, s_d, ws, (size_t)WD_NOALLOC_SCRATCH_BYTES, out,
                  B, K, E, H, I, stream);

@@ -19,9 +19,9 @@
 // (their own wave's region, or with the down kernel's workgroup barrier the
 // per-slot products), and compute the same FP32 sums of exact products on
 // v_mfma_f32_16x16x32_bf16 in another order.  Gate/up keeps no atomic and no
-// buffer besides the intermediate; the down kernel's expert split adds one
-// counter per 16-output block and a scratch of FP32 partial sums, which the
-// second of the block's two workgroups adds in a fixed order.
+// buffer besides the intermediate; the down kernel's expert split adds a
+// scratch cell per output, through which the two workgroups of a block hand
+// over their FP32 partial sums (one atomic exchange per output).
 #pragma once
 
 #include <type_traits>
@@ -49,19 +49,21 @@ struct LayerArgs {
     int nblocks;             // workgroups in the grid
     int wpb;                 // waves per workgroup
     int esplit;              // down, matrix-core form: workgroups per 16-output block, each for one class of experts
-    float *dpart;            // down, expert split: partial outputs [esplit][H/16][B][16] (FP32)
-    int *dcount;             // down, expert split: per 16-output block, how many of its workgroups finished
-    int *zero_ptr;           // gate/up: words the first workgroup sets to zero before anything else (or null)
+    uint64_t *dcell;         // down, expert split: one cell per output [H/16][B][16], zero between calls
+    uint4 *zero_ptr;         // gate/up: 16-byte words the workgroups set to zero first (or null)
     int zero_n;
 };
 
-// The first workgroup clears zero_n words at zero_ptr (the down kernel's
-// per-block counters of the expert split, when both kernels run as one layer:
+// The workgroups clear zero_n 16-byte words at zero_ptr, each its own share
+// (the down kernel's expert-split cells, when both kernels run as one layer:
 // the down kernel, launched after this one on the same stream, finds them
 // zero).
 __device__ __forceinline__ void zero_words(const LayerArgs &a) {
-    if (a.zero_n > 0 && blockIdx.x == 0)
-        for (int i = (int)threadIdx.x; i < a.zero_n; i += 64 * a.wpb) a.zero_ptr[i] = 0;
+    if (a.zero_n > 0) {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < a.zero_n; i += a.nblocks * (int)blockDim.x)
+            a.zero_ptr[i] = z;
+    }
 }
 
 // Makes the compiler load the kernel arguments a wave needs first in one
@@ -1476,39 +1478,26 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
         }
         return;
     }
-    // Expert split (two workgroups per block, all tokens each): this class's sums go to the
-    // scratch; the second of the two workgroups to finish -- found with one counter per block,
-    // nobody waits -- adds the other's in class order, part 0 + part 1, and writes the output,
-    // then clears the counter for the next call.  A token's result still depends on its own
-    // slots only.  The two workgroups may sit on different XCDs: the partial sums go through
-    // the coherence point (agent-scope stores, written through; agent-scope loads), the
-    // counter is a plain atomic, and no cache is written back or invalidated (an
-    // acquire-release atomic would write back the XCD's L2 in every workgroup).
-    float *mine = a.dpart + ((size_t)part * a.nrowblk + hb) * ((size_t)a.B * 16);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int t = (int)threadIdx.x + 64 * W * j;
-        if (t < nt) __hip_atomic_store(mine + t, yv[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __shared__ int lsecond;
-    wait_vmcnt<0>();                                   // this wave's sums have reached the coherence point
-    __syncthreads();                                   // ... and every wave's
-    if (threadIdx.x == 0) {
-        const int prev = __hip_atomic_fetch_add(a.dcount + hb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lsecond = prev == 1;
-        if (prev == 1) __hip_atomic_store(a.dcount + hb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!lsecond) return;
-    // issued after the counter said the other workgroup had added (its sums complete before)
-    const float *other = a.dpart + ((size_t)(1 - part) * a.nrowblk + hb) * ((size_t)a.B * 16);
+    // Expert split (two workgroups per block, all tokens each): each output's two partial sums
+    // meet in its scratch cell.  A thread swaps its sum, tagged, into the cell with one atomic
+    // exchange; whichever of the two comes second gets the other's sum back, adds them in class
+    // order (part 0 + part 1), writes the output and clears the cell for the next call.  Nobody
+    // waits and no barrier or counter is involved.  A token's result still depends on its own
+    // slots only.  The two workgroups may sit on different XCDs: the exchange is an agent-scope
+    // atomic, performed at the coherence point, and no cache is written back or invalidated.
+    uint64_t *cell = a.dcell + (size_t)hb * ((size_t)a.B * 16);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int t = (int)threadIdx.x + 64 * W * j;
         if (t < nt) {
-            const float o = __hip_atomic_load(other + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float y = part == 0 ? yv[j] + o : o + yv[j];
-            a.out[(size_t)(tb0 + (t >> 4)) * H + (size_t)hb * 16 + (t & 15)] = to_bf16(y);
+            const uint64_t mine = (uint64_t)__builtin_bit_cast(uint32_t, yv[j]) | 1ull << 32;
+            const uint64_t got = __hip_atomic_exchange(cell + t, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (got >> 32) {                           // the other class's sum was there: this is the second
+                const float o = __builtin_bit_cast(float, (uint32_t)got);
+                const float y = part == 0 ? yv[j] + o : o + yv[j];
+                a.out[(size_t)(tb0 + (t >> 4)) * H + (size_t)hb * 16 + (t & 15)] = to_bf16(y);
+                __hip_atomic_store(cell + t, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }

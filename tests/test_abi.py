@@ -311,8 +311,8 @@ def test_lds_gate_up_form_limits():
 def test_down_expert_split_host_checks():
     """The down kernel's expert split needs scratch of wd_down_scratch_bytes(B, H)
     (256-byte aligned), the matrix-core form and no token ranges."""
-    assert lib.wd_down_scratch_bytes(32, 2048) == 512 + 2 * 32 * 2048 * 4
-    assert lib.wd_down_scratch_bytes(1, 4096) == 1024 + 2 * 4096 * 4
+    assert lib.wd_down_scratch_bytes(32, 2048) == 32 * 2048 * 8          # one 8-byte cell per output
+    assert lib.wd_down_scratch_bytes(1, 4096) == 4096 * 8
     assert lib.wd_down_scratch_bytes(0, 2048) == 0 and lib.wd_down_scratch_bytes(1, 100) == 0
     assert lib.wd_layer_workspace_bytes(32, 8, 2048, 768) == 32 * 8 * 768 * 2 + lib.wd_down_scratch_bytes(32, 2048)
     assert lib.wd_layer_workspace_bytes(1, 8, 2048, 96) == 1536 + lib.wd_down_scratch_bytes(1, 2048)
