@@ -1138,53 +1138,60 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     // n % W) in expert order, experts that other token ranges use as well first, then the rest:
     // the workgroups of the other ranges of this output block stream the shared rows at about
     // the same time, so the later reads find them in the L2.  Each expert owns a run of lslot
-    // entries, runs in dealing order; every wave computes all run starts (a prefix sum of the
-    // counts, 64 experts at a time) and keeps its own experts' (e, first entry, count) in lexp
-    // and its own in lcur (wave << 16 | first entry), then files its experts' slots into their
-    // runs.  (Neither the order of experts nor the order of slots within a run changes a
-    // result: each slot's products depend on its own act column only and are kept per slot,
-    // and the fold takes them per token in expert order.)
+    // entries, runs in expert order; every wave computes all run starts and keeps its own
+    // experts' (e, first entry, count) in lexp and lcur (wave << 16 | first entry), then files
+    // its experts' slots into their runs.  (Neither the order of experts nor the order of slots
+    // within a run changes a result: each slot's products depend on its own act column only and
+    // are kept per slot, and the fold takes them per token in expert order.)
     // With 8 waves and one token range the deal is dynamic: experts with more than one group
     // first, then the rest, each wave taking the next one from a shared counter when it moves on,
     // so a wave given a heavy expert takes fewer, and a wave that streams slower than the others
     // (the memory system serves them unevenly) is not left with a fixed share.  (Which wave
     // serves an expert changes no result.)
     const bool dyn = W < 16 && a.tsplit == 1;   // 16 waves: static
+    // The deal order: first the experts of the first kind (dynamic deal: more than one group of
+    // slots; several token ranges: used by another range too), then the rest, each kind in expert
+    // order.  One pass counts the first kind; a second gives every routed expert its place n in
+    // the deal and its run start (runs in expert order, a prefix sum of the counts 64 experts at
+    // a time).  n's wave keeps the expert in lcur, and in its own list at n / W (static deal) or
+    // in lq at n (dynamic).
+    const bool two_kinds = dyn || a.tsplit > 1;
+    auto first_kind = [&](int e, int c) { return dyn ? c > G : loth[e] != 0; };
     int nx = 0, nused = 0;
     {
-        int gs = 0, seen = 0;                         // entries and experts dealt so far
-        for (int pass = 0; pass < 2; ++pass)
-            for (int base = 0; base < E && (pass == 1 || a.tsplit > 1 || dyn); base += 64) {   // one range: no shared expert
+        int n0 = 0;                                    // experts of the first kind
+        if (two_kinds)
+            for (int base = 0; base < E; base += 64) {
                 const int e = base + lane;
                 const int c = e < E ? (int)lcnt[e] : 0;
-                const bool sel = dyn ? (c > G) == (pass == 0) : (loth[e < E ? e : 0] != 0) == (pass == 0);
-                const bool used = c > 0 && sel;
-                const int cu = used ? c : 0;
-                const int first = gs + wave_incl_scan(cu) - cu;
-                const uint64_t um = __builtin_amdgcn_ballot_w64(used);
-                const int n = seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
-                const bool own = used && n % W == wv;
-                if (own) lcur[e] = (uint32_t)wv << 16 | (uint32_t)first;
-                if (dyn && own) lq[n] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)cu << 20;
-                uint64_t om = __builtin_amdgcn_ballot_w64(own);
-                if constexpr (W < 16) {                // the wave's experts of the 64 in one masked store
-                    const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(om >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)om, 0u));
-                    if (own) lexp[wv][nx + r] = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)cu << 20;
-                    nx += __builtin_popcountll(om);
-                } else {                               // one at a time (fewer registers)
-                    while (om) {
-                        const int l = (int)__builtin_ctzll(om);
-                        om &= om - 1;
-                        const uint32_t f = (uint32_t)__builtin_amdgcn_readlane(first, l);
-                        const uint32_t cn = (uint32_t)__builtin_amdgcn_readlane(cu, l);
-                        if (lane == 0) lexp[wv][nx] = (uint32_t)(base + l) | f << 10 | cn << 20;
-                        ++nx;
-                    }
-                }
-                seen += __builtin_popcountll(um);
-                gs = __builtin_amdgcn_readlane(first + cu, 63);   // entries of the experts dealt so far
+                n0 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c > 0 && first_kind(e < E ? e : 0, c)));
             }
-        nused = seen;
+        int gs = 0, s0 = 0, s1 = 0;                    // entries, and experts of each kind, so far
+        for (int base = 0; base < E; base += 64) {
+            const int e = base + lane;
+            const int c = e < E ? (int)lcnt[e] : 0;
+            const bool used = c > 0;
+            const bool k0 = two_kinds && used && first_kind(e < E ? e : 0, c);
+            const int cu = used ? c : 0;
+            const int first = gs + wave_incl_scan(cu) - cu;
+            const uint64_t m0 = __builtin_amdgcn_ballot_w64(k0), m1 = __builtin_amdgcn_ballot_w64(used && !k0);
+            const int r0 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u));
+            const int r1 = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u));
+            const int n = k0 ? s0 + r0 : n0 + s1 + r1;
+            if (used && n % W == wv) {
+                const uint32_t entry = (uint32_t)e | (uint32_t)first << 10 | (uint32_t)cu << 20;
+                lcur[e] = (uint32_t)wv << 16 | (uint32_t)first;
+                if (dyn)
+                    lq[n] = entry;
+                else
+                    lexp[wv][n / W] = entry;
+            }
+            s0 += __builtin_popcountll(m0);
+            s1 += __builtin_popcountll(m1);
+            gs = __builtin_amdgcn_readlane(first + cu, 63);   // entries of the experts so far
+        }
+        nused = s0 + s1;
+        nx = nused > wv ? (nused - wv + W - 1) / W : 0;    // this wave's experts in the static deal
     }
     if (dyn) nx = INT_MAX;                             // known once the deal runs out
     // The task sequence, compiled twice: with the static deal (each wave's list fixed by the scan)
