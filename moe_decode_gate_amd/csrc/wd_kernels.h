@@ -985,14 +985,17 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // y = fma(w_slot, P[h][slot], y), the token form's routing-weight fold, and
 // writes out[b][h] = BF16(y).  A token's result depends on its own slots only
 // (not on the other tokens, the wave that served an expert, or its top-k
-// order).  Each output is owned by one workgroup: no atomic, no buffer besides
-// the output.  Every Wd byte is read once per call.
+// order).  Each output is owned by one workgroup, or with the expert split
+// (esplit 2) by the two workgroups of its block, one per class of experts, that
+// meet in one scratch cell per output (one atomic exchange each; see the end of
+// the kernel).  Every Wd byte is read once per call, except for an expert used
+// by several token ranges.
 //
 // At the start the workgroup copies its slots' ids and router weights to LDS,
 // counts the slots per expert (LDS atomics, one thread per slot) and computes
-// each slot's fold rank; every wave then finds its experts and the start of
-// each expert's run of slot entries (a wave prefix sum of the counts, 64
-// experts per step) and files its experts' slots into their runs.  A wave's
+// each slot's fold rank; every wave then finds each routed expert's place in
+// the deal and the start of its run of slot entries (a wave prefix sum of the
+// counts, 64 experts per step) and files its experts' slots into their runs.  A wave's
 // work is then a sequence of tasks (expert, group of up to
 // G slots, batch of 4 64-element steps).  The loads of a task (the 16 rows'
 // codes, coalesced as in the matrix-core gate/up; the rows' E8M0 bytes; the
@@ -1014,7 +1017,7 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
 // workgroups leave idle.
 // Limits per token range: MAXS slots (each slot's 16 products, its id, router
 // weight, fold rank and run entry are kept in LDS) and MAXS / 8 tokens; 512
-// slots with 16 waves (147 KB of LDS), 512 or 1,024 with 8 (115 or 152 KB).
+// slots with 16 waves (147 KB of LDS), 512 or 1,024 with 8 (119 or 156 KB).
 // E <= 1024.
 // ---------------------------------------------------------------------------
 constexpr int kDnMfmaMaxB = 64;
