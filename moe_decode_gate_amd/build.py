@@ -25,6 +25,8 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-FP32 VALU forms in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments ahead of any aggregate go to SGPRs at dispatch (gfx950 kernarg preload)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -237,7 +237,8 @@ int launched() {
 
 // ---- runtime -> compile-time dispatch ------------------------------------
 
-typedef void (*KernelFn)(LayerArgs);
+// The kernels launched through launch(): leading scalar arguments (WD_LEAD_PARAMS), then LayerArgs.
+typedef void (*KernelFn)(const int32_t *, int, int, int, int, int, int, int, int, uint32_t, int, LayerArgs);
 
 template <int... V>
 struct Ints {};
@@ -340,11 +341,14 @@ int launch(KernelFn fn, LayerArgs a, const wd_launch &c, hipStream_t s) {
     a.nblocks = blocks;
     a.wpb = c.waves_per_block;
     const unsigned lds = (unsigned)c.lds_bytes;
+    // the leading arguments repeat the fields a wave needs before its first routing-id load
     if (c.start_event || c.stop_event)
         hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, s,
-                              (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a);
+                              (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a.ids, a.nwaves, a.nblocks,
+                              a.wpb, a.remap, a.order, a.B, a.K, a.nrowblk, a.nci_magic, a.I, a);
     else
-        hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, s, a);
+        hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, s, a.ids, a.nwaves, a.nblocks,
+                           a.wpb, a.remap, a.order, a.B, a.K, a.nrowblk, a.nci_magic, a.I, a);
     return launched();
 }
 

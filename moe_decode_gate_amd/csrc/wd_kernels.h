@@ -104,6 +104,21 @@ __device__ __forceinline__ int logical_wave(const LayerArgs &a) {
     return __builtin_amdgcn_readfirstlane(g * a.wpb + (int)(threadIdx.x >> 6));
 }
 
+// Leading scalar arguments of the kernels launched with LayerArgs: the values a wave needs to
+// find its place in the grid and to address its first routing-id load, ahead of the LayerArgs
+// block (which repeats them).  The library is built with kernel-argument preloading, so the
+// dispatch puts these in SGPRs before the wave starts and the id load goes out at once, instead
+// of after a scalar load of the argument block (about 0.2 us per launch of a one-token layer).
+#define WD_LEAD_PARAMS                                                                              \
+    const int32_t *__restrict__ l_ids, int l_nwaves, int l_nblocks, int l_wpb, int l_remap, int l_order, \
+        int l_B, int l_K, int l_nrowblk, uint32_t l_nci_magic, int l_I
+
+// logical_wave from the leading arguments
+__device__ __forceinline__ int lead_wave(int remap, int nblocks, int wpb) {
+    const int g = remap == 1 ? xcd_logical((int)blockIdx.x, nblocks) : (int)blockIdx.x;
+    return __builtin_amdgcn_readfirstlane(g * wpb + (int)(threadIdx.x >> 6));
+}
+
 // ---------------------------------------------------------------------------
 // Gate/up: one wave per (token b, slot k, block of G * R intermediate rows).
 //
@@ -123,24 +138,27 @@ __device__ __forceinline__ int logical_wave(const LayerArgs &a) {
 // j = jb * G * R + r * G + g.
 // ---------------------------------------------------------------------------
 template <int CPL, int R, int LPR, bool TAIL, int MATH, bool NT>
-__global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256) void gate_up_kernel(WD_LEAD_PARAMS, LayerArgs a) {
     constexpr int G = 64 / LPR;
-    zero_words(a);
     const int lane = threadIdx.x & 63;
     const int grp = lane / LPR, tl = lane % LPR;
-    args_early(a);
-    const int t = logical_wave(a);
-    if (t >= a.nwaves) return;                       // wave-uniform exit
+    const int t = lead_wave(l_remap, l_nblocks, l_wpb);
+    if (t >= l_nwaves) {                             // wave-uniform exit
+        zero_words(a);
+        return;
+    }
 
     int b, k, jb;
-    if (a.order == 1) {                              // t = (jb * B + b) * K + k
-        k = t % a.K; const int r = t / a.K; b = r % a.B; jb = r / a.B;
+    if (l_order == 1) {                              // t = (jb * B + b) * K + k
+        k = t % l_K; const int r = t / l_K; b = r % l_B; jb = r / l_B;
     } else {                                         // t = (b * K + k) * nrowblk + jb
-        jb = t % a.nrowblk; const int r = t / a.nrowblk; k = r % a.K; b = r / a.K;
+        jb = t % l_nrowblk; const int r = t / l_nrowblk; k = r % l_K; b = r / l_K;
     }
+    int e = sload(l_ids + b * l_K + k);              // (b, k) is wave-uniform
+    zero_words(a);
+    args_early(a);
     const int H = a.H, I = a.I;
     const int NC = H >> 4;                           // chunks per row
-    int e = sload(a.ids + b * a.K + k);              // (b, k) is wave-uniform
     const bool bad = (unsigned)e >= (unsigned)a.E;   // never read out of bounds for a bad id
     if (bad) e = 0;
 
@@ -233,11 +251,11 @@ __global__ __launch_bounds__(256) void gate_up_kernel(LayerArgs a) {
 // (order 1), else (expert t / nrowblk, row block t % nrowblk).
 // ---------------------------------------------------------------------------
 template <int CPL, int R, bool TAIL>
-__global__ __launch_bounds__(256) void gate_up_expert_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256) void gate_up_expert_kernel(WD_LEAD_PARAMS, LayerArgs a) {
     zero_words(a);
     const int lane = threadIdx.x & 63;
-    const int t = logical_wave(a);
-    if (t >= a.nwaves) return;
+    const int t = lead_wave(l_remap, l_nblocks, l_wpb);
+    if (t >= l_nwaves) return;
     int e, jb;
     expert_unit(a, t, e, jb);
     const int BK = a.B * a.K, H = a.H, I = a.I, NC = H >> 4;
@@ -392,10 +410,9 @@ struct MfmaBatch {                      // one wave's loads for kMfmaSteps 64-el
 static_assert(kMfmaSteps == 4, "one 8-byte scale load and 256 bytes per row cover a batch");
 
 template <bool SC8, int NGMAX, int HS>
-__global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256) void gate_up_mfma_kernel(WD_LEAD_PARAMS, LayerArgs a) {
     static_assert(HS == 1 || HS == 2, "one wave per unit, or a pair splitting H");
     constexpr int kWpb = HS == 2 ? 2 : 4;             // waves per workgroup
-    zero_words(a);
     // per wave: the batch's 16 gate and 16 up rows x 256 bytes, 16-byte slots XOR-swizzled by row,
     // and each lane's E8M0 bytes of the batch (kept in LDS: a register copy of the prefetched
     // bytes would make the compute wait for the whole prefetch)
@@ -403,8 +420,11 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     __shared__ uint64_t stile[kWpb][2][64];
     __shared__ f32x4 xch[HS == 2 ? NGMAX : 1][2][64];  // HS 2: the second wave's sums for the first
     const int lane = threadIdx.x & 63;
-    const int lw = logical_wave(a);
-    if (lw >= a.nwaves) return;                       // with HS 2, nwaves is even: pairs exit together
+    const int lw = lead_wave(l_remap, l_nblocks, l_wpb);
+    if (lw >= l_nwaves) {                             // with HS 2, nwaves is even: pairs exit together
+        zero_words(a);
+        return;
+    }
     // HS 2: the two waves of a workgroup serve one unit, each over its half of the H axis (an
     // equal number of whole 256-element batches); the second hands its FP32 sums to the first,
     // which adds them to its own (first half + second half) and writes the results
@@ -463,6 +483,24 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
     };
     MfmaBatch cur;
 
+    // Slots routed to e, found 512 at a time: eight independent id loads, then ballots.
+    uint64_t mk[8];
+    int chunk = 0, next_chunk = 0;
+    const int lBK = l_B * l_K;
+    auto refill = [&]() {
+        int idv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = next_chunk + 64 * u + lane;
+            idv[u] = sl < lBK ? l_ids[sl] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mk[u] = __builtin_amdgcn_ballot_w64(idv[u] == e);
+        chunk = next_chunk;
+        next_chunk += 512;
+    };
+    refill();
+    zero_words(a);
     if (e == 0 && half == 0) {   // NaN rows for slots whose id is outside [0, E)
         for (int base = 0; base < BK; base += 64) {
             const int sl = base + lane;
@@ -475,23 +513,6 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
             }
         }
     }
-
-    // Slots routed to e, found 512 at a time: eight independent id loads, then ballots.
-    uint64_t mk[8];
-    int chunk = 0, next_chunk = 0;
-    auto refill = [&]() {
-        int idv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = next_chunk + 64 * u + lane;
-            idv[u] = sl < BK ? a.ids[sl] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) mk[u] = __builtin_amdgcn_ballot_w64(idv[u] == e);
-        chunk = next_chunk;
-        next_chunk += 512;
-    };
-    refill();
     // The first batch only once the routing shows a slot for e (or the ids need more than one
     // scan): a wave whose expert no slot uses reads no weights.
     {
@@ -672,15 +693,17 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(LayerArgs a) {
 // Waves drain their loads before exiting.
 // ---------------------------------------------------------------------------
 template <int WPB>
-__global__ __launch_bounds__(64 * WPB) void gate_up_mfma_lds_kernel(LayerArgs a) {
-    zero_words(a);
+__global__ __launch_bounds__(64 * WPB) void gate_up_mfma_lds_kernel(WD_LEAD_PARAMS, LayerArgs a) {
     constexpr int kSeg = 8;                                // 16-byte segments per row per batch
     __shared__ u32x4 ring0[WPB][2][16][kSeg];              // slot 0: [wave][gate, up][row][slot]
     __shared__ u32x4 ring1[WPB][2][16][kSeg];              // slot 1
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int unit = logical_wave(a);
-    if (unit >= a.nwaves) return;                          // wave-uniform, before any load
+    const int unit = lead_wave(l_remap, l_nblocks, l_wpb);
+    if (unit >= l_nwaves) {                                // wave-uniform, before any load
+        zero_words(a);
+        return;
+    }
     int e, jb;
     expert_unit(a, unit, e, jb);
     const int BK = a.B * a.K, H = a.H, I = a.I;
@@ -712,6 +735,24 @@ __global__ __launch_bounds__(64 * WPB) void gate_up_mfma_lds_kernel(LayerArgs a)
     issue(ring0, 0);
     issue(ring1, 1 % nb);
 
+    // Slots routed to e, found 512 at a time: eight independent id loads, then ballots.
+    uint64_t mk[8];
+    int chunk = 0, next_chunk = 0;
+    const int lBK = l_B * l_K;
+    auto refill = [&]() {
+        int idv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = next_chunk + 64 * u + lane;
+            idv[u] = sl < lBK ? l_ids[sl] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mk[u] = __builtin_amdgcn_ballot_w64(idv[u] == e);
+        chunk = next_chunk;
+        next_chunk += 512;
+    };
+    refill();
+    zero_words(a);
     if (e == 0) {              // NaN rows for slots whose id is outside [0, E)
         for (int base = 0; base < BK; base += 64) {
             const int sl = base + lane;
@@ -724,23 +765,6 @@ __global__ __launch_bounds__(64 * WPB) void gate_up_mfma_lds_kernel(LayerArgs a)
             }
         }
     }
-
-    // Slots routed to e, found 512 at a time: eight independent id loads, then ballots.
-    uint64_t mk[8];
-    int chunk = 0, next_chunk = 0;
-    auto refill = [&]() {
-        int idv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = next_chunk + 64 * u + lane;
-            idv[u] = sl < BK ? a.ids[sl] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) mk[u] = __builtin_amdgcn_ballot_w64(idv[u] == e);
-        chunk = next_chunk;
-        next_chunk += 512;
-    };
-    refill();
 
     // per-lane offsets of the rows' E8M0 bytes (4 per batch) and, per group, of x
     const uint32_t sg_off = (uint32_t)r16 * nbr, su_off = (uint32_t)(I + r16) * nbr;
@@ -906,16 +930,15 @@ __global__ __launch_bounds__(64 * WPB) void gate_up_mfma_lds_kernel(LayerArgs a)
 // weight in with one FMA, acc += w_k * p.
 // ---------------------------------------------------------------------------
 template <int CPL, int R, bool TAIL, int MATH, bool NT>
-__global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256) void down_kernel(WD_LEAD_PARAMS, LayerArgs a) {
     const int lane = threadIdx.x & 63;
-    args_early(a);
-    const int t = logical_wave(a);
-    if (t >= a.nwaves) return;
+    const int t = lead_wave(l_remap, l_nblocks, l_wpb);
+    if (t >= l_nwaves) return;
 
     int b, hb;
-    if (a.order == 1) { b = t % a.B; hb = t / a.B; }        // t = hb * B + b
-    else { hb = t % a.nrowblk; b = t / a.nrowblk; }         // t = b * nrowblk + hb
-    const int H = a.H, I = a.I, K = a.K;
+    if (l_order == 1) { b = t % l_B; hb = t / l_B; }        // t = hb * B + b
+    else { hb = t % l_nrowblk; b = t / l_nrowblk; }         // t = b * nrowblk + hb
+    const int I = l_I, K = l_K, H = a.H;
     const int NCI = I >> 4;                                  // chunks per expert row
     const int NC = K * NCI;
     const size_t nbr = (size_t)(I >> 5);
@@ -930,9 +953,9 @@ __global__ __launch_bounds__(256) void down_kernel(LayerArgs a) {
         const int c = lane + 64 * i;
         const bool ok = !TAIL || c < NC;
         const int cc = ok ? c : 0;
-        const int kk = (int)(((uint64_t)cc * a.nci_magic) >> 22);   // cc / NCI (checked on the host)
+        const int kk = (int)(((uint64_t)cc * l_nci_magic) >> 22);   // cc / NCI (checked on the host)
         const int ci = cc - kk * NCI;
-        int e = a.ids[b * K + kk];
+        int e = l_ids[b * K + kk];
         bad |= ok && (unsigned)e >= (unsigned)a.E;
         if ((unsigned)e >= (unsigned)a.E) e = 0;
         wbase[i] = (size_t)e * H * I + (size_t)ci * 16;
