@@ -452,7 +452,7 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         const bool sc8 = (I / 32) % 8 == 0 && aligned(s_d, 4);
         // 8 waves: groups of 8 slots; 16 waves (register budget of four waves per SIMD): 4
         constexpr int S = wd::kDnMfmaMaxSlots, SW = wd::kDnMfmaMaxSlotsWide;
-        void (*fn)(LayerArgs) =
+        void (*fn)(const int32_t *, const float *, int, int, int, int, int, int, LayerArgs) =
             c.waves_per_block == 16 ? (sc8 ? wd::down_mfma_kernel<16, 4, true, S> : wd::down_mfma_kernel<16, 4, false, S>)
             : big                   ? (sc8 ? wd::down_mfma_kernel<8, 8, true, SW> : wd::down_mfma_kernel<8, 8, false, SW>)
                                     : (sc8 ? wd::down_mfma_kernel<8, 8, true, S> : wd::down_mfma_kernel<8, 8, false, S>);
@@ -471,11 +471,14 @@ int down_impl(const uint16_t *act, const int32_t *ids, const float *tw, const ui
         a.wpb = c.waves_per_block;
         const hipStream_t st = (hipStream_t)stream;
         const unsigned lds = (unsigned)c.lds_bytes;
+        // the leading arguments repeat what a workgroup needs to load its range's ids and weights
         if (c.start_event || c.stop_event)
             hipExtLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, st,
-                                  (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a);
+                                  (hipEvent_t)c.start_event, (hipEvent_t)c.stop_event, 0, a.ids, a.tw, a.nrowblk,
+                                  a.esplit, a.tsplit, a.B, a.K, a.E, a);
         else
-            hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, st, a);
+            hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * c.waves_per_block), lds, st, a.ids, a.tw, a.nrowblk,
+                               a.esplit, a.tsplit, a.B, a.K, a.E, a);
         return launched();
     }
     const int nc = K * (I / 16);

@@ -1061,8 +1061,14 @@ struct DownCursor {    // position in a wave's task sequence
     int e, start, cnt; // that expert, its first entry in the wave's slot list, its slot count
 };
 
+// Leading scalar arguments (preloaded into SGPRs at dispatch, as WD_LEAD_PARAMS): what a
+// workgroup needs to find its token range and load the range's ids and router weights.
+#define WD_DOWN_LEAD_PARAMS                                                                         \
+    const int32_t *__restrict__ l_ids, const float *__restrict__ l_tw, int l_nrowblk, int l_esplit, int l_tsplit, \
+        int l_B, int l_K, int l_E
+
 template <int W, int G, bool SC8, int MAXS>
-__global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
+__global__ __launch_bounds__(64 * W) void down_mfma_kernel(WD_DOWN_LEAD_PARAMS, LayerArgs a) {
     static_assert(MAXS == kDnMfmaMaxSlots || (MAXS == kDnMfmaMaxSlotsWide && W == 8), "slot capacity");
     constexpr int kMaxB = MAXS == kDnMfmaMaxSlots ? kDnMfmaMaxB : kDnMfmaMaxBWide;
     constexpr int kXRow = 33;                          // u32x4 per act row in LDS: 256 bf16 + 16 bytes of padding
@@ -1082,15 +1088,28 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     __shared__ int lnext;                              // dynamic deal: the next expert to hand out
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform: the task state stays scalar
-    const int hb = (int)blockIdx.x % a.nrowblk;
-    const int rg = (int)blockIdx.x / a.nrowblk;
-    const int part = rg & (a.esplit - 1);              // expert split: this workgroup's experts are e % esplit == part
-    const int tpr = (a.B + a.tsplit - 1) / a.tsplit;   // tokens per range
-    const int tb0 = rg / a.esplit * tpr;               // this workgroup's tokens: [tb0, tb1)
-    const int tb1 = min(a.B, tb0 + tpr);
+    const int hb = (int)blockIdx.x % l_nrowblk;
+    const int rg = (int)blockIdx.x / l_nrowblk;
+    const int part = rg & (l_esplit - 1);              // expert split: this workgroup's experts are e % esplit == part
+    const int tpr = (l_B + l_tsplit - 1) / l_tsplit;   // tokens per range
+    const int tb0 = rg / l_esplit * tpr;               // this workgroup's tokens: [tb0, tb1)
+    const int tb1 = min(l_B, tb0 + tpr);
     if (tb0 >= tb1) return;                            // workgroup-uniform: a range past the batch
-    const int H = a.H, I = a.I, E = a.E;
-    const int sl0 = tb0 * a.K, sl1 = tb1 * a.K;        // its slots
+    const int E = l_E, K = l_K;
+    const int sl0 = tb0 * K, sl1 = tb1 * K;            // its slots
+    const int nsl = sl1 - sl0;
+    // the range's ids and router weights, every load issued before anything waits (the leading
+    // arguments address them); they go to LDS once the tables below are cleared
+    constexpr int kIt = (MAXS + 64 * W - 1) / (64 * W);
+    int idr[kIt];
+    float twr[kIt];
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) {
+        const int t = (int)threadIdx.x + 64 * W * j;
+        idr[j] = t < nsl ? l_ids[sl0 + t] : 0;
+        twr[j] = t < nsl ? l_tw[sl0 + t] : 0.f;
+    }
+    const int H = a.H, I = a.I;
     const int r16 = lane & 15, q = lane >> 4;
     const int wrow = lane >> 4, wslot = lane & 15;
     u32x4(*wt)[16] = tile[wv];
@@ -1101,8 +1120,6 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     const int nsb = (s_hi + kMfmaSteps - 1) / kMfmaSteps;   // batches per expert
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    const int nsl = sl1 - sl0;
-    const int K = a.K;
     for (int t = (int)threadIdx.x; t < E; t += 64 * W) {
         lcnt[t] = 0;
         lcur[t] = 0xFFFFFFFFu;
@@ -1111,17 +1128,8 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(LayerArgs a) {
     if (threadIdx.x == 0) {
         lnext = W;                                     // experts 0 .. W-1 of the deal go to waves 0 .. W-1
     }
-    // the range's ids and router weights into LDS, every load issued before the first is used
+    // the range's ids and router weights into LDS
     {
-        constexpr int kIt = (MAXS + 64 * W - 1) / (64 * W);
-        int idr[kIt];
-        float twr[kIt];
-#pragma unroll
-        for (int j = 0; j < kIt; ++j) {
-            const int t = (int)threadIdx.x + 64 * W * j;
-            idr[j] = t < nsl ? a.ids[sl0 + t] : 0;
-            twr[j] = t < nsl ? a.tw[sl0 + t] : 0.f;
-        }
 #pragma unroll
         for (int j = 0; j < kIt; ++j) {
             const int t = (int)threadIdx.x + 64 * W * j;
