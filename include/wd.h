@@ -295,7 +295,8 @@ int wd_moe_decode(const uint16_t *x, const int32_t *topk_ids, const float *topk_
  * calls that overlap in time on one GPU (different streams, or several host
  * threads without ordering) race on it and must be serialised by the caller;
  * calls in order on one stream are safe.  Nothing in the array needs to start
- * at zero (gate/up writes every act element the down kernel reads). */
+ * at zero (gate/up writes every act element the down kernel reads, and clears
+ * the down kernel's expert-split cells when the array holds them after act). */
 int wd_moe_decode_noalloc(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                           const uint8_t *w_gu, const uint8_t *s_gu,
                           const uint8_t *w_d, const uint8_t *s_d, uint16_t *out,
