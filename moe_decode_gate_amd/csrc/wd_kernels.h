@@ -155,7 +155,6 @@ __global__ __launch_bounds__(256) void gate_up_kernel(WD_LEAD_PARAMS, LayerArgs 
         jb = t % l_nrowblk; const int r = t / l_nrowblk; k = r % l_K; b = r / l_K;
     }
     int e = sload(l_ids + b * l_K + k);              // (b, k) is wave-uniform
-    zero_words(a);
     args_early(a);
     const int H = a.H, I = a.I;
     const int NC = H >> 4;                           // chunks per row
@@ -195,23 +194,32 @@ __global__ __launch_bounds__(256) void gate_up_kernel(WD_LEAD_PARAMS, LayerArgs 
         const uint8_t *wu = wg + (size_t)I * H;
         const uint8_t *sg = a.s + (erow + j) * nbr;
         const uint8_t *su = sg + (size_t)I * nbr;
-        float g = 0.f, u = 0.f;
+        // the row's loads, all issued before the first is used (the compiler would otherwise
+        // wait for each chunk's before issuing the next)
+        u32x4 qg[CPL], qu[CPL];
+        uint8_t bg[CPL], bu[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = tl + LPR * i;
-            const bool ok = !TAIL || c < NC;
-            const int cc = ok ? c : 0;
-            const u32x4 qg = ldw<NT>(wg + cc * 16);
-            const u32x4 qu = ldw<NT>(wu + cc * 16);
-            const float fg = e8m0_operand(sg[cc >> 1]);
-            const float fu = e8m0_operand(su[cc >> 1]);
+            const int cc = (!TAIL || c < NC) ? c : 0;
+            qg[i] = ldw<NT>(wg + cc * 16);
+            qu[i] = ldw<NT>(wu + cc * 16);
+            bg[i] = sg[cc >> 1];
+            bu[i] = su[cc >> 1];
+        }
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const bool ok = !TAIL || tl + LPR * i < NC;
+            const float fg = e8m0_operand(bg[i]);
+            const float fu = e8m0_operand(bu[i]);
             float g2, u2;
             if constexpr (MATH == kMathF32) {
-                g2 = dot16_f32(qg, fg, xv[i], g);
-                u2 = dot16_f32(qu, fu, xv[i], u);
+                g2 = dot16_f32(qg[i], fg, xv[i], g);
+                u2 = dot16_f32(qu[i], fu, xv[i], u);
             } else {
-                g2 = dot16_dot2(qg, fg, xp0[i], xp1[i], g);
-                u2 = dot16_dot2(qu, fu, xp0[i], xp1[i], u);
+                g2 = dot16_dot2(qg[i], fg, xp0[i], xp1[i], g);
+                u2 = dot16_dot2(qu[i], fu, xp0[i], xp1[i], u);
             }
             g = ok ? g2 : g;                         // lanes past the row end add nothing
             u = ok ? u2 : u;
@@ -229,6 +237,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(WD_LEAD_PARAMS, LayerArgs 
     for (int r = 1; r < R; ++r) mine = tl == r ? res[r] : mine;
     if (tl < R)
         a.out[((size_t)b * a.K + k) * I + (size_t)(jbase + tl * G)] = to_bf16(mine);
+    zero_words(a);                                   // last: its branch would split the loads' schedule
 }
 
 // ---------------------------------------------------------------------------
