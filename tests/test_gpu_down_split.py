@@ -82,16 +82,17 @@ def test_down_expert_split(name, spec, B, routing, W):
         assert np.array_equal(part, ob[sub])
 
 
-def test_whole_layer_entry_points_use_the_split():
+@pytest.mark.parametrize("B", [16, 32])
+def test_whole_layer_entry_points_use_the_split(B):
     """wd_moe_decode with the layer workspace (the binding's default) and the
     no-allocation entry point run the expert split, bit-identical to gate/up
     followed by the split down; with a workspace of act alone wd_moe_decode
-    keeps the token ranges (held to the oracle too)."""
+    runs the down kernel without the split (held to the oracle too).  B = 16 clears the
+    split's cells from the token-form gate/up, B = 32 from the matrix-core one."""
     from moe_decode_gate_amd import binding as wd
     spec = gen.LayerSpec(E=128, K=8, H=2048, I=768, seed=126)
     L = gen.make_layer(spec, threads=16)
     dl = DevLayer(L)
-    B = 32
     t = gen.make_tokens(spec, B)
     dt = DevTokens(t)
     act = wd.gate_up(dt.x, dt.ids, dl.wgu, dl.sgu)
