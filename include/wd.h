@@ -157,8 +157,11 @@ enum wd_status {
  *                    512, else one range of 8 waves; a larger batch takes the
  *                    fewest ranges (2 or 4) that hold it, 16 waves when each
  *                    range has at most 64 tokens and 512 slots, else 8.
- *   weight_loads     1 = cached weight loads; 2 = non-temporal (the rows are
- *                    streamed once and not kept in the caches)
+ *   weight_loads     token forms: 1 = cached weight loads; 2 = non-temporal
+ *                    (the rows are streamed once and not kept in the caches).
+ *                    Forms 3 and 4 take 1 (form 3 always loads its weight
+ *                    codes non-temporally: each pass reads an expert's rows
+ *                    once)
  *   token_split      down, form 3 only: 1, 2 or 4 workgroups per block of 16
  *                    output dims, each serving its own contiguous range of
  *                    ceil(B / token_split) tokens (an expert shared by

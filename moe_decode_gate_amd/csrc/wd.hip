@@ -206,7 +206,8 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (down && (c.lanes_per_row != 64 || c.form == 2)) return WD_ERR_UNSUPPORTED;
     if (c.form == 2 && (c.lanes_per_row != 64 || c.math != wd::kMathDot2 || c.weight_loads != 1))
         return WD_ERR_UNSUPPORTED;
-    // matrix-core expert form: fixed 16-row blocks and lane layout, BF16 operands, cached loads
+    // matrix-core expert form: fixed 16-row blocks and lane layout, BF16 operands; the knob stays 1
+    // (form 3 loads its codes non-temporally in any case)
     if (c.form >= 3 && (c.rows_per_wave != 1 || c.lanes_per_row != 64 || c.math != wd::kMathDot2 ||
                         c.weight_loads != 1))
         return WD_ERR_UNSUPPORTED;
