@@ -467,7 +467,9 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(WD_LEAD_PARAMS, Layer
     const uint8_t *pg0 = a.w + ((size_t)e * 2 * I + (size_t)jb * 16) * (size_t)H;
     const uint8_t *pu0 = pg0 + (size_t)I * H;
     const int wrow = lane >> 4, wslot = lane & 15;
-    auto load_batch = [&](int s0, MfmaBatch &bt) {
+    // an in-bounds address in x (at least 64 bytes) for the code loads whose data is not used
+    const uint8_t *xdum = reinterpret_cast<const uint8_t *>(a.x) + 16 * (lane & 3);
+    auto load_batch = [&](int s0, MfmaBatch &bt, bool dummy) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = 4 * (j & 3) + wrow;
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(WD_LEAD_PARAMS, Layer
             // non-temporal: the rows are read once per pass, and keeping them out of the way leaves
             // the caches to the routing ids and x, which every wave reads (bit-identical; B = 32
             // 69.6 -> 67.9 us)
-            bt.v[j] = ldw<true>(base + (k < H ? k : 0));   // past H: clamped, zeroed when read
+            bt.v[j] = ldw<true>(dummy ? xdum : base + (k < H ? k : 0));   // past H: clamped, zeroed when read
         }
         if constexpr (SC8) {
             const int o = 2 * s0 + 8 <= (int)nbr ? 2 * s0 : 0;   // always 2 s0 for H % 256 == 0
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(WD_LEAD_PARAMS, Layer
         for (int u = 0; u < 8; ++u) any |= mk[u];
         if (any == 0 && next_chunk >= BK) return;
     }
-    load_batch(s_lo, cur);
+    load_batch(s_lo, cur, false);
 
     // One pass per up to 16 * NGMAX slots routed to e: the weight batches stream once per
     // pass and feed one 16-slot tile, or with NGMAX 2 two when more than 16 slots remain (the
@@ -578,11 +580,11 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(WD_LEAD_PARAMS, Layer
                     x1[g][i] = ld16(xr[g] + kc + 8);
                 }
             // prefetch into the same registers (their codes are in LDS now): the next batch, this
-            // wave's first batch again for a further pass, or else this batch again (unused; its
-            // lines are still in the cache, so the load that keeps every batch alike costs no
-            // HBM traffic)
+            // wave's first batch again for a further pass, or else loads whose data is not used
+            // (the codes from x, which the caches hold, the scale bytes this batch's again), so
+            // that every batch issues the same loads and each wait counts exactly
             const bool more = s0 + kMfmaSteps < s_hi;
-            load_batch(more ? s0 + kMfmaSteps : cnt == kPass ? s_lo : s0, cur);
+            load_batch(more ? s0 + kMfmaSteps : cnt == kPass ? s_lo : s0, cur, !more && cnt != kPass);
 #pragma unroll
             for (int i = 0; i < kMfmaSteps; ++i) {
                 const int k = 64 * (s0 + i) + 16 * q;
@@ -1305,16 +1307,20 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(WD_DOWN_LEAD_PARAMS, 
         // used counts exactly the younger sets' loads.  Past the end of the sequence the cursor
         // keeps naming the last expert (and expert 0 for a wave with none), so the loads stay
         // in bounds; their data is never used.
+        // an in-bounds address in act (at least 64 bytes) for the code loads past the end of the
+        // wave's tasks, whose data is not used
+        const uint8_t *adum = reinterpret_cast<const uint8_t *>(a.act_in) + 16 * (lane & 3);
         auto issue_w = [&](DownSet<G> &st) {              // the task's weight codes and E8M0 bytes
             const int e = ld.e;
             const int s0 = ld.sb * kMfmaSteps;
+            const bool dummy = ld.x >= nx;                 // past the end: keep the loads, not the HBM reads
             const uint8_t *pw = a.w + ((size_t)e * H + (size_t)hb * 16) * (size_t)I + 64 * s0;
             const int lim = I - 64 * s0;                   // bytes of each row left from this batch on
     #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int seg = 16 * (wslot ^ (4 * j + wrow));
                 // non-temporal, as in the matrix-core gate/up: the cached act rows and tables stay
-                st.v[j] = ldw<true>(pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0));   // past I: the row's start, zeroed when read
+                st.v[j] = ldw<true>(dummy ? adum : pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0));   // past I: the row's start, zeroed when read
             }
             const uint8_t *ps = a.s + ((size_t)e * H + (size_t)hb * 16) * (size_t)nbr + soff;
             if constexpr (SC8) {       // rows of a multiple of 8 E8M0 bytes (I % 256 == 0): one 8-byte load
