@@ -129,7 +129,7 @@ enum wd_status {
  *                    ahead in registers; needs H a multiple of 256, s_gu
  *                    4-byte aligned, B * H * 2 <= 0x7FFF0000 and 2 or 4
  *                    waves per workgroup (default 4).
- *                    Default: 3 when B >= 20 (B >= 4 when H >= 4096) and
+ *                    Default: 3 when B >= 18 (B >= 4 when H >= 4096) and
  *                    none of rows_per_wave, lanes_per_row, math,
  *                    weight_loads is set, else 1.
  *                    down: 1 = one wave per (token, block of output dims);
@@ -235,7 +235,7 @@ typedef struct wd_launch {
  * "How the two kernels work"; the Chinese summary's "Gate/Up Kernel"):
  * act[b,k,j] = BF16(SiLU(g) * u) with g, u the dot products of x[b] with gate
  * row j and up row I+j of expert e = topk_ids[b,k], MXFP8 converted exactly
- * as it is read, FP32 accumulation, x read once for both.  Below 20 tokens
+ * as it is read, FP32 accumulation, x read once for both.  Below 18 tokens
  * (4 when H >= 4096; the default token form) one 64-lane wave serves each
  * (token, slot, block of rows) and reduces across its lanes: no LDS, no
  * barrier.  From there on the default is the expert form on the matrix cores

@@ -70,12 +70,14 @@ bool down_big_range(int tpr, int K) {
 // for B in {1, 2, 4, 8, 16, 32, 64}:
 //   gate/up, B <= 4: one row per 64-lane wave, BF16-pair dot products,
 //          non-temporal weight loads (no row is read twice), hardware order;
-//   gate/up, B 5..23: 32 lanes per row, 4 rows per lane group (8 per wave),
+//   gate/up, B 5..17 (and form 1 above): 32 lanes per row, 4 rows per lane group (8 per wave),
 //          row-block-major order with XCD-contiguous numbering, so the tokens
 //          that share an expert row read it from the same L2 while resident;
-//   gate/up, B >= 20 (B >= 4 when H >= 4096): the expert form on the matrix
+//   gate/up, B >= 18 (B >= 4 when H >= 4096): the expert form on the matrix
 //          cores (one wave per expert row block, and none for an expert no slot
-//          uses; Qwen-3 layer 58.6 against 61.5 us at B = 20, 70 against 85 at
+//          uses; Qwen-3 layer 55.3 against 57.0 us at B = 18 with its weight
+//          codes non-temporal, the token form ahead at B = 16, 51.7 against
+//          53.1; before that: 58.6 against 61.5 us at B = 20, 70 against 85 at
 //          B = 32, 75 against 136 at B = 64, the token form ahead at B = 16, 52.9
 //          against 55.0; on the 4096 / 1536 layer with Zipf routing, with the H
 //          split, 59.8 against 65.0 us at B = 4, 74.4 against 79.8 at B = 6, the
@@ -119,7 +121,7 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.form == 0) {
         const bool mfma = down ? untuned && c.waves_per_block == 0 && B >= (wide ? 3 : have_scratch ? 13 : 24) &&
                                      down_min_ranges(B, K) > 0 && E <= wd::kDnMfmaMaxE
-                               : untuned && (B >= 20 || (H >= 4096 && B >= 4));
+                               : untuned && (B >= 18 || (H >= 4096 && B >= 4));
         c.form = mfma ? 3 : 1;
     }
     if (c.form >= 3 && c.rows_per_wave == 0) c.rows_per_wave = 1;   // one 16-row block per wave

@@ -351,7 +351,7 @@ def test_gate_up_h_split(H, B, routing):
 
 def test_gate_up_lds_form_bad_ids_and_default():
     """Form 4 writes NaN rows for ids outside [0, E), and its intermediate is
-    bit-identical to the default's (form 3 from B = 20)."""
+    bit-identical to the default's (form 3 from B = 18)."""
     spec = gen.LayerSpec(E=16, K=4, H=1024, I=320, seed=97)
     dl = DevLayer(gen.make_layer(spec, threads=16))
     t = gen.make_tokens(spec, 30)

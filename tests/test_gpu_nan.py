@@ -7,7 +7,7 @@ the NaN.  A NaN in a down-projection row h of expert e reaches out[b, h] of
 each token b routed to e (NaN times anything, zero included, is NaN); a NaN
 in a gate or up row j of e makes act[b, k, j] NaN for those tokens and, through
 the down projection, their whole output row.  Checked under the token forms
-(small batch) and the matrix-core forms (from B = 20), whose tiles share a weight
+(small batch) and the matrix-core forms (from B = 18), whose tiles share a weight
 row across several tokens and must still keep the NaN to the columns of the
 tokens that use it."""
 import numpy as np
