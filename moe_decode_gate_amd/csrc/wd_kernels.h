@@ -475,9 +475,10 @@ __global__ __launch_bounds__(256) void gate_up_mfma_kernel(WD_LEAD_PARAMS, Layer
             const int r = 4 * (j & 3) + wrow;
             const int k = 64 * s0 + 16 * (wslot ^ r);
             const uint8_t *base = (j < 4 ? pg0 : pu0) + (size_t)r * H;
-            // non-temporal: the rows are read once per pass, and keeping them out of the way leaves
-            // the caches to the routing ids and x, which every wave reads (bit-identical; B = 32
-            // 69.6 -> 67.9 us)
+            // non-temporal: a pass reads the rows once, and keeping them out of the way leaves the
+            // caches to the routing ids and x, which every wave reads (bit-identical; B = 32
+            // 69.6 -> 67.9 us; an expert with more than a pass's slots reads its rows again in
+            // the next pass, from memory, and is still faster so)
             bt.v[j] = ldw<true>(dummy ? xdum : base + (k < H ? k : 0));   // past H: clamped, zeroed when read
         }
         if constexpr (SC8) {
@@ -1319,8 +1320,14 @@ __global__ __launch_bounds__(64 * W) void down_mfma_kernel(WD_DOWN_LEAD_PARAMS, 
     #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int seg = 16 * (wslot ^ (4 * j + wrow));
-                // non-temporal, as in the matrix-core gate/up: the cached act rows and tables stay
-                st.v[j] = ldw<true>(dummy ? adum : pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0));   // past I: the row's start, zeroed when read
+                const uint8_t *p = dummy ? adum : pw + (seg < lim ? coff[j] : coff[j] - seg - 64 * s0);   // past I: the row's start, zeroed when read
+                // with one token range non-temporal, as in the matrix-core gate/up (the cached act
+                // rows and tables stay); with several, the other ranges' workgroups read the same
+                // rows from the L2
+                if constexpr (D)
+                    st.v[j] = ldw<true>(p);
+                else
+                    st.v[j] = ld16(p);
             }
             const uint8_t *ps = a.s + ((size_t)e * H + (size_t)hb * 16) * (size_t)nbr + soff;
             if constexpr (SC8) {       // rows of a multiple of 8 E8M0 bytes (I % 256 == 0): one 8-byte load
