@@ -158,7 +158,9 @@ enum wd_status {
  *                    fewest ranges (2 or 4) that hold it, 16 waves when each
  *                    range has at most 64 tokens and 512 slots, else 8.
  *   weight_loads     token forms: 1 = cached weight loads; 2 = non-temporal
- *                    (the rows are streamed once and not kept in the caches).
+ *                    (the rows are streamed past the caches; gate/up: 32 or 64
+ *                    lanes per row; down: one row per wave).  0 = default: 2
+ *                    for gate/up, and for the down below 3 tokens, else 1.
  *                    Forms 3 and 4 take 1 (form 3 always loads its weight
  *                    codes non-temporally: each pass reads an expert's rows
  *                    once)

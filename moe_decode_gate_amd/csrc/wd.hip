@@ -180,15 +180,20 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.xcd_remap == 0) c.xcd_remap = ((!down && !batch) || expert_form) ? 2 : 1;
     if (c.math == 0) c.math = (down && batch && !wide && c.form != 3) ? wd::kMathF32 : wd::kMathDot2;
     if (c.weight_loads == 0) {
-        // non-temporal where no other wave re-reads the rows and the variant is compiled
+        // non-temporal where it measured faster and the variant is compiled
         const bool nt_ok = c.math == wd::kMathDot2 && c.form == 1 &&
-                           (down ? c.rows_per_wave == 1 : (c.lanes_per_row == 0 || c.lanes_per_row == 64));
-        c.weight_loads = (!batch && nt_ok) ? 2 : 1;
+                           (down ? c.rows_per_wave == 1
+                                 : (c.lanes_per_row == 0 || c.lanes_per_row == 64 || c.lanes_per_row == 32));
+        // gate/up's token form non-temporal at every B (the tokens that share an expert row read
+        // it at about the same time, and the cached x rows stay: Qwen-3 layer B = 8 31.4 -> 28.8
+        // us, B = 16 51.5 -> 50.8); the token-form down only below 3 tokens (cached B = 4 9.29
+        // against 9.56 us)
+        c.weight_loads = ((!batch || !down) && nt_ok) ? 2 : 1;
     }
     // 32 lanes per row hold at most 8 chunks each (H <= 4096); longer rows take 64
     if (c.lanes_per_row == 0)
         c.lanes_per_row =
-            (!down && batch && c.form == 1 && c.math == wd::kMathDot2 && c.weight_loads != 2 && H <= 4096) ? 32 : 64;
+            (!down && batch && c.form == 1 && c.math == wd::kMathDot2 && H <= 4096) ? 32 : 64;
     if (c.rows_per_wave != 1 && c.rows_per_wave != 2 && c.rows_per_wave != 4 && c.rows_per_wave != 8)
         return WD_ERR_UNSUPPORTED;
     // down on the matrix cores: one workgroup of 8 or 16 waves per block of 16 outputs
@@ -257,13 +262,13 @@ KernelFn dispatch(int v, Ints<V0, Vs...>, F f) {
 
 // Which variants are compiled.  Token-form gate/up: every chunk count, row
 // count and tail; FP32 math only with 64 lanes per row and cached loads,
-// non-temporal loads only with 64 lanes per row.  Expert form: register use
+// non-temporal loads with 32 or 64 lanes per row.  Expert form: register use
 // limits R * CPL to 8.  Down: non-temporal loads only at one row per wave.
 template <int CPL, int R, int LPR, int M, int NT>
 constexpr bool gate_up_compiled() {
     if (R == 8) return false;
     if (M == wd::kMathF32) return LPR == 64 && NT == 0;
-    return NT == 0 || LPR == 64;
+    return NT == 0 || LPR == 64 || LPR == 32;
 }
 template <int CPL, int R>
 constexpr bool gate_up_expert_compiled() { return R <= 4 && R * CPL <= 8; }
