@@ -160,7 +160,8 @@ enum wd_status {
  *   weight_loads     token forms: 1 = cached weight loads; 2 = non-temporal
  *                    (the rows are streamed past the caches; gate/up: 32 or 64
  *                    lanes per row; down: one row per wave).  0 = default: 2
- *                    for gate/up, and for the down below 3 tokens, else 1.
+ *                    for gate/up up to 16 tokens and for the down below 3,
+ *                    else 1.
  *                    Forms 3 and 4 take 1 (form 3 always loads its weight
  *                    codes non-temporally: each pass reads an expert's rows
  *                    once)

@@ -184,11 +184,11 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
         const bool nt_ok = c.math == wd::kMathDot2 && c.form == 1 &&
                            (down ? c.rows_per_wave == 1
                                  : (c.lanes_per_row == 0 || c.lanes_per_row == 64 || c.lanes_per_row == 32));
-        // gate/up's token form non-temporal at every B (the tokens that share an expert row read
-        // it at about the same time, and the cached x rows stay: Qwen-3 layer B = 8 31.4 -> 28.8
-        // us, B = 16 51.5 -> 50.8); the token-form down only below 3 tokens (cached B = 4 9.29
+        // gate/up's token form non-temporal up to 16 tokens, where few tokens share an expert row
+        // (Qwen-3 layer B = 8 31.4 -> 28.8 us, B = 16 51.5 -> 50.8; at B = 32, where rows are
+        // shared, 84.9 -> 96.0); the token-form down only below 3 tokens (cached B = 4 9.29
         // against 9.56 us)
-        c.weight_loads = ((!batch || !down) && nt_ok) ? 2 : 1;
+        c.weight_loads = ((!batch || (!down && B <= 16)) && nt_ok) ? 2 : 1;
     }
     // 32 lanes per row hold at most 8 chunks each (H <= 4096); longer rows take 64
     if (c.lanes_per_row == 0)
