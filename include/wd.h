@@ -159,9 +159,9 @@ enum wd_status {
  *                    range has at most 64 tokens and 512 slots, else 8.
  *   weight_loads     token forms: 1 = cached weight loads; 2 = non-temporal
  *                    (the rows are streamed past the caches; gate/up: 32 or 64
- *                    lanes per row; down: one row per wave).  0 = default: 2
- *                    for gate/up up to 16 tokens and for the down below 3,
- *                    else 1.
+ *                    lanes per row; down: one or two rows per wave).  0 =
+ *                    default: 2 for gate/up up to 16 tokens and for the down
+ *                    at one or two rows per wave (one token), else 1.
  *                    Forms 3 and 4 take 1 (form 3 always loads its weight
  *                    codes non-temporally: each pass reads an expert's rows
  *                    once)

@@ -182,11 +182,12 @@ int resolve(const wd_launch *in, int B, int K, int E, int H, int I, bool down, w
     if (c.weight_loads == 0) {
         // non-temporal where it measured faster and the variant is compiled
         const bool nt_ok = c.math == wd::kMathDot2 && c.form == 1 &&
-                           (down ? c.rows_per_wave == 1
+                           (down ? c.rows_per_wave <= 2
                                  : (c.lanes_per_row == 0 || c.lanes_per_row == 64 || c.lanes_per_row == 32));
         // gate/up's token form non-temporal up to 16 tokens, where few tokens share an expert row
         // (Qwen-3 layer B = 8 31.4 -> 28.8 us, B = 16 51.5 -> 50.8; at B = 32, where rows are
-        // shared, 84.9 -> 96.0); the token-form down only below 3 tokens (cached B = 4 9.29
+        // shared, 84.9 -> 96.0); the token-form down at one or two rows per wave (one token; the
+        // 128-expert / H 4096 / I 1536 layer at B = 1: step 28.9 -> 28.3 us; cached B = 4 9.29
         // against 9.56 us)
         c.weight_loads = ((!batch || (!down && B <= 16)) && nt_ok) ? 2 : 1;
     }
@@ -273,7 +274,7 @@ constexpr bool gate_up_compiled() {
 template <int CPL, int R>
 constexpr bool gate_up_expert_compiled() { return R <= 4 && R * CPL <= 8; }
 template <int CPL, int R, int M, int NT>
-constexpr bool down_compiled() { return NT == 0 || (R == 1 && M == wd::kMathDot2); }
+constexpr bool down_compiled() { return NT == 0 || (R <= 2 && M == wd::kMathDot2); }
 
 KernelFn gate_up_fn(int cpl, int R, int lpr, int tail, int math, int nt) {
     return dispatch(cpl, Ints<1, 2, 4, 8>{}, [&](auto C) {
